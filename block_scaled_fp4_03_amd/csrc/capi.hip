@@ -1,0 +1,235 @@
+// C ABI of the library: argument validation on the host, then the launchers.
+// Nothing here allocates, frees or synchronises (except under
+// NVFP4MOE_SYNC_CHECK=1, a debugging aid).
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/nvfp4moe.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool sync_check_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("NVFP4MOE_SYNC_CHECK");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+int32_t finish(const char* who, hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  if (sync_check_enabled()) {
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: kernel failed: %s", who, hipGetErrorString(e));
+  }
+  g_last_error.clear();
+  return NVFP4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_size(int32_t dtype) {
+  return dtype == NVFP4_DTYPE_F32 ? 4 : (dtype == NVFP4_DTYPE_BF16 ? 2 : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+int32_t nvfp4_version(void) { return 100; }
+
+int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                       const float* gs, uint8_t* codes, uint8_t* scales, void* stream) {
+  const int es = elem_size(x_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "nvfp4_quantize: unknown dtype %d", x_dtype);
+  if (rows < 0 || cols < 0) return fail(NVFP4_ESHAPE, "nvfp4_quantize: negative size");
+  if (cols % 16) return fail(NVFP4_ESHAPE, "nvfp4_quantize: cols=%lld is not a multiple of 16", (long long)cols);
+  if (ld_x < cols) return fail(NVFP4_ESHAPE, "nvfp4_quantize: ld_x < cols");
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!x || !gs || !codes || !scales) return fail(NVFP4_EINVAL, "nvfp4_quantize: null pointer");
+  if (!aligned(x, 16) || (ld_x * es) % 16 || !aligned(codes, 8) || !aligned(gs, 4))
+    return fail(NVFP4_EALIGN, "nvfp4_quantize: x and its row pitch must be 16-byte aligned, codes 8-byte");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("nvfp4_quantize",
+                nvfp4::launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, rows, cols, ld_x, gs, codes, scales, s), s);
+}
+
+size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n) {
+  if (batch <= 0 || n < 0) return 0;
+  return (size_t)batch * (size_t)nvfp4::amax_chunks(n) * sizeof(float);
+}
+
+int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_t n, int64_t stride,
+                           float* gs_out, void* ws, size_t ws_bytes, void* stream) {
+  const int es = elem_size(x_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "nvfp4_global_scale: unknown dtype %d", x_dtype);
+  if (batch < 0 || n < 0) return fail(NVFP4_ESHAPE, "nvfp4_global_scale: negative size");
+  if (batch > 65535) return fail(NVFP4_ESHAPE, "nvfp4_global_scale: batch > 65535");
+  if (n % 8) return fail(NVFP4_ESHAPE, "nvfp4_global_scale: n must be a multiple of 8");
+  if (stride < n) return fail(NVFP4_ESHAPE, "nvfp4_global_scale: stride < n");
+  if (batch == 0) return NVFP4_OK;
+  if (!x || !gs_out || !ws) return fail(NVFP4_EINVAL, "nvfp4_global_scale: null pointer");
+  if (ws_bytes < nvfp4_global_scale_workspace_size(batch, n))
+    return fail(NVFP4_ESHAPE, "nvfp4_global_scale: workspace too small");
+  if (!aligned(x, 16) || (stride * es) % 16 || !aligned(ws, 16) || !aligned(gs_out, 4))
+    return fail(NVFP4_EALIGN, "nvfp4_global_scale: x, its pitch and ws must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("nvfp4_global_scale",
+                nvfp4::launch_global_scale(x, x_dtype == NVFP4_DTYPE_BF16, batch, n, stride, gs_out,
+                                           (float*)ws, s),
+                s);
+}
+
+int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                          float* topk_w, int32_t* expert_offsets, int32_t* sorted_token_ids,
+                          int32_t* inv_perm, void* stream) {
+  if (T < 0) return fail(NVFP4_ESHAPE, "moe_route_permute: T < 0");
+  if (E < 1 || E > NVFP4_MAX_EXPERTS)
+    return fail(NVFP4_ESHAPE, "moe_route_permute: E=%d outside [1, %d]", E, NVFP4_MAX_EXPERTS);
+  if (k < 1 || k > E || k > NVFP4_MAX_TOPK)
+    return fail(NVFP4_ESHAPE, "moe_route_permute: k=%d outside [1, min(E, %d)]", k, NVFP4_MAX_TOPK);
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return fail(NVFP4_ESHAPE, "moe_route_permute: T*k >= 2^31");
+  if (!expert_offsets) return fail(NVFP4_EINVAL, "moe_route_permute: null pointer");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_token_ids || !inv_perm))
+    return fail(NVFP4_EINVAL, "moe_route_permute: null pointer");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_token_ids, 4) || !aligned(inv_perm, 4))
+    return fail(NVFP4_EALIGN, "moe_route_permute: arrays must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("moe_route_permute",
+                nvfp4::launch_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets,
+                                            sorted_token_ids, inv_perm, s),
+                s);
+}
+
+int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                           int64_t a_rows, const int32_t* a_row_index, const uint8_t* w_codes,
+                           const uint8_t* w_scales, const float* w_gs, const int32_t* n_seg,
+                           int32_t n_segs, const int32_t* group_offsets, int32_t G, int64_t M, int64_t N,
+                           int64_t K, void* out, int32_t out_dtype, int64_t ld_out, void* stream) {
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: unknown out dtype %d", out_dtype);
+  if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: G=%d", G);
+  if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: n_segs=%d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);
+  if (M < 0 || N < 1 || K < 32 || K % 32)
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: need M >= 0, N >= 1, K >= 32 and K %% 32 == 0");
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: M and N must be below 2^31");
+  if (ld_out < N) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: ld_out < N");
+  if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: a_rows too small");
+  if (!n_seg) return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: null n_seg");
+  if (n_seg[0] != 0 || n_seg[n_segs] != N)
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: n_seg must run from 0 to N");
+  for (int i = 0; i < n_segs; ++i)
+    if (n_seg[i + 1] <= n_seg[i]) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: n_seg must increase");
+  if (M == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !w_gs || !group_offsets || !out)
+    return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: null pointer");
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
+      !aligned(out, 16) || !aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(group_offsets, 4) ||
+      !aligned(a_row_index, 4))
+    return fail(NVFP4_EALIGN, "nvfp4_grouped_gemm: codes and out must be 16-byte aligned, scales 4-byte");
+  nvfp4::GemmArgs a;
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.a_gs = a_gs;
+  a.a_rows = a_row_index ? a_rows : M;
+  a.a_row_index = a_row_index;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.w_gs = w_gs;
+  for (int i = 0; i < 5; ++i) a.n_seg[i] = i <= n_segs ? n_seg[i] : (int32_t)N;
+  a.n_segs = n_segs;
+  a.group_offsets = group_offsets;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.out = out;
+  a.out_bf16 = out_dtype == NVFP4_DTYPE_BF16;
+  a.ld_out = ld_out;
+  hipStream_t s = (hipStream_t)stream;
+  return finish("nvfp4_grouped_gemm", nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I, int64_t ld,
+                         const float* gs_h, uint8_t* h_codes, uint8_t* h_scales, void* stream) {
+  const int es = elem_size(in_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "silu_mul_requant: unknown dtype %d", in_dtype);
+  if (M < 0 || I < 0) return fail(NVFP4_ESHAPE, "silu_mul_requant: negative size");
+  if (I % 16) return fail(NVFP4_ESHAPE, "silu_mul_requant: I must be a multiple of 16");
+  if (ld < 2 * I) return fail(NVFP4_ESHAPE, "silu_mul_requant: ld < 2*I");
+  if (M == 0 || I == 0) return NVFP4_OK;
+  if (!gate_up || !gs_h || !h_codes || !h_scales) return fail(NVFP4_EINVAL, "silu_mul_requant: null pointer");
+  if (!aligned(gate_up, 16) || (ld * es) % 16 || !aligned(h_codes, 8) || !aligned(gs_h, 4))
+    return fail(NVFP4_EALIGN, "silu_mul_requant: gate_up and its pitch must be 16-byte aligned, codes 8-byte");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("silu_mul_requant",
+                nvfp4::launch_silu_mul_requant(gate_up, in_dtype == NVFP4_DTYPE_BF16, M, I, ld, gs_h, h_codes,
+                                               h_scales, s),
+                s);
+}
+
+size_t silu_mul_global_scale_workspace_size(int64_t M, int64_t I) {
+  if (M < 0 || I < 0) return 0;
+  return (size_t)nvfp4::silu_amax_chunks(M, I) * sizeof(float);
+}
+
+int32_t silu_mul_global_scale(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I, int64_t ld,
+                              float* gs_out, void* ws, size_t ws_bytes, void* stream) {
+  const int es = elem_size(in_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "silu_mul_global_scale: unknown dtype %d", in_dtype);
+  if (M < 0 || I < 0) return fail(NVFP4_ESHAPE, "silu_mul_global_scale: negative size");
+  if (I % 16) return fail(NVFP4_ESHAPE, "silu_mul_global_scale: I must be a multiple of 16");
+  if (ld < 2 * I) return fail(NVFP4_ESHAPE, "silu_mul_global_scale: ld < 2*I");
+  if (!gs_out || !ws) return fail(NVFP4_EINVAL, "silu_mul_global_scale: null pointer");
+  if (M > 0 && I > 0 && !gate_up) return fail(NVFP4_EINVAL, "silu_mul_global_scale: null pointer");
+  if (ws_bytes < silu_mul_global_scale_workspace_size(M, I))
+    return fail(NVFP4_ESHAPE, "silu_mul_global_scale: workspace too small");
+  if (!aligned(gate_up, 16) || (ld * es) % 16 || !aligned(ws, 16) || !aligned(gs_out, 4))
+    return fail(NVFP4_EALIGN, "silu_mul_global_scale: gate_up, its pitch and ws must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("silu_mul_global_scale",
+                nvfp4::launch_silu_mul_global_scale(gate_up, in_dtype == NVFP4_DTYPE_BF16, M, I, ld, gs_out,
+                                                    (float*)ws, s),
+                s);
+}
+
+int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm, const float* topk_w, int64_t T,
+                    int32_t k, int64_t H, uint16_t* out, void* stream) {
+  const int es = elem_size(y_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "moe_combine: unknown dtype %d", y_dtype);
+  if (T < 0 || H < 0) return fail(NVFP4_ESHAPE, "moe_combine: negative size");
+  if (k < 1 || k > NVFP4_MAX_TOPK) return fail(NVFP4_ESHAPE, "moe_combine: k=%d outside [1, %d]", k, NVFP4_MAX_TOPK);
+  if (H % 8) return fail(NVFP4_ESHAPE, "moe_combine: H must be a multiple of 8");
+  if (T == 0 || H == 0) return NVFP4_OK;
+  if (!y || !inv_perm || !topk_w || !out) return fail(NVFP4_EINVAL, "moe_combine: null pointer");
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(inv_perm, 4) || !aligned(topk_w, 4))
+    return fail(NVFP4_EALIGN, "moe_combine: y and out must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("moe_combine",
+                nvfp4::launch_combine(y, y_dtype == NVFP4_DTYPE_BF16, inv_perm, topk_w, T, k, H, out, s), s);
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI layer (capi.cpp) and the kernel
+// translation units: small device reductions shared by several kernels, and
+// the host-side launchers each .hip file defines.  Launchers assume their
+// arguments were validated by the C ABI layer and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+#ifdef __HIPCC__
+// Max over a wave64, every lane gets the result.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Max over a block of at most 1024 threads (a multiple of 64); every thread
+// gets the result.  Uses 64 bytes of shared memory.
+__device__ __forceinline__ float block_max(float v) {
+  __shared__ float part[16];
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[w] = v;
+  __syncthreads();
+  const int nw = (blockDim.x + 63) >> 6;
+  float r = 0.0f;
+  for (int i = 0; i < nw; ++i) r = __builtin_fmaxf(r, part[i]);
+  __syncthreads();
+  return r;
+}
+
+// gs = amax / (6 * 448) in the dequantisation direction; 1.0 for amax == 0.
+__device__ __forceinline__ float global_scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+#endif
+
+// --- launchers (defined in the .hip files) --------------------------------
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                           const float* gs, uint8_t* codes, uint8_t* scales, hipStream_t s);
+int64_t amax_chunks(int64_t n);
+hipError_t launch_global_scale(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride,
+                               float* gs_out, float* partial, hipStream_t s);
+
+hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                                float* w, int32_t* offsets, int32_t* sorted_ids, int32_t* inv,
+                                hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_gs;
+  int64_t a_rows;
+  const int32_t* a_row_index;  // nullable
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_gs;
+  int32_t n_seg[5];            // n_seg[0..n_segs], padded with N
+  int32_t n_segs;
+  const int32_t* group_offsets;
+  int32_t G;
+  int64_t M, N, K;
+  void* out;
+  int32_t out_bf16;
+  int64_t ld_out;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+
+hipError_t launch_silu_mul_requant(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
+                                   const float* gs_h, uint8_t* codes, uint8_t* scales, hipStream_t s);
+int64_t silu_amax_chunks(int64_t M, int64_t I);
+hipError_t launch_silu_mul_global_scale(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
+                                        float* gs_out, float* partial, hipStream_t s);
+
+hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const float* w, int64_t T,
+                          int k, int64_t H, uint16_t* out, hipStream_t s);
+
+}  // namespace nvfp4

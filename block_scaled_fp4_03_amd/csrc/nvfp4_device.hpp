@@ -1,0 +1,173 @@
+// Device-side number formats and math shared by the gfx950 kernels.
+//
+// NVFP4: E2M1 element codes (sign bit 3, magnitudes {0,0.5,1,1.5,2,3,4,6}),
+// one E4M3 (FN) scale per 16 elements, one float32 global scale per tensor in
+// the dequantisation direction.  Every float step below is a single IEEE
+// float32 operation; the library is compiled with -ffp-contract=off so no
+// multiply-add is fused behind our back, which keeps the quantised codes,
+// routing weights and combine results identical on every run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// E2M1 encode: magnitude index of a = |v| >= 0, round to nearest with ties to
+// the even index, saturating at index 7 (6.0).  Each comparison adds one when
+// a passes the boundary between two neighbouring magnitudes; a tie stays on
+// the even side, so boundaries below an odd index use '>' and boundaries
+// below an even index use '>='.
+__device__ __forceinline__ uint32_t e2m1_index(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+// E4M3 (FN) code of a finite s >= 0: round to nearest-even on a 3-bit
+// mantissa, saturate at 448 (code 0x7E); never NaN.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (s >= 448.0f) return 0x7Eu;                 // 448..464 rounds to 448; above saturates
+  const uint32_t u = __float_as_uint(s);
+  const int e = (int)(u >> 23) - 127;
+  if (e < -6) {
+    // E4M3 subnormals are m * 2^-9; s * 512 is exact, rint is ties-to-even,
+    // and m == 8 is the smallest normal (code 0x08) as it should be.
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  // Normal: round the float32 mantissa to 3 bits, ties to even.  A carry out
+  // of the mantissa bumps the exponent, which the bit arithmetic does for us.
+  const uint32_t lsb = (u >> 20) & 1u;
+  const uint32_t r = u + 0x7FFFFu + lsb;
+  const uint32_t code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E4M3 (FN) value of a non-negative code; exact.  gfx950 converts OCP E4M3
+// natively (checked over all 256 codes).
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+
+// Quantise one 16-element block.  x: 16 finite floats.  Returns the scale code
+// and writes the 16 packed codes (element 2i in the low nibble) as two words.
+__device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float gs,
+                                                     uint32_t& lo, uint32_t& hi) {
+  float bamax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bamax = __builtin_fmaxf(bamax, __builtin_fabsf(x[i]));
+  const float d = 6.0f * gs;
+  const float s = bamax / d;
+  const uint32_t sq = e4m3_encode(s);
+  const float sf = e4m3_decode(sq);
+  lo = 0u;
+  hi = 0u;
+  if (sf == 0.0f) return 0u;
+  const float r = 1.0f / (sf * gs);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = x[i] * r;
+    const uint32_t c = e2m1_index(__builtin_fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  return sq;
+}
+
+// ---------------------------------------------------------------------------
+// float32 exponential for SiLU and the routing softmax (Cody & Waite, 1980):
+// n = rint(x*log2 e); r = (x - n*L_hi) - n*L_lo with L_hi = 355/512 (exact
+// products for |n| < 2^15) and L_lo = ln 2 - L_hi; p = sum_{j<=8} r^j/j! by
+// Horner; result p * 2^n.  x > 88 gives +Inf, x < -80 gives 0, so finite
+// non-zero results are normal floats.
+__device__ __forceinline__ float exp_f32(float x) {
+  if (x > 88.0f) return __builtin_inff();
+  if (x < -80.0f) return 0.0f;
+  const float kLog2e = 0x1.715476p+0f;    // nearest float to 1/ln 2
+  const float kLnHi = 0x1.63p-1f;        // 355/512
+  const float kLnLo = -0x1.bd0106p-13f;  // ln 2 - 355/512, to float
+  const float n = __builtin_rintf(x * kLog2e);
+  float r = x - n * kLnHi;
+  r = r - n * kLnLo;
+  // 1/j! for j = 8..0, each rounded to float
+  float p = 0x1.a01a02p-16f;                     // 1/8!
+  p = p * r + 0x1.a01a02p-13f;                   // 1/7!
+  p = p * r + 0x1.6c16c2p-10f;                   // 1/6!
+  p = p * r + 0x1.111112p-7f;                    // 1/5!
+  p = p * r + 0x1.555556p-5f;                    // 1/4!
+  p = p * r + 0x1.555556p-3f;                    // 1/3!
+  p = p * r + 0.5f;                                    // 1/2!
+  p = p * r + 1.0f;                                    // 1/1!
+  p = p * r + 1.0f;                                    // 1/0!
+  return __builtin_ldexpf(p, (int)n);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> float (round to nearest-even; inputs are finite).
+__device__ __forceinline__ uint16_t bf16_from_float(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Load 16 consecutive elements (bf16 or f32) as floats.  p must be 16-byte
+// aligned.
+template <bool kBf16>
+__device__ __forceinline__ void load16(const void* p, float (&x)[16]) {
+  if constexpr (kBf16) {
+    const uint4* q = (const uint4*)p;
+    const uint4 a = q[0], b = q[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* q = (const float4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = q[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation for the matrix cores: eight E2M1 codes (one 32-bit word,
+// element 0 in the low nibble) times their block scale, as eight f16 values.
+// The gfx950 convert instruction takes only the exponent of its scale
+// operand, so it is used with scale 1 (exact E2M1 -> f16) and the E4M3 block
+// scale is applied with a packed f16 multiply.  e2m1 * e4m3 has at most five
+// significant bits and lies in [2^-10, 2688], so the f16 product is exact.
+__device__ __forceinline__ half8_t dequant8(uint32_t codes, half2_t sf2) {
+  half8_t r;
+  const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sf2;
+  const half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sf2;
+  const half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sf2;
+  const half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sf2;
+  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
+  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
+  return r;
+}
+
+// E4M3 scale code -> the f16 pair (sf, sf) for dequant8.
+__device__ __forceinline__ half2_t scale_pair(uint32_t code) {
+  const _Float16 h = (_Float16)e4m3_decode(code);     // exact: E4M3 values fit f16
+  half2_t r;
+  r[0] = h;
+  r[1] = h;
+  return r;
+}
+
+}  // namespace nvfp4

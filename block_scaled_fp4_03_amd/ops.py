@@ -1,0 +1,140 @@
+"""Thin torch binding over the C ABI: argument marshalling only.
+
+Every function takes CUDA (HIP) tensors, allocates its outputs with torch
+(device memory is all torch is used for here), and enqueues the library's
+kernels on torch's current stream.  All arithmetic happens in the HIP
+kernels; a missing library or a non-GPU tensor raises.
+"""
+import ctypes
+
+import torch
+
+from . import lib as _lib
+
+_DT = {torch.float32: _lib.DTYPE_F32, torch.bfloat16: _lib.DTYPE_BF16}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("nvfp4moe ops take GPU tensors only")
+
+
+def _dtype(t):
+    if t.dtype not in _DT:
+        raise ValueError("unsupported dtype %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def quantize(x, gs, codes=None, scales=None):
+    """x [rows, cols] f32/bf16 (row pitch x.stride(0)), gs: 1-element f32
+    tensor.  Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16])."""
+    _check_dev(x, gs)
+    rows, cols = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    if codes is None:
+        codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
+    _lib.call("nvfp4_quantize", _p(x), _dtype(x), rows, cols, x.stride(0), _p(gs), _p(codes),
+              _p(scales), _stream())
+    return codes, scales
+
+
+def global_scale(x, out=None):
+    """Per-slice global scales amax/2688 of x [batch, n] (or a 1-D x)."""
+    _check_dev(x)
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    if x2.stride(1) != 1:
+        raise ValueError("x must have unit inner stride")
+    batch, n = x2.shape
+    if out is None:
+        out = torch.empty(batch, dtype=torch.float32, device=x.device)
+    lib = _lib.load()
+    ws_bytes = lib.nvfp4_global_scale_workspace_size(batch, n)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    _lib.call("nvfp4_global_scale", _p(x2), _dtype(x2), batch, n, x2.stride(0), _p(out), _p(ws),
+              ws.numel(), _stream())
+    return out
+
+
+def route_permute(logits, k):
+    """logits [T, E] f32 -> (ids [T,k] i32, w [T,k] f32, offsets [E+1] i32,
+    sorted_token_ids [T*k] i32, inv [T,k] i32)."""
+    _check_dev(logits)
+    if logits.dtype != torch.float32 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous float32")
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T, k, dtype=torch.int32, device=dev)
+    _lib.call("moe_route_permute", _p(logits), T, E, k, _p(ids), _p(w), _p(off), _p(sorted_ids),
+              _p(inv), _stream())
+    return ids, w, off, sorted_ids, inv
+
+
+def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_offsets, M,
+                 a_row_index=None, out_dtype=torch.float32, out=None):
+    """out [M, N] = alpha * A . W^T per group (see nvfp4_grouped_gemm)."""
+    _check_dev(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, group_offsets, a_row_index)
+    G, N, K2 = w_codes.shape
+    K = 2 * K2
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=w_codes.device)
+    seg = (ctypes.c_int32 * len(n_seg))(*[int(v) for v in n_seg])
+    _lib.call("nvfp4_grouped_gemm", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
+              _p(a_row_index), _p(w_codes), _p(w_scales), _p(w_gs), seg, len(n_seg) - 1,
+              _p(group_offsets), G, M, N, K, _p(out), _dtype(out), out.stride(0), _stream())
+    return out
+
+
+def silu_mul_requant(gate_up, gs_h, codes=None, scales=None):
+    """gate_up [M, 2I] f32/bf16 -> NVFP4 h (codes [M, I/2], scales [M, I/16])."""
+    _check_dev(gate_up, gs_h)
+    M, I2 = gate_up.shape
+    I = I2 // 2
+    if codes is None:
+        codes = torch.empty(M, I // 2, dtype=torch.uint8, device=gate_up.device)
+    if scales is None:
+        scales = torch.empty(M, I // 16, dtype=torch.uint8, device=gate_up.device)
+    _lib.call("silu_mul_requant", _p(gate_up), _dtype(gate_up), M, I, gate_up.stride(0), _p(gs_h),
+              _p(codes), _p(scales), _stream())
+    return codes, scales
+
+
+def silu_mul_global_scale(gate_up, out=None):
+    """Global scale amax(SiLU(gate)*up)/2688 of gate_up [M, 2I]."""
+    _check_dev(gate_up)
+    M, I2 = gate_up.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=gate_up.device)
+    lib = _lib.load()
+    ws_bytes = lib.silu_mul_global_scale_workspace_size(M, I)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=gate_up.device)
+    _lib.call("silu_mul_global_scale", _p(gate_up), _dtype(gate_up), M, I, gate_up.stride(0), _p(out),
+              _p(ws), ws.numel(), _stream())
+    return out
+
+
+def combine(y, inv, w, out=None):
+    """y [T*k, H] f32/bf16, inv [T, k], w [T, k] -> out [T, H] bf16."""
+    _check_dev(y, inv, w)
+    T, k = inv.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _lib.call("moe_combine", _p(y), _dtype(y), _p(inv), _p(w), T, k, H, _p(out), _stream())
+    return out

@@ -1,0 +1,121 @@
+"""Compositions of the C-ABI ops into the three workloads of the path.
+
+* routed MoE layer: quantise x -> route + permute -> L1 grouped GEMM over the
+  stacked gate_up weights (gate and up with their own global scales) ->
+  SiLU(gate)*up re-quantised -> L2 grouped GEMM over the down weights (bf16
+  out) -> weighted combine (bf16);
+* shared expert: the same with one group and no routing or combine;
+* MLA projections: one-group GEMMs, the fused q_a+kv weight with two global
+  scales, then q_b.
+Every step is one call into libnvfp4moe.so; torch only provides the buffers
+and the stream.  Weight preparation (drawing seeded weights and quantising
+them with the library's own quantiser) lives here too.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import ops, workloads
+
+
+@dataclass
+class NVFP4Weights:
+    """A stack of G NVFP4 matrices [G, N, K] with per-(group, segment) scales."""
+    codes: torch.Tensor      # uint8 [G, N, K/2]
+    scales: torch.Tensor     # uint8 [G, N, K/16]
+    gs: torch.Tensor         # float32 [G, S]
+    n_seg: tuple             # S+1 column boundaries
+
+    @property
+    def nbytes(self):
+        return self.codes.numel() + self.scales.numel()
+
+
+def quantize_stack(mats, n_seg, device):
+    """Quantise float32 matrices (each [N, K], one global scale per column
+    segment, computed by the library from the segment's amax) into one stack."""
+    G = len(mats)
+    N, K = mats[0].shape
+    S = len(n_seg) - 1
+    codes = torch.empty(G, N, K // 2, dtype=torch.uint8, device=device)
+    scales = torch.empty(G, N, K // 16, dtype=torch.uint8, device=device)
+    gs = torch.empty(G, S, dtype=torch.float32, device=device)
+    for g, m in enumerate(mats):
+        m = m.to(device=device, dtype=torch.float32).contiguous()
+        for s in range(S):
+            r0, r1 = n_seg[s], n_seg[s + 1]
+            ops.global_scale(m[r0:r1].reshape(1, -1), out=gs[g, s:s + 1])
+            ops.quantize(m[r0:r1], gs[g, s:s + 1], codes=codes[g, r0:r1], scales=scales[g, r0:r1])
+    return NVFP4Weights(codes, scales, gs, tuple(n_seg))
+
+
+def moe_weights(wl, device, seed=0, experts=None):
+    """(W1, W2) of a routed workload: W1 stacked gate_up [E, 2I, H] with
+    segments (gate, up), W2 down [E, H, I].  Drawn expert by expert on
+    `device` and quantised there."""
+    E = wl.E if experts is None else experts
+    I, H = wl.I, wl.H
+    gen_dev = device if wl.weights_on_device else "cpu"
+    w1 = NVFP4Weights(torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=device),
+                      torch.empty(E, 2 * I, H // 16, dtype=torch.uint8, device=device),
+                      torch.empty(E, 2, dtype=torch.float32, device=device), (0, I, 2 * I))
+    w2 = NVFP4Weights(torch.empty(E, H, I // 2, dtype=torch.uint8, device=device),
+                      torch.empty(E, H, I // 16, dtype=torch.uint8, device=device),
+                      torch.empty(E, 1, dtype=torch.float32, device=device), (0, H))
+    for e in range(E):
+        for W, f in ((w1, workloads.moe_gate_up), (w2, workloads.moe_down)):
+            m = f(wl, e, seed, gen_dev).to(device)
+            for s in range(len(W.n_seg) - 1):
+                r0, r1 = W.n_seg[s], W.n_seg[s + 1]
+                ops.global_scale(m[r0:r1].reshape(1, -1), out=W.gs[e, s:s + 1])
+                ops.quantize(m[r0:r1], W.gs[e, s:s + 1], codes=W.codes[e, r0:r1], scales=W.scales[e, r0:r1])
+            del m
+    return w1, w2
+
+
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
+    """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
+    1-element f32 tensors.  Returns out [T, H] bf16 (and the stages)."""
+    T, H = x.shape
+    I2 = w1.codes.shape[1]
+    xc, xs = ops.quantize(x, gs_x)
+    ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
+    R = T * k
+    gu = ops.grouped_gemm(xc, xs, gs_x, w1.codes, w1.scales, w1.gs, w1.n_seg, off, R,
+                          a_row_index=sorted_ids, out_dtype=torch.float32)
+    hc, hs = ops.silu_mul_requant(gu, gs_h)
+    y = ops.grouped_gemm(hc, hs, gs_h, w2.codes, w2.scales, w2.gs, w2.n_seg, off, R,
+                         out_dtype=torch.bfloat16)
+    out = ops.combine(y, inv, w)
+    if keep:
+        return out, dict(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv,
+                         gate_up=gu, hc=hc, hs=hs, y=y)
+    return out
+
+
+def shared_expert(x, w1, w2, gs_x, gs_h, keep=False):
+    """Shared expert: one group, no routing.  Returns y [T, H] bf16."""
+    T = x.shape[0]
+    off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
+    xc, xs = ops.quantize(x, gs_x)
+    gu = ops.grouped_gemm(xc, xs, gs_x, w1.codes, w1.scales, w1.gs, w1.n_seg, off, T)
+    hc, hs = ops.silu_mul_requant(gu, gs_h)
+    y = ops.grouped_gemm(hc, hs, gs_h, w2.codes, w2.scales, w2.gs, w2.n_seg, off, T,
+                         out_dtype=torch.bfloat16)
+    if keep:
+        return y, dict(xc=xc, xs=xs, gate_up=gu, hc=hc, hs=hs)
+    return y
+
+
+def mla_projections(x1, x2, w_qakv, w_qb, gs_x1, gs_x2):
+    """MLA projections: x1 [T, 7168] through fused q_a+kv (two segments, two
+    global scales), x2 [T, 1536] through q_b.  Both outputs bf16."""
+    T = x1.shape[0]
+    off = torch.tensor([0, T], dtype=torch.int32, device=x1.device)
+    c1, s1 = ops.quantize(x1, gs_x1)
+    o1 = ops.grouped_gemm(c1, s1, gs_x1, w_qakv.codes, w_qakv.scales, w_qakv.gs, w_qakv.n_seg, off, T,
+                          out_dtype=torch.bfloat16)
+    c2, s2 = ops.quantize(x2, gs_x2)
+    o2 = ops.grouped_gemm(c2, s2, gs_x2, w_qb.codes, w_qb.scales, w_qb.gs, w_qb.n_seg, off, T,
+                          out_dtype=torch.bfloat16)
+    return o1, o2

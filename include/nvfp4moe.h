@@ -1,0 +1,238 @@
+/*
+ * nvfp4moe.h - C ABI of the MI355X (gfx950) NVFP4 mixture-of-experts expert
+ * pipeline.
+ *
+ * The pipeline is: quantise the layer input to NVFP4, route each token to its
+ * top-k experts and group the (token, expert) rows by expert, run the first
+ * grouped GEMM against the stacked gate_up weights, apply SiLU(gate) * up and
+ * re-quantise the intermediate to NVFP4, run the second grouped GEMM against
+ * the down weights, and combine each token's k expert outputs with the routing
+ * weights.  This is the expert pipeline planned on the page "Current Bug: vLLM
+ * produces empty/garbage output" (revision e8b289e, section "Revised Plan: Our
+ * Own NVFP4 Kernels", Phase 1), with 384 experts and top-6 routing in the
+ * full model ("CURRENT_BUG.md - DeepSeek-V4 Blackwell NVFP4", section
+ * "Architecture Notes").  The shared expert is the same pipeline with one
+ * group and no routing, and the MLA projections are one-group GEMMs.
+ *
+ * NVFP4 tensor layout (row-major, C columns, C a multiple of 16):
+ *   codes  uint8 [rows, C/2]   E2M1 codes, element 2i in the LOW nibble of
+ *                              byte i, element 2i+1 in the high nibble;
+ *                              bit 3 of a code is the sign, bits 0-2 index
+ *                              the magnitudes {0,0.5,1,1.5,2,3,4,6}.
+ *   scales uint8 [rows, C/16]  one E4M3 (FN: bias 7, max 448) code per 16
+ *                              consecutive elements of a row, no swizzle.
+ *   gs     float32             one global scale per tensor in the
+ *                              DEQUANTISATION direction:
+ *                              value = gs * e4m3(scale) * e2m1(code).
+ * The direction matters: the page revision a51edd2 ("What the quant method
+ * does") shows a scale used as its own inverse blowing activations up to
+ * NaN.  Here quantisation divides by gs and saturates (block scale 448, code
+ * +-6) instead of overflowing.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is DEVICE memory owned by the caller unless the
+ *     comment says "host".  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream).  Device-side faults surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated on the host before any HIP call; a failing
+ *     check returns a non-zero status and launches nothing.
+ *     nvfp4_last_error() then describes the failure (thread-local string).
+ *   - Index arrays produced on the device (row indices, group offsets) are
+ *     not trusted: kernels clamp them so that no access leaves the buffers
+ *     whose sizes were passed in; out-of-range entries give unspecified
+ *     values, never out-of-bounds accesses.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *   - Calls are deterministic: the same inputs give bit-identical outputs.
+ *   - Setting the environment variable NVFP4MOE_SYNC_CHECK=1 makes every entry
+ *     point synchronise its stream after launching and report kernel faults
+ *     as NVFP4_EHIP (a debugging aid; off by default).
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_EINVAL 1      /* null pointer, unknown enum value, negative size */
+#define NVFP4_ESHAPE 2      /* a size constraint does not hold */
+#define NVFP4_EALIGN 3      /* a pointer is not aligned as required */
+#define NVFP4_EHIP 4        /* the HIP runtime reported an error */
+
+/* Element types of float tensors crossing the boundary. */
+#define NVFP4_DTYPE_F32 0
+#define NVFP4_DTYPE_BF16 1
+
+/* Upper limits checked by the entry points. */
+#define NVFP4_MAX_EXPERTS 1024
+#define NVFP4_MAX_TOPK 16
+#define NVFP4_MAX_SEGMENTS 4
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t nvfp4_version(void);
+
+/*
+ * nvfp4_quantize - quantise a float tensor to NVFP4 with a given global
+ * scale.
+ *   x        [rows, ld_x] of x_dtype (F32 or BF16); columns [0, cols) are
+ *            quantised.  16-byte aligned, ld_x*elem_size a multiple of 16.
+ *   gs       device pointer to ONE float32, the global scale (dequantisation
+ *            direction, > 0).
+ *   codes    out [rows, cols/2], scales out [rows, cols/16], both dense.
+ * Per 16-element block (each step one IEEE float32 operation, no fused
+ * multiply-add): bamax = max|x_i|; s = bamax / (6*gs); sq = E4M3(s), rounded
+ * to nearest-even and saturated at 448; sf = value(sq).  If sf == 0 every
+ * code of the block is 0x0.  Otherwise r = 1/(sf*gs) and code_i = sign bit of
+ * x_i, plus the E2M1 magnitude nearest to |x_i*r| (ties to the even code,
+ * saturating at 6).
+ * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless
+ * rows >= 0, cols % 16 == 0, ld_x >= cols; EALIGN for misaligned pointers or
+ * row pitch.  rows == 0 or cols == 0 is a no-op.
+ */
+int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                       int64_t ld_x, const float* gs, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/*
+ * nvfp4_global_scale - per-slice global scales from the amax of each slice:
+ * gs[b] = fp32(amax(x[b, 0:n]) / 2688), or 1.0 when the amax is 0
+ * (2688 = 6 * 448 is the largest magnitude one block can encode).  Used for
+ * weights (one scale per projection) and for warmup calibration of
+ * activation scales.
+ *   x        [batch, stride] of x_dtype, slice b = x[b, 0:n]; 16-byte aligned,
+ *            stride*elem_size a multiple of 16, n a multiple of 8.
+ *   gs_out   out [batch] float32.
+ *   ws       workspace of at least nvfp4_global_scale_workspace_size(batch, n)
+ *            bytes (16-byte aligned; may be NULL if that size is 0).
+ * The maximum is order-independent, so the result is exact and deterministic.
+ */
+size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n);
+int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_t n,
+                           int64_t stride, float* gs_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * moe_route_permute - top-k routing and the group-by-expert permutation.
+ *   logits            [T, E] float32 router logits.
+ *   topk_ids          out [T, k] int32: slot 0 is the largest logit; equal
+ *                     logits are ordered by expert id (lower first).
+ *   topk_w            out [T, k] float32: softmax over the k selected logits,
+ *                     w_j = e_j / sum with e_j = exp(l_j - l_0) (float32
+ *                     exponential by Cody-Waite reduction and a degree-8
+ *                     Taylor polynomial, 0 below -80) and the sum taken in
+ *                     slot order.
+ *   expert_offsets    out [E+1] int32: rows of expert e are
+ *                     [expert_offsets[e], expert_offsets[e+1]).
+ *   sorted_token_ids  out [T*k] int32: token of each permuted row; within an
+ *                     expert rows follow the flat index t*k + j.
+ *   inv_perm          out [T, k] int32: the permuted row holding (t, j).
+ * Top-k and scatter are what the routed experts have and the shared expert
+ * lacks (page "Current Bug: vLLM produces empty/garbage output", e8b289e,
+ * section "Phase 1: CuTeDSL Shared Expert Kernel").
+ * Errors: EINVAL for null pointers; ESHAPE unless T >= 0,
+ * 1 <= E <= NVFP4_MAX_EXPERTS, 1 <= k <= min(E, NVFP4_MAX_TOPK),
+ * T*k < 2^31.  T == 0 writes expert_offsets = 0 and nothing else.
+ */
+int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
+                          int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                          int32_t* sorted_token_ids, int32_t* inv_perm, void* stream);
+
+/*
+ * nvfp4_grouped_gemm - grouped GEMM of two NVFP4 operands.
+ *   For every group g and every row m in [group_offsets[g], group_offsets[g+1]):
+ *     out[m, n] = alpha(g, n) * sum_k A[m, k] * W[g, n, k]
+ *   where A and W are the block-scaled values e2m1 * e4m3 (without global
+ *   scales) and alpha(g, n) = fp32(a_gs * w_gs[g, s]) for the column segment
+ *   s with n_seg[s] <= n < n_seg[s+1].  This is the epilogue factor
+ *   activation-global-scale x weight-global-scale of page revision a51edd2
+ *   ("What the quant method does"); the per-segment weight scales are the
+ *   page's dual global scales for fused weights (gate+up, q_a+kv; e8b289e,
+ *   "Phase 2: CuTeDSL Attention Kernel").  Products are exact and sums are
+ *   float32 (matrix-core accumulation), so results agree with the exact
+ *   contraction to float32 summation error, not bitwise.
+ *   a_codes, a_scales  A storage, [a_rows, K/2] and [a_rows, K/16].
+ *   a_gs               ONE float32.
+ *   a_row_index        [M] int32 or NULL: logical row m reads stored row
+ *                      a_row_index[m] (the gather by sorted_token_ids);
+ *                      NULL means row m is stored row m (then a_rows >= M).
+ *   w_codes, w_scales  [G, N, K/2], [G, N, K/16].
+ *   w_gs               [G, n_segs] float32.
+ *   n_seg              HOST array of n_segs+1 int32: 0 = n_seg[0] < ... <
+ *                      n_seg[n_segs] = N.
+ *   group_offsets      [G+1] int32, non-decreasing, 0 .. M.
+ *   out                [M, ld_out] of out_dtype (F32 or BF16, rounded to
+ *                      nearest-even), columns [0, N) written; rows outside
+ *                      every group are left untouched.
+ * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless
+ * 1 <= G <= NVFP4_MAX_EXPERTS, 1 <= n_segs <= NVFP4_MAX_SEGMENTS, M >= 0,
+ * N >= 1, K >= 32 with K % 32 == 0, ld_out >= N, a_rows >= 0 (and >= M when
+ * a_row_index is NULL), n_seg increasing from 0 to N; EALIGN unless codes
+ * and scales are 4-byte aligned and out is 16-byte aligned.
+ */
+int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                           int64_t a_rows, const int32_t* a_row_index,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                           const int32_t* n_seg, int32_t n_segs,
+                           const int32_t* group_offsets, int32_t G,
+                           int64_t M, int64_t N, int64_t K,
+                           void* out, int32_t out_dtype, int64_t ld_out, void* stream);
+
+/*
+ * silu_mul_requant - h = SiLU(gate) * up, re-quantised to NVFP4.
+ *   gate_up  [M, ld] of in_dtype (F32 or BF16): gate in columns [0, I), up in
+ *            [I, 2I) (the stacked gate_up order).
+ *   gs_h     ONE float32, the global scale of h.
+ *   h_codes  out [M, I/2]; h_scales out [M, I/16].
+ * Per element in float32, each step one IEEE operation: e = exp(-g) (the
+ * same exponential as moe_route_permute, +Inf above 88), s = g / (1 + e),
+ * h = s * u; then the quantisation of nvfp4_quantize with gs_h.
+ * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless M >= 0,
+ * I % 16 == 0, ld >= 2I; EALIGN unless gate_up is 16-byte aligned and
+ * ld*elem_size is a multiple of 16.
+ */
+int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I,
+                         int64_t ld, const float* gs_h, uint8_t* h_codes, uint8_t* h_scales,
+                         void* stream);
+
+/*
+ * silu_mul_global_scale - gs_out = fp32(amax(SiLU(gate)*up) / 2688) (1.0 if
+ * the amax is 0), with h computed exactly as in silu_mul_requant: the warmup
+ * calibration of the intermediate's global scale.
+ *   ws  workspace of silu_mul_global_scale_workspace_size(M, I) bytes.
+ */
+size_t silu_mul_global_scale_workspace_size(int64_t M, int64_t I);
+int32_t silu_mul_global_scale(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I,
+                              int64_t ld, float* gs_out, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * moe_combine - weighted sum of each token's k expert outputs.
+ *   y        [T*k, H] of y_dtype (F32 or BF16), permuted rows.
+ *   inv_perm [T, k] int32, topk_w [T, k] float32 (from moe_route_permute).
+ *   out      [T, H] bf16 (uint16 storage).
+ * out[t] = bf16(acc) with acc = w_0*y[inv[t,0]], then acc = acc + w_j*y[inv[t,j]]
+ * for j = 1..k-1, each product and sum a separate float32 operation, one
+ * rounding to bf16 (nearest-even) at the end.  The page keeps the final
+ * scatter in BF16 (e8b289e, "Phase 3: Clean up").
+ * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless T >= 0,
+ * 1 <= k <= NVFP4_MAX_TOPK, H % 8 == 0; EALIGN unless y and out are 16-byte
+ * aligned.
+ */
+int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm,
+                    const float* topk_w, int64_t T, int32_t k, int64_t H, uint16_t* out,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

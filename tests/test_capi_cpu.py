@@ -1,0 +1,116 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_03_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", src))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("library not built")
+    return lib.load()
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_version(L):
+    assert L.nvfp4_version() >= 100
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+
+
+def _err(L):
+    return L.nvfp4_last_error().decode()
+
+
+def test_quantize_validation(L):
+    assert L.nvfp4_quantize(FAKE, 7, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 24, 24, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert "multiple of 16" in _err(L)
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 32, 16, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert L.nvfp4_quantize(NULL, lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_quantize(ctypes.c_void_p(0x1004), lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE,
+                            NULL) == lib.EALIGN
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 0, 32, 32, NULL, NULL, NULL, NULL) == lib.OK
+
+
+def test_route_validation(L):
+    f = L.moe_route_permute
+    assert f(FAKE, 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 2000, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 384, 17, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert f(FAKE, -1, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert f(NULL, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert f(FAKE, 4, 8, 2, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == lib.EINVAL
+
+
+def _gemm(L, **kw):
+    a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, w_codes=FAKE,
+             w_scales=FAKE, w_gs=FAKE, n_seg=[0, 64], group_offsets=FAKE, G=1, M=8, N=64, K=64,
+             out=FAKE, out_dtype=lib.DTYPE_F32, ld_out=64)
+    a.update(kw)
+    seg = (ctypes.c_int32 * len(a["n_seg"]))(*a["n_seg"])
+    return L.nvfp4_grouped_gemm(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"],
+                                a["w_codes"], a["w_scales"], a["w_gs"], seg, len(a["n_seg"]) - 1,
+                                a["group_offsets"], a["G"], a["M"], a["N"], a["K"], a["out"],
+                                a["out_dtype"], a["ld_out"], NULL)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, K=48) == lib.ESHAPE            # K % 32
+    assert _gemm(L, K=0) == lib.ESHAPE
+    assert _gemm(L, G=0) == lib.ESHAPE
+    assert _gemm(L, G=1025) == lib.ESHAPE
+    assert _gemm(L, n_seg=[0, 32]) == lib.ESHAPE   # does not end at N
+    assert _gemm(L, n_seg=[0, 40, 40, 64]) == lib.ESHAPE
+    assert _gemm(L, n_seg=[0, 8, 16, 24, 32, 64]) == lib.ESHAPE   # 5 segments
+    assert _gemm(L, ld_out=32) == lib.ESHAPE
+    assert _gemm(L, a_rows=4) == lib.ESHAPE        # no row index: need a_rows >= M
+    assert _gemm(L, out_dtype=5) == lib.EINVAL
+    assert _gemm(L, w_codes=NULL) == lib.EINVAL
+    assert _gemm(L, out=ctypes.c_void_p(0x1008)) == lib.EALIGN
+    assert _gemm(L, M=0, a_codes=NULL, out=NULL) == lib.OK
+
+
+def test_silu_and_combine_validation(L):
+    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 24, 48, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert L.silu_mul_requant(FAKE, 3, 4, 32, 64, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 0, 64, FAKE, NULL) == lib.ESHAPE
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 2, 60, FAKE, NULL) == lib.ESHAPE
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, NULL, FAKE, 4, 2, 64, FAKE, NULL) == lib.EINVAL
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 0, 2, 64, NULL, NULL) == lib.OK
+
+
+def test_global_scale_validation_and_workspace(L):
+    assert L.nvfp4_global_scale_workspace_size(0, 100) == 0
+    assert L.nvfp4_global_scale_workspace_size(3, 16384) == 3 * 4
+    assert L.nvfp4_global_scale_workspace_size(1, 16384 * 5000) == 1024 * 4
+    assert L.nvfp4_global_scale(FAKE, lib.DTYPE_F32, 2, 12, 16, FAKE, FAKE, 64, NULL) == lib.ESHAPE
+    assert L.nvfp4_global_scale(FAKE, lib.DTYPE_F32, 2, 16, 16, FAKE, FAKE, 0, NULL) == lib.ESHAPE
+    assert L.silu_mul_global_scale(FAKE, lib.DTYPE_F32, 4, 20, 40, FAKE, FAKE, 64, NULL) == lib.ESHAPE

@@ -1,0 +1,255 @@
+"""Op-level parity of the HIP library against the oracle on seeded inputs:
+bit-exact for quantised codes, scales, routing and permutation, SiLU-requant
+and combine; the float32 summation bound for the grouped GEMM.  Shapes cover
+several tiles, ragged tails, empty groups and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import (F32, bf16_tensor, check_gemm, dev, exact_gemm_rows, log, oracle_nvfp4, to_np)
+from block_scaled_fp4_03_amd import ops
+from oracle import formats, moe, quant
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(rows, cols, seed, outliers=True, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
+    if outliers and x.size >= 1000:
+        pos = rng.choice(x.size, x.size // 1000, replace=False)
+        x.reshape(-1)[pos] *= 20
+    if rows > 1 and cols >= 32:
+        x[0, :16] = 0.0
+        x[1, 16:32] *= np.float32(1e-7)
+    return formats.bf16_round(x)
+
+
+# --- quantise ---------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,dtype", [(1, 16, "bf16"), (7, 48, "f32"), (33, 256, "bf16"),
+                                             (300, 7168, "bf16"), (64, 3072, "f32")])
+def test_quantize_bit_exact(rows, cols, dtype):
+    log("quantize", rows, cols, dtype)
+    x = _x(rows, cols, rows + cols)
+    gs = quant.global_scale(quant.amax(x))
+    c_ref, s_ref = quant.quantize(x, gs)
+    xt = bf16_tensor(x, dev()) if dtype == "bf16" else torch.from_numpy(x).to(dev())
+    gst = torch.tensor([gs], dtype=torch.float32, device=dev())
+    c, s = ops.quantize(xt, gst)
+    assert np.array_equal(to_np(c), c_ref)
+    assert np.array_equal(to_np(s), s_ref)
+
+
+def test_quantize_saturation_and_tiny_gs():
+    log("quantize saturation")
+    x = _x(16, 128, 3)
+    for gs in [F32(0.00025141), F32(1e-6), F32(7.5), F32(1e-30)]:
+        c_ref, s_ref = quant.quantize(x, gs)
+        c, s = ops.quantize(bf16_tensor(x, dev()), torch.tensor([gs], device=dev()))
+        assert np.array_equal(to_np(c), c_ref) and np.array_equal(to_np(s), s_ref), gs
+
+
+def test_quantize_row_pitch_and_empty():
+    log("quantize pitch")
+    x = _x(9, 96, 4)
+    big = np.zeros((9, 128), dtype=np.float32)
+    big[:, :96] = x
+    gs = quant.global_scale(quant.amax(x))
+    t = bf16_tensor(big, dev())[:, :96]
+    c, s = ops.quantize(t, torch.tensor([gs], device=dev()))
+    c_ref, s_ref = quant.quantize(x, gs)
+    assert np.array_equal(to_np(c), c_ref) and np.array_equal(to_np(s), s_ref)
+    c0, s0 = ops.quantize(torch.empty(0, 64, dtype=torch.bfloat16, device=dev()), torch.ones(1, device=dev()))
+    assert c0.shape == (0, 32)
+
+
+def test_global_scale_bit_exact():
+    log("global_scale")
+    x = _x(48, 7168, 5)
+    t = torch.from_numpy(x).to(dev())
+    g = to_np(ops.global_scale(t.reshape(1, -1)))
+    assert g[0] == quant.global_scale(quant.amax(x))
+    rows = to_np(ops.global_scale(t))            # a 2-D tensor: one scale per row
+    assert all(rows[i] == quant.global_scale(quant.amax(x[i])) for i in range(x.shape[0]))
+    g2 = to_np(ops.global_scale(t.reshape(4, -1)))
+    for b in range(4):
+        assert g2[b] == quant.global_scale(quant.amax(x.reshape(4, -1)[b]))
+    gb = to_np(ops.global_scale(bf16_tensor(x, dev()).reshape(-1)))
+    assert gb[0] == g[0]
+    z = to_np(ops.global_scale(torch.zeros(2, 64, device=dev())))
+    assert (z == 1.0).all()
+
+
+# --- routing and permutation --------------------------------------------------
+
+def _route_case(T, E, k, seed, zipf=0.0, ties=False):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if zipf:
+        rank = rng.permutation(E) + 1.0
+        lg = (lg + (-zipf * np.log(rank)).astype(np.float32)).astype(np.float32)
+    if ties:
+        lg = np.round(lg * 2).astype(np.float32) / 2
+        lg[::3] = 0.0
+        lg[1::5, ::2] = -0.0
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k,zipf,ties", [(16, 8, 2, 0, False), (256, 384, 6, 0, False),
+                                             (8192, 384, 6, 1.1, False), (100, 384, 6, 0, True),
+                                             (5, 1, 1, 0, False), (3, 16, 16, 0, True),
+                                             (77, 1024, 16, 0, False), (1, 64, 6, 0, True)])
+def test_route_permute_bit_exact(T, E, k, zipf, ties):
+    log("route", T, E, k, zipf, ties)
+    lg = _route_case(T, E, k, T * 7 + E, zipf, ties)
+    ids_r, w_r = moe.route_topk(lg, k)
+    off_r, srt_r, inv_r = moe.permute(ids_r, E)
+    ids, w, off, srt, inv = ops.route_permute(torch.from_numpy(lg).to(dev()), k)
+    assert np.array_equal(to_np(ids), ids_r)
+    assert np.array_equal(to_np(w).view(np.uint32), w_r.view(np.uint32))
+    assert np.array_equal(to_np(off), off_r)
+    assert np.array_equal(to_np(srt), srt_r)
+    assert np.array_equal(to_np(inv), inv_r)
+
+
+def test_route_permute_empty_batch():
+    ids, w, off, srt, inv = ops.route_permute(torch.empty(0, 8, device=dev()), 2)
+    assert (to_np(off) == 0).all()
+
+
+# --- grouped GEMM ---------------------------------------------------------------
+
+def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=3):
+    log("gemm", counts if len(counts) < 12 else (len(counts), sum(counts)), N, K, n_seg, gather, out_bf16)
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    M = int(sum(counts))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a_rows = M + a_extra if gather else M
+    ac, as_, ags = oracle_nvfp4(_x(max(a_rows, 1), K, seed, outliers=True))
+    ac, as_ = ac[:a_rows], as_[:a_rows]
+    row_index = rng.integers(0, a_rows, M).astype(np.int32) if gather else None
+    S = len(n_seg) - 1
+    wc = np.empty((G, N, K // 2), np.uint8)
+    ws = np.empty((G, N, K // 16), np.uint8)
+    wgs = np.empty((G, S), np.float32)
+    for g in range(G):
+        wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        for s in range(S):
+            r0, r1 = n_seg[s], n_seg[s + 1]
+            c, sc, gg = oracle_nvfp4(wf[r0:r1])
+            wc[g, r0:r1], ws[g, r0:r1], wgs[g, s] = c, sc, gg
+    d = dev()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    out = ops.grouped_gemm(T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), n_seg, T(off), M,
+                           a_row_index=T(row_index) if gather else None,
+                           out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    got = to_np(out)
+    # oracle (the definition) and the float64 pieces for the error bound
+    ref_o = moe.grouped_gemm(ac, as_, ags, wc, ws, wgs, n_seg, off, a_row_index=row_index,
+                             out_dtype="bf16" if out_bf16 else "f32")
+    A_idx = row_index if gather else np.arange(M)
+    worst = 0.0
+    for g in range(G):
+        r0, r1 = off[g], off[g + 1]
+        if r1 == r0:
+            continue
+        ex, ab = exact_gemm_rows(ac[A_idx[r0:r1]], as_[A_idx[r0:r1]], wc[g], ws[g])
+        alpha = np.empty(N)
+        for s in range(S):
+            alpha[n_seg[s]:n_seg[s + 1]] = float(F32(F32(ags) * wgs[g, s]))
+        worst = max(worst, check_gemm(got[r0:r1], ex, ab, alpha[None, :], K, out_bf16, "group %d" % g))
+        # and against the oracle's own rounded output
+        assert np.allclose(got[r0:r1], ref_o[r0:r1], rtol=2 ** -7 if out_bf16 else 1e-4,
+                           atol=np.abs(ref_o[r0:r1]).max() * 1e-4 + 1e-30)
+    log("  max err / rms = %.3g" % worst)
+    return got
+
+
+def test_gemm_one_group_plain():
+    _gemm_case([64], 128, 256, [0, 128], 1)
+
+
+def test_gemm_decode_shaped_many_groups_with_empty():
+    rng = np.random.default_rng(2)
+    counts = rng.integers(0, 12, 40).tolist()
+    counts[3] = 0
+    counts[-1] = 0
+    _gemm_case(counts, 320, 1024, [0, 160, 320], 2, gather=True)
+
+
+def test_gemm_rows_over_16_per_group_and_ragged_n():
+    _gemm_case([17, 1, 33, 0, 5], 200, 512, [0, 100, 200], 3, gather=True, out_bf16=True)
+
+
+def test_gemm_k_tails():
+    for K in (32, 96, 160, 288, 320, 544, 576):
+        _gemm_case([5, 9], 72, K, [0, 72], 4 + K)
+
+
+def test_gemm_tile_kernel_shapes():
+    # enough rows per group for the LDS-tiled kernel; ragged M and N tails
+    _gemm_case([300, 130, 0, 77], 200, 256, [0, 64, 200], 5, gather=True)
+    _gemm_case([513], 384, 512, [0, 384], 6, out_bf16=True)
+
+
+def test_gemm_four_segments_and_bf16():
+    _gemm_case([70, 70], 256, 128, [0, 32, 100, 160, 256], 7, out_bf16=True)
+
+
+def test_gemm_empty_m():
+    d = dev()
+    z = torch.zeros(0, 32, dtype=torch.uint8, device=d)
+    out = ops.grouped_gemm(z, torch.zeros(0, 4, dtype=torch.uint8, device=d), torch.ones(1, device=d),
+                           torch.zeros(1, 16, 32, dtype=torch.uint8, device=d),
+                           torch.zeros(1, 16, 4, dtype=torch.uint8, device=d), torch.ones(1, 1, device=d),
+                           [0, 16], torch.zeros(2, dtype=torch.int32, device=d), 0)
+    assert out.shape == (0, 16)
+
+
+def test_gemm_deterministic():
+    a = _gemm_case([9, 40, 3], 256, 512, [0, 256], 8, gather=True)
+    b = _gemm_case([9, 40, 3], 256, 512, [0, 256], 8, gather=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# --- SiLU-requant and combine ---------------------------------------------------
+
+@pytest.mark.parametrize("M,I,dtype", [(1, 16, "f32"), (37, 128, "f32"), (200, 3072, "f32"), (64, 512, "bf16")])
+def test_silu_mul_requant_bit_exact(M, I, dtype):
+    log("silu", M, I, dtype)
+    rng = np.random.default_rng(M + I)
+    gu = (rng.standard_normal((M, 2 * I)) * 3).astype(np.float32)
+    gu[0, :4] = [0.0, 30.0, -95.0, 89.5]
+    if dtype == "bf16":
+        gu = formats.bf16_round(gu)
+    h = moe.silu_mul(gu)
+    gs = quant.global_scale(quant.amax(h) * F32(0.8))
+    c_ref, s_ref = quant.quantize(h, gs)
+    t = torch.from_numpy(gu).to(dev())
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    c, s = ops.silu_mul_requant(t, torch.tensor([gs], device=dev()))
+    assert np.array_equal(to_np(c), c_ref)
+    assert np.array_equal(to_np(s), s_ref)
+    g = to_np(ops.silu_mul_global_scale(t))
+    assert g[0] == quant.global_scale(quant.amax(h))
+
+
+@pytest.mark.parametrize("T,k,H,dtype", [(16, 2, 256, "bf16"), (256, 6, 7168, "bf16"), (9, 1, 24, "f32"),
+                                         (33, 16, 64, "f32")])
+def test_combine_bit_exact(T, k, H, dtype):
+    log("combine", T, k, H, dtype)
+    rng = np.random.default_rng(T * k)
+    y = formats.bf16_round(rng.standard_normal((T * k, H)).astype(np.float32))
+    if dtype == "f32":
+        y = rng.standard_normal((T * k, H)).astype(np.float32)
+    inv = rng.permutation(T * k).reshape(T, k).astype(np.int32)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    ref = moe.combine(y, inv, w)
+    yt = torch.from_numpy(y).to(dev())
+    if dtype == "bf16":
+        yt = yt.to(torch.bfloat16)
+    out = ops.combine(yt, torch.from_numpy(inv).to(dev()), torch.from_numpy(w).to(dev()))
+    assert np.array_equal(to_np(out).view(np.uint32), ref.view(np.uint32))
