@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Throughput of the NVFP4 MoE expert pipeline on one MI355X.
+
+One step = one pass of the whole routed MoE layer over one batch that is
+already resident in HBM: NVFP4 quantisation of x, top-6 routing and the
+group-by-expert permutation, the L1 grouped GEMM over the stacked gate_up
+weights, SiLU(gate)*up re-quantised to NVFP4, the L2 grouped GEMM over the
+down weights, and the weighted combine back to token order (bf16 out).
+
+Default workload: the decode layer, T=256 tokens, hidden 7168, expert
+intermediate 3072, 384 experts, top-6, seeded synthetic inputs (x ~ N(0,1)
+in bf16, router logits ~ N(0,1), weights ~ N(0, 0.02^2) drawn on the GPU and
+quantised to NVFP4 by the library).  `--workload prefill` runs the T=8192
+layer with Zipf(1.1)-skewed expert popularity; the default run also measures
+it and reports it under "prefill".
+
+Prints ONE JSON line.  `value` is tokens/s of the whole layer; `roofline`
+is the dominant kernel (the L1 grouped GEMM) against its bound; `cpu_baseline`
+is the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/f16 matrix peak, TFLOP/s
+NVFP4_BYTES_PER_ELEM = 0.5 + 1.0 / 16.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "block_scaled_fp4_03_amd", "csrc", "grouped_gemm.hip")
+METRIC = "MoE layer tokens/s + TFLOP/s (% HBM roofline decode, % MFMA peak prefill)"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(GEMM_SRC, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per L1 launch from committed rocprofv3 counter runs (FETCH_SIZE
+    and WRITE_SIZE, scaled by the same counters on a copy of known size), or
+    None when no summary exists or the kernel source changed since."""
+    path = os.path.join(PROFILE_DIR, "grouped_gemm_l1_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+class Layer:
+    """The routed layer on the GPU: weights, inputs, activation scales."""
+
+    def __init__(self, wl, device):
+        import torch
+        from block_scaled_fp4_03_amd import ops, pipeline, workloads
+        self.wl = wl
+        self.dev = device
+        t0 = time.time()
+        self.w1, self.w2 = pipeline.moe_weights(wl, device)
+        torch.cuda.synchronize()
+        self.weight_setup_s = time.time() - t0
+        b = workloads.batch(wl, seed=0)
+        self.x = b["x"].to(device=device, dtype=torch.bfloat16)
+        self.logits = b["logits"].to(device)
+        # activation global scales from the warmup batch (seed 1), computed by
+        # the library: gs_x from amax(x_warm); gs_h from amax(SiLU(g)*u) of the
+        # warmup batch's L1 output
+        warm = workloads.warmup_batch(wl)
+        xw = warm["x"].to(device=device, dtype=torch.bfloat16)
+        self.gs_x = ops.global_scale(xw.reshape(1, -1))
+        xc, xs = ops.quantize(xw, self.gs_x)
+        ids, w, off, srt, inv = ops.route_permute(warm["logits"].to(device), wl.k)
+        gu = ops.grouped_gemm(xc, xs, self.gs_x, self.w1.codes, self.w1.scales, self.w1.gs, self.w1.n_seg,
+                              off, xw.shape[0] * wl.k, a_row_index=srt)
+        self.gs_h = ops.silu_mul_global_scale(gu)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        """One layer pass; if ev is given, record events around each op."""
+        from block_scaled_fp4_03_amd import ops
+        import torch
+        wl = self.wl
+        T = self.x.shape[0]
+        R = T * wl.k
+        rec = (lambda name: ev[name].append(torch.cuda.Event(enable_timing=True)) or ev[name][-1].record()) \
+            if ev is not None else (lambda name: None)
+        rec("start")
+        xc, xs = ops.quantize(self.x, self.gs_x)
+        rec("quantize")
+        ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
+        rec("route_permute")
+        gu = ops.grouped_gemm(xc, xs, self.gs_x, self.w1.codes, self.w1.scales, self.w1.gs, self.w1.n_seg, off, R,
+                              a_row_index=srt)
+        rec("gemm_l1")
+        hc, hs = ops.silu_mul_requant(gu, self.gs_h)
+        rec("silu_mul_requant")
+        y = ops.grouped_gemm(hc, hs, self.gs_h, self.w2.codes, self.w2.scales, self.w2.gs, self.w2.n_seg, off, R,
+                             out_dtype=torch.bfloat16)
+        rec("gemm_l2")
+        out = ops.combine(y, inv, w)
+        rec("combine")
+        self._off = off
+        return out
+
+    def touched_experts(self):
+        import torch
+        off = self._off.cpu().numpy()
+        return int((np.diff(off) > 0).sum())
+
+
+def time_layer(layer, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    names = ["start", "quantize", "route_permute", "gemm_l1", "silu_mul_requant", "gemm_l2", "combine"]
+    ev = {n: [] for n in names}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(steps):
+        layer.step(ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_op = {}
+    for i in range(1, len(names)):
+        a, b = names[i - 1], names[i]
+        per_op[b] = float(np.mean([ev[a][s].elapsed_time(ev[b][s]) for s in range(steps)]))
+    return total_ms / steps, per_op
+
+
+def algorithmic(wl, n_touched):
+    """Algorithmic FLOPs of one layer and bytes of one L1 launch."""
+    T, H, I, k = wl.T, wl.H, wl.I, wl.k
+    R = T * k
+    flops = 6.0 * R * H * I
+    w1_bytes = 2 * I * H * NVFP4_BYTES_PER_ELEM
+    l1_bytes = n_touched * w1_bytes + T * H * NVFP4_BYTES_PER_ELEM + R * 2 * I * 4
+    l1_flops = 4.0 * R * H * I
+    return flops, l1_bytes, l1_flops
+
+
+def run_gpu(workload, steps, warmup):
+    import torch
+    from block_scaled_fp4_03_amd import workloads
+    wl = workloads.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    print("[bench] %s: preparing weights (%d experts) and inputs" % (workload, wl.E), file=sys.stderr, flush=True)
+    layer = Layer(wl, dev)
+    print("[bench] %s: weights ready in %.1fs, timing %d+%d steps" % (workload, layer.weight_setup_s, warmup, steps),
+          file=sys.stderr, flush=True)
+    ms, per_op = time_layer(layer, steps, warmup)
+    n_touched = layer.touched_experts()
+    flops, l1_bytes, l1_flops = algorithmic(wl, n_touched)
+    res = dict(ms=ms, per_op_ms=per_op, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
+               tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl)
+    return res
+
+
+def roofline(res, bound):
+    l1_ms = res["per_op_ms"]["gemm_l1"]
+    if bound == "hbm":
+        ach = res["l1_bytes"] / (l1_ms * 1e-3) / 1e9
+        peak = HBM_PEAK_GBS
+        unit = "GB/s"
+    else:
+        ach = res["l1_flops"] / (l1_ms * 1e-3) / 1e12
+        peak = F16_MFMA_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+            "traffic": measured_traffic(res["wl"].name), "kernel": "nvfp4_grouped_gemm L1 (gate_up)",
+            "kernel_ms": round(l1_ms, 4)}
+
+
+def cpu_baseline(res, n_experts=8):
+    """The oracle timed on the host on a bounded sample: n_experts of the
+    touched experts with all their routed rows (L1, SiLU-requant, L2), plus
+    the per-token steps (quantise, route, permute, combine) for the whole
+    batch; the expert part is scaled by touched/n_experts."""
+    import torch
+    from block_scaled_fp4_03_amd import workloads
+    from oracle import moe, quant
+    layer, wl = res["layer"], res["wl"]
+    x = layer.x.float().cpu().numpy()
+    logits = layer.logits.cpu().numpy()
+    gs_x = np.float32(layer.gs_x.item())
+    gs_h = np.float32(layer.gs_h.item())
+    # untimed: oracle-quantised weights of the sampled experts (from the
+    # same seeded float32 weights the GPU quantised)
+    ids, _ = moe.route_topk(logits, wl.k)
+    experts = sorted(set(ids.reshape(-1).tolist()))[:n_experts]
+    gen = "cuda:0" if wl.weights_on_device else "cpu"
+    w1c, w1s, w1g, w2c, w2s, w2g = [], [], [], [], [], []
+    for e in experts:
+        m1 = workloads.moe_gate_up(wl, e, 0, gen).cpu().numpy()
+        m2 = workloads.moe_down(wl, e, 0, gen).cpu().numpy()
+        gg = quant.global_scale(quant.amax(m1[:wl.I]))
+        gu = quant.global_scale(quant.amax(m1[wl.I:]))
+        cg, sg = quant.quantize(m1[:wl.I], gg)
+        cu, su = quant.quantize(m1[wl.I:], gu)
+        w1c.append(np.concatenate([cg, cu])); w1s.append(np.concatenate([sg, su])); w1g.append([gg, gu])
+        c2, s2, g2 = moe.quantize_weight(m2)
+        w2c.append(c2); w2s.append(s2); w2g.append([g2])
+    w1 = (np.stack(w1c), np.stack(w1s), np.array(w1g, np.float32))
+    w2 = (np.stack(w2c), np.stack(w2s), np.array(w2g, np.float32))
+    # timed: per-token part over the whole batch
+    t0 = time.perf_counter()
+    xq = quant.quantize(x, gs_x)
+    ids, wts = moe.route_topk(logits, wl.k)
+    off, srt, inv = moe.permute(ids, wl.E)
+    t_tok = time.perf_counter() - t0
+    # timed: expert part on the sampled experts with all their rows
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
+    counts = [int(off[e + 1] - off[e]) for e in experts]
+    soff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    t1 = time.perf_counter()
+    gu = moe.grouped_gemm(xq[0], xq[1], gs_x, w1[0], w1[1], w1[2], [0, wl.I, 2 * wl.I], soff,
+                          a_row_index=srt[rows])
+    hq = moe.silu_mul_requant(gu, gs_h)
+    y = moe.grouped_gemm(hq[0], hq[1], gs_h, w2[0], w2[1], w2[2], [0, wl.H], soff, out_dtype="bf16")
+    t_exp = time.perf_counter() - t1
+    # combine over the whole batch with stand-in rows (same arithmetic)
+    yfull = np.zeros((wl.T * wl.k, wl.H), np.float32)
+    yfull[rows] = y
+    t2 = time.perf_counter()
+    moe.combine(yfull, inv, wts)
+    t_tok += time.perf_counter() - t2
+    n_t = res["n_touched"]
+    est = t_tok + t_exp * n_t / len(experts)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"value": round(wl.T / est, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d of %d touched experts with all their %d routed rows (L1, SiLU-requant, L2), "
+                      "scaled by %d/%d; quantise, route, permute and combine over all %d tokens; "
+                      "timed %.1fs of CPU work; host %d logical CPUs" % (
+                          len(experts), n_t, int(sum(counts)), n_t, len(experts), wl.T, t_tok + t_exp,
+                          os.cpu_count())}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    main_res = run_gpu(args.workload, args.steps, args.warmup)
+    bound = "hbm" if args.workload == "decode" else "mfma"
+    wl = main_res["wl"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "%s MoE layer: T=%d, hidden %d, intermediate %d, %d experts, top-%d%s" % (
+            wl.name, wl.T, wl.H, wl.I, wl.E, wl.k, ", Zipf(1.1) expert popularity" if wl.zipf else ""),
+            "tokens": wl.T, "experts_touched": main_res["n_touched"],
+            "weights": "NVFP4 (E2M1 codes, E4M3 scale per 16, FP32 global scale per projection)"},
+        "tflops": round(main_res["tflops"], 2),
+        "per_op_ms": {k: round(v, 4) for k, v in main_res["per_op_ms"].items()},
+        "roofline": roofline(main_res, bound),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(main_res, args.cpu_experts)
+    del main_res
+    if args.workload == "decode" and not args.no_prefill:
+        torch.cuda.empty_cache()
+        pre = run_gpu("prefill", max(3, args.steps // 4), max(1, args.warmup // 2))
+        line["prefill"] = {"value": round(pre["tokens_per_s"], 1), "unit": "tokens/s",
+                           "ms_per_step": round(pre["ms"], 4), "tflops": round(pre["tflops"], 2),
+                           "experts_touched": pre["n_touched"],
+                           "per_op_ms": {k: round(v, 4) for k, v in pre["per_op_ms"].items()},
+                           "roofline": roofline(pre, "mfma")}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
