@@ -68,7 +68,7 @@ class Layer:
         self.wl = wl
         self.dev = device
         t0 = time.time()
-        self.w1, self.w2 = pipeline.moe_weights(wl, device)
+        self.w1, self.w2 = pipeline.moe_weights(wl, device, drop_rows=True)
         torch.cuda.synchronize()
         self.weight_setup_s = time.time() - t0
         b = workloads.batch(wl, seed=0)
@@ -82,8 +82,7 @@ class Layer:
         self.gs_x = ops.global_scale(xw.reshape(1, -1))
         xc, xs = ops.quantize(xw, self.gs_x)
         ids, w, off, srt, inv = ops.route_permute(warm["logits"].to(device), wl.k)
-        gu = ops.grouped_gemm(xc, xs, self.gs_x, self.w1.codes, self.w1.scales, self.w1.gs, self.w1.n_seg,
-                              off, xw.shape[0] * wl.k, a_row_index=srt)
+        gu = self.w1.gemm(xc, xs, self.gs_x, off, xw.shape[0] * wl.k, a_row_index=srt)
         self.gs_h = ops.silu_mul_global_scale(gu)
         torch.cuda.synchronize()
 
@@ -101,13 +100,11 @@ class Layer:
         rec("quantize")
         ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
         rec("route_permute")
-        gu = ops.grouped_gemm(xc, xs, self.gs_x, self.w1.codes, self.w1.scales, self.w1.gs, self.w1.n_seg, off, R,
-                              a_row_index=srt)
+        gu = self.w1.gemm(xc, xs, self.gs_x, off, R, a_row_index=srt)
         rec("gemm_l1")
         hc, hs = ops.silu_mul_requant(gu, self.gs_h)
         rec("silu_mul_requant")
-        y = ops.grouped_gemm(hc, hs, self.gs_h, self.w2.codes, self.w2.scales, self.w2.gs, self.w2.n_seg, off, R,
-                             out_dtype=torch.bfloat16)
+        y = self.w2.gemm(hc, hs, self.gs_h, off, R, out_dtype=torch.bfloat16)
         rec("gemm_l2")
         out = ops.combine(y, inv, w)
         rec("combine")
@@ -263,7 +260,20 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=8)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (x3); used to calibrate the "
+                         "HBM byte counters of rocprofv3 against a transfer of known size")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)

@@ -123,11 +123,14 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
 
 int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                            int64_t a_rows, const int32_t* a_row_index, const uint8_t* w_codes,
-                           const uint8_t* w_scales, const float* w_gs, const int32_t* n_seg,
+                           const uint8_t* w_scales, int32_t w_layout, const float* w_gs, const int32_t* n_seg,
                            int32_t n_segs, const int32_t* group_offsets, int32_t G, int64_t M, int64_t N,
                            int64_t K, void* out, int32_t out_dtype, int64_t ld_out, void* stream) {
   if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
     return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: unknown out dtype %d", out_dtype);
+  if (w_layout != NVFP4_LAYOUT_ROWS && w_layout != NVFP4_LAYOUT_TILED)
+    return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: unknown weight layout %d", w_layout);
+  const bool tiled = w_layout == NVFP4_LAYOUT_TILED;
   if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: G=%d", G);
   if (n_segs < 1 || n_segs > NVFP4_MAX_SEGMENTS)
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: n_segs=%d outside [1, %d]", n_segs, NVFP4_MAX_SEGMENTS);
@@ -135,6 +138,7 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: need M >= 0, N >= 1, K >= 32 and K %% 32 == 0");
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: M and N must be below 2^31");
+  if (tiled && K % 256) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: the tiled layout needs K %% 256 == 0");
   if (ld_out < N) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: ld_out < N");
   if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: a_rows too small");
@@ -144,7 +148,7 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   for (int i = 0; i < n_segs; ++i)
     if (n_seg[i + 1] <= n_seg[i]) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: n_seg must increase");
   if (M == 0) return NVFP4_OK;
-  if (!a_codes || !a_scales || !a_gs || !w_codes || !w_scales || !w_gs || !group_offsets || !out)
+  if (!a_codes || !a_scales || !a_gs || !w_codes || (!tiled && !w_scales) || !w_gs || !group_offsets || !out)
     return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: null pointer");
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
       !aligned(out, 16) || !aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(group_offsets, 4) ||
@@ -157,7 +161,8 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   a.a_rows = a_row_index ? a_rows : M;
   a.a_row_index = a_row_index;
   a.w_codes = w_codes;
-  a.w_scales = w_scales;
+  a.w_scales = tiled ? nullptr : w_scales;
+  a.w_tiled = tiled ? 1 : 0;
   a.w_gs = w_gs;
   for (int i = 0; i < 5; ++i) a.n_seg[i] = i <= n_segs ? n_seg[i] : (int32_t)N;
   a.n_segs = n_segs;
@@ -171,6 +176,22 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   a.ld_out = ld_out;
   hipStream_t s = (hipStream_t)stream;
   return finish("nvfp4_grouped_gemm", nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K) {
+  if (G < 1 || N < 1 || K < 256 || K % 256) return 0;
+  return (size_t)nvfp4::prepared_bytes(G, N, K);
+}
+
+int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t G, int64_t N, int64_t K,
+                              uint8_t* out, void* stream) {
+  if (G < 1 || N < 1 || K < 256 || K % 256)
+    return fail(NVFP4_ESHAPE, "nvfp4_prepare_weights: need G >= 1, N >= 1, K >= 256 and K %% 256 == 0");
+  if (!w_codes || !w_scales || !out) return fail(NVFP4_EINVAL, "nvfp4_prepare_weights: null pointer");
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(out, 16))
+    return fail(NVFP4_EALIGN, "nvfp4_prepare_weights: buffers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish("nvfp4_prepare_weights", nvfp4::launch_prepare(w_codes, w_scales, G, N, K, out, s), s);
 }
 
 int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I, int64_t ld,

@@ -103,7 +103,7 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8
 // contiguous bytes of codes and one 4-byte word of scales of its row, and
 // MFMA j (0..7) takes word j of those bytes (block scale byte j / 2).  The
 // tail (K % 256) runs K-steps of 32 with lane q feeding [kt + 8q, kt + 8q + 8).
-template <int NBW>
+template <int NBW, bool kTiled>
 __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) {
   constexpr int BN = 4 * NBW * 16;
   const int lane = threadIdx.x & 63;
@@ -129,15 +129,25 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
   const uint8_t* a_c = p.a_codes + a_row * KB;
   const uint8_t* a_s = p.a_scales + a_row * KS;
 
-  // W rows (output columns) of this lane
+  // W rows (output columns) of this lane.  Row-major: the lane's own row.
+  // Tiled: the first tile of the lane's 16-row block (the lane offset inside
+  // a tile is added at load time); tiles of one block follow each other in k.
   const uint8_t* w_c[NBW];
   const uint8_t* w_s[NBW];
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
-    const int64_t n = clampv<int64_t>(n0 + cb * 16 + r, 0, p.N - 1);
-    const int64_t wr = (int64_t)g * p.N + n;
-    w_c[cb] = p.w_codes + wr * KB;
-    w_s[cb] = p.w_scales + wr * KS;
+    if constexpr (kTiled) {
+      const int64_t nb_per_g = (p.N + 15) / 16;
+      int64_t nb = (n0 + cb * 16) / 16;
+      nb = nb < nb_per_g ? nb : nb_per_g - 1;
+      w_c[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes;
+      w_s[cb] = w_c[cb];
+    } else {
+      const int64_t n = clampv<int64_t>(n0 + cb * 16 + r, 0, p.N - 1);
+      const int64_t wr = (int64_t)g * p.N + n;
+      w_c[cb] = p.w_codes + wr * KB;
+      w_s[cb] = p.w_scales + wr * KS;
+    }
   }
 
   floatx4_t acc[NBW];
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
 
   // The 256-step loads one 4-byte word of scales per lane, which needs the
   // scale rows (K/16 bytes) to be 4-byte aligned, i.e. K % 64 == 0.
-  const int64_t K256 = K % 64 == 0 ? K - K % 256 : 0;
+  const int64_t K256 = kTiled ? K : (K % 64 == 0 ? K - K % 256 : 0);
   if (K256 > 0) {
     // software pipeline: the next step's bytes are in flight while the
     // current step is dequantised and multiplied
@@ -167,9 +177,16 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
       }
 #pragma unroll
       for (int cb = 0; cb < NBW; ++cb) {
-        d0[cb] = __builtin_nontemporal_load((const u32x4*)(w_c[cb] + cofs));
-        d1[cb] = __builtin_nontemporal_load((const u32x4*)(w_c[cb] + cofs + 16));
-        sw[cb] = __builtin_nontemporal_load((const uint32_t*)(w_s[cb] + sofs));
+        if constexpr (kTiled) {
+          const uint8_t* t = w_c[cb] + (kb / 256) * kTileBytes;
+          d0[cb] = *(const u32x4*)(t + 16 * lane);
+          d1[cb] = *(const u32x4*)(t + 1024 + 16 * lane);
+          sw[cb] = *(const uint32_t*)(t + 2048 + 4 * lane);
+        } else {
+          d0[cb] = *(const u32x4*)(w_c[cb] + cofs);
+          d1[cb] = *(const u32x4*)(w_c[cb] + cofs + 16);
+          sw[cb] = *(const uint32_t*)(w_s[cb] + sofs);
+        }
       }
     };
     load(0, ac0, ac1, as, wc0, wc1, ws);
@@ -241,6 +258,7 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
 // word s of those bytes.
 constexpr int TBM = 128, TBN = 128, TBK = 64;
 
+template <bool kTiled>
 __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   __shared__ uint8_t lds_ac[2][TBM * 32];
   __shared__ uint8_t lds_wc[2][TBN * 32];
@@ -271,8 +289,22 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   int64_t a_row = a_ok ? (p.a_row_index ? (int64_t)p.a_row_index[am] : am) : 0;
   a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
   const uint8_t* a_c = p.a_codes + a_row * KB + 16 * chalf;
-  const int64_t wn_row = (int64_t)g * p.N + clampv<int64_t>(n0 + crow, 0, p.N - 1);
-  const uint8_t* w_c = p.w_codes + wn_row * KB + 16 * chalf;
+  // W codes: row-major, thread t moves 16 B of row t / 2 like A.  Tiled,
+  // thread t takes 16-row block t / 32, half (t / 16) % 2, row t % 16: the
+  // k-step of 64 is one quarter (q' = ks % 4) of a 256-k tile, whose halves
+  // sit at 256 q' + 16 r and 1024 + 256 q' + 16 r.
+  const int w_lds_row = kTiled ? ((tid >> 5) * 16 + (tid & 15)) : crow;
+  const int w_half = kTiled ? ((tid >> 4) & 1) : chalf;
+  const int64_t nb_per_g = (p.N + 15) / 16;
+  const uint8_t* w_c;
+  if constexpr (kTiled) {
+    int64_t nb = n0 / 16 + (tid >> 5);
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    w_c = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes + 1024 * w_half + 16 * (tid & 15);
+  } else {
+    const int64_t wn_row = (int64_t)g * p.N + clampv<int64_t>(n0 + crow, 0, p.N - 1);
+    w_c = p.w_codes + wn_row * KB + 16 * chalf;
+  }
   const int srow = tid & 127;
   const uint8_t* s_src;
   if (tid < 128) {
@@ -280,6 +312,10 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
     int64_t sr = sm < row1 ? (p.a_row_index ? (int64_t)p.a_row_index[sm] : sm) : 0;
     sr = clampv<int64_t>(sr, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
     s_src = p.a_scales + sr * KS;
+  } else if constexpr (kTiled) {
+    int64_t nb = n0 / 16 + (srow >> 4);
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    s_src = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes + 2048 + 4 * (srow & 15);
   } else {
     s_src = p.w_scales + ((int64_t)g * p.N + clampv<int64_t>(n0 + srow, 0, p.N - 1)) * KS;
   }
@@ -295,12 +331,19 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   uint32_t rs;
   auto gload = [&](int64_t ks) {
     ra = *(const u32x4*)(a_c + ks * 32);
-    rw = __builtin_nontemporal_load((const u32x4*)(w_c + ks * 32));
-    rs = *(const uint32_t*)(s_src + ks * 4);
+    if constexpr (kTiled) {
+      const int64_t tofs = (ks >> 2) * kTileBytes + 256 * (ks & 3);
+      rw = *(const u32x4*)(w_c + tofs);
+      rs = tid < 128 ? *(const uint32_t*)(s_src + ks * 4)
+                     : *(const uint32_t*)(s_src + (ks >> 2) * kTileBytes + 64 * (ks & 3));
+    } else {
+      rw = *(const u32x4*)(w_c + ks * 32);
+      rs = *(const uint32_t*)(s_src + ks * 4);
+    }
   };
   auto lstore = [&](int buf) {
     *(u32x4*)(&lds_ac[buf][crow * 32 + 16 * chalf]) = ra;
-    *(u32x4*)(&lds_wc[buf][crow * 32 + 16 * chalf]) = rw;
+    *(u32x4*)(&lds_wc[buf][w_lds_row * 32 + 16 * w_half]) = rw;
     if (tid < 128) lds_as[buf][srow] = rs;
     else lds_ws[buf][srow] = rs;
   };
@@ -364,12 +407,19 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (many_rows) {
     const int64_t n_tiles = (a.N + TBN - 1) / TBN;
     const int64_t slots = (a.M + TBM - 1) / TBM + a.G;
-    hipLaunchKernelGGL(gemm_tile, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
+    if (a.w_tiled)
+      hipLaunchKernelGGL(gemm_tile<true>, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
+    else
+      hipLaunchKernelGGL(gemm_tile<false>, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
   } else {
     constexpr int NBW = 4;
     const int64_t n_tiles = (a.N + 4 * NBW * 16 - 1) / (4 * NBW * 16);
     const int64_t slots = (a.M + 15) / 16 + a.G;
-    hipLaunchKernelGGL(gemm_rows16<NBW>, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
+    if (a.w_tiled)
+      hipLaunchKernelGGL((gemm_rows16<NBW, true>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
+    else
+      hipLaunchKernelGGL((gemm_rows16<NBW, false>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a,
+                         n_tiles);
   }
   return hipGetLastError();
 }

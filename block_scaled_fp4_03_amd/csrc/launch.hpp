@@ -38,6 +38,10 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
 }
 #endif
 
+// Bytes of one tile of the prepared (tiled) weight layout: 16 rows x 256 k
+// of codes (2048 B) and their scales (256 B).
+constexpr int kTileBytes = 2304;
+
 // --- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
                            const float* gs, uint8_t* codes, uint8_t* scales, hipStream_t s);
@@ -49,14 +53,19 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, in
                                 float* w, int32_t* offsets, int32_t* sorted_ids, int32_t* inv,
                                 hipStream_t s);
 
+int64_t prepared_bytes(int64_t G, int64_t N, int64_t K);
+hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int64_t G, int64_t N, int64_t K,
+                          uint8_t* out, hipStream_t s);
+
 struct GemmArgs {
   const uint8_t* a_codes;
   const uint8_t* a_scales;
   const float* a_gs;
   int64_t a_rows;
   const int32_t* a_row_index;  // nullable
-  const uint8_t* w_codes;
-  const uint8_t* w_scales;
+  const uint8_t* w_codes;      // row-major codes, or the tiled buffer
+  const uint8_t* w_scales;     // row-major scales (unused when tiled)
+  int32_t w_tiled;             // 1: w_codes is the prepared tiled layout
   const float* w_gs;
   int32_t n_seg[5];            // n_seg[0..n_segs], padded with N
   int32_t n_segs;

@@ -7,6 +7,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe
 
 OK, EINVAL, ESHAPE, EALIGN, EHIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
+LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 MAX_EXPERTS, MAX_TOPK, MAX_SEGMENTS = 1024, 16, 4
 
 _P = ctypes.c_void_p
@@ -22,8 +23,10 @@ SIGNATURES = {
     "nvfp4_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
-    "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, ctypes.POINTER(_I32), _I32,
+    "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,
                                   _P, _I32, _I64, _I64, _I64, _P, _I32, _I64, _P]),
+    "nvfp4_prepared_weight_bytes": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_prepare_weights": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "silu_mul_requant": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P]),
     "silu_mul_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "silu_mul_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),

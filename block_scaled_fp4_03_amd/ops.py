@@ -85,17 +85,40 @@ def route_permute(logits, k):
     return ids, w, off, sorted_ids, inv
 
 
-def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_offsets, M,
-                 a_row_index=None, out_dtype=torch.float32, out=None):
-    """out [M, N] = alpha * A . W^T per group (see nvfp4_grouped_gemm)."""
-    _check_dev(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, group_offsets, a_row_index)
+def prepared_weight_bytes(G, N, K):
+    return _lib.load().nvfp4_prepared_weight_bytes(G, N, K)
+
+
+def prepare_weights(w_codes, w_scales, out=None):
+    """Row-major NVFP4 weights [G, N, K/2] + [G, N, K/16] -> the tiled buffer
+    (uint8, 1-D) that grouped_gemm streams (see nvfp4_prepare_weights)."""
+    _check_dev(w_codes, w_scales)
     G, N, K2 = w_codes.shape
     K = 2 * K2
     if out is None:
-        out = torch.empty(M, N, dtype=out_dtype, device=w_codes.device)
+        out = torch.empty(prepared_weight_bytes(G, N, K), dtype=torch.uint8, device=w_codes.device)
+    _lib.call("nvfp4_prepare_weights", _p(w_codes), _p(w_scales), G, N, K, _p(out), _stream())
+    return out
+
+
+def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_offsets, M,
+                 a_row_index=None, out_dtype=torch.float32, out=None, w_tiled=None):
+    """out [M, N] = alpha * A . W^T per group (see nvfp4_grouped_gemm).
+    w_codes/w_scales give G, N, K; if w_tiled (the prepare_weights buffer) is
+    passed, the kernel reads the weights from it instead."""
+    _check_dev(a_codes, a_scales, a_gs, w_gs, group_offsets, a_row_index, w_tiled)
+    G, N, K2 = w_codes.shape
+    K = 2 * K2
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
     seg = (ctypes.c_int32 * len(n_seg))(*[int(v) for v in n_seg])
+    if w_tiled is not None:
+        wc, ws, layout = w_tiled, None, _lib.LAYOUT_TILED
+    else:
+        _check_dev(w_codes, w_scales)
+        wc, ws, layout = w_codes, w_scales, _lib.LAYOUT_ROWS
     _lib.call("nvfp4_grouped_gemm", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
-              _p(a_row_index), _p(w_codes), _p(w_scales), _p(w_gs), seg, len(n_seg) - 1,
+              _p(a_row_index), _p(wc), _p(ws), layout, _p(w_gs), seg, len(n_seg) - 1,
               _p(group_offsets), G, M, N, K, _p(out), _dtype(out), out.stride(0), _stream())
     return out
 

@@ -20,15 +20,35 @@ from . import ops, workloads
 
 @dataclass
 class NVFP4Weights:
-    """A stack of G NVFP4 matrices [G, N, K] with per-(group, segment) scales."""
+    """A stack of G NVFP4 matrices [G, N, K] with per-(group, segment) scales.
+
+    `tiled`, when set, is the same weights rearranged by prepare_weights; the
+    GEMM then streams it instead of the row-major codes and scales (which may
+    be dropped to save memory: `codes`/`scales` then keep only their shape)."""
     codes: torch.Tensor      # uint8 [G, N, K/2]
     scales: torch.Tensor     # uint8 [G, N, K/16]
     gs: torch.Tensor         # float32 [G, S]
     n_seg: tuple             # S+1 column boundaries
+    tiled: torch.Tensor = None
 
     @property
     def nbytes(self):
         return self.codes.numel() + self.scales.numel()
+
+    def prepare(self, drop_rows=False):
+        """Build the tiled copy (K must be a multiple of 256)."""
+        K = self.codes.shape[2] * 2
+        if K % 256 == 0:
+            self.tiled = ops.prepare_weights(self.codes, self.scales)
+            if drop_rows:
+                # keep only the shapes (tensors without storage)
+                self.codes = torch.empty(self.codes.shape, dtype=torch.uint8, device="meta")
+                self.scales = torch.empty(self.scales.shape, dtype=torch.uint8, device="meta")
+        return self
+
+    def gemm(self, a_codes, a_scales, a_gs, group_offsets, M, **kw):
+        return ops.grouped_gemm(a_codes, a_scales, a_gs, self.codes, self.scales, self.gs, self.n_seg,
+                                group_offsets, M, w_tiled=self.tiled, **kw)
 
 
 def quantize_stack(mats, n_seg, device):
@@ -46,13 +66,14 @@ def quantize_stack(mats, n_seg, device):
             r0, r1 = n_seg[s], n_seg[s + 1]
             ops.global_scale(m[r0:r1].reshape(1, -1), out=gs[g, s:s + 1])
             ops.quantize(m[r0:r1], gs[g, s:s + 1], codes=codes[g, r0:r1], scales=scales[g, r0:r1])
-    return NVFP4Weights(codes, scales, gs, tuple(n_seg))
+    return NVFP4Weights(codes, scales, gs, tuple(n_seg)).prepare()
 
 
-def moe_weights(wl, device, seed=0, experts=None):
+def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False):
     """(W1, W2) of a routed workload: W1 stacked gate_up [E, 2I, H] with
     segments (gate, up), W2 down [E, H, I].  Drawn expert by expert on
-    `device` and quantised there."""
+    `device` and quantised there; with `tiled`, also rearranged for the GEMM
+    (and with `drop_rows` the row-major copies are released)."""
     E = wl.E if experts is None else experts
     I, H = wl.I, wl.H
     gen_dev = device if wl.weights_on_device else "cpu"
@@ -70,6 +91,9 @@ def moe_weights(wl, device, seed=0, experts=None):
                 ops.global_scale(m[r0:r1].reshape(1, -1), out=W.gs[e, s:s + 1])
                 ops.quantize(m[r0:r1], W.gs[e, s:s + 1], codes=W.codes[e, r0:r1], scales=W.scales[e, r0:r1])
             del m
+    if tiled:
+        w1.prepare(drop_rows)
+        w2.prepare(drop_rows)
     return w1, w2
 
 
@@ -81,11 +105,9 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
     xc, xs = ops.quantize(x, gs_x)
     ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
     R = T * k
-    gu = ops.grouped_gemm(xc, xs, gs_x, w1.codes, w1.scales, w1.gs, w1.n_seg, off, R,
-                          a_row_index=sorted_ids, out_dtype=torch.float32)
+    gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=sorted_ids, out_dtype=torch.float32)
     hc, hs = ops.silu_mul_requant(gu, gs_h)
-    y = ops.grouped_gemm(hc, hs, gs_h, w2.codes, w2.scales, w2.gs, w2.n_seg, off, R,
-                         out_dtype=torch.bfloat16)
+    y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16)
     out = ops.combine(y, inv, w)
     if keep:
         return out, dict(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv,
@@ -98,10 +120,9 @@ def shared_expert(x, w1, w2, gs_x, gs_h, keep=False):
     T = x.shape[0]
     off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
     xc, xs = ops.quantize(x, gs_x)
-    gu = ops.grouped_gemm(xc, xs, gs_x, w1.codes, w1.scales, w1.gs, w1.n_seg, off, T)
+    gu = w1.gemm(xc, xs, gs_x, off, T)
     hc, hs = ops.silu_mul_requant(gu, gs_h)
-    y = ops.grouped_gemm(hc, hs, gs_h, w2.codes, w2.scales, w2.gs, w2.n_seg, off, T,
-                         out_dtype=torch.bfloat16)
+    y = w2.gemm(hc, hs, gs_h, off, T, out_dtype=torch.bfloat16)
     if keep:
         return y, dict(xc=xc, xs=xs, gate_up=gu, hc=hc, hs=hs)
     return y
@@ -113,9 +134,7 @@ def mla_projections(x1, x2, w_qakv, w_qb, gs_x1, gs_x2):
     T = x1.shape[0]
     off = torch.tensor([0, T], dtype=torch.int32, device=x1.device)
     c1, s1 = ops.quantize(x1, gs_x1)
-    o1 = ops.grouped_gemm(c1, s1, gs_x1, w_qakv.codes, w_qakv.scales, w_qakv.gs, w_qakv.n_seg, off, T,
-                          out_dtype=torch.bfloat16)
+    o1 = w_qakv.gemm(c1, s1, gs_x1, off, T, out_dtype=torch.bfloat16)
     c2, s2 = ops.quantize(x2, gs_x2)
-    o2 = ops.grouped_gemm(c2, s2, gs_x2, w_qb.codes, w_qb.scales, w_qb.gs, w_qb.n_seg, off, T,
-                          out_dtype=torch.bfloat16)
+    o2 = w_qb.gemm(c2, s2, gs_x2, off, T, out_dtype=torch.bfloat16)
     return o1, o2

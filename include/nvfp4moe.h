@@ -69,6 +69,10 @@ extern "C" {
 #define NVFP4_DTYPE_F32 0
 #define NVFP4_DTYPE_BF16 1
 
+/* Layouts of the weight operand of nvfp4_grouped_gemm. */
+#define NVFP4_LAYOUT_ROWS 0   /* codes [G, N, K/2] and scales [G, N, K/16], row-major */
+#define NVFP4_LAYOUT_TILED 1  /* one buffer written by nvfp4_prepare_weights */
+
 /* Upper limits checked by the entry points. */
 #define NVFP4_MAX_EXPERTS 1024
 #define NVFP4_MAX_TOPK 16
@@ -164,7 +168,11 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *   a_row_index        [M] int32 or NULL: logical row m reads stored row
  *                      a_row_index[m] (the gather by sorted_token_ids);
  *                      NULL means row m is stored row m (then a_rows >= M).
- *   w_codes, w_scales  [G, N, K/2], [G, N, K/16].
+ *   w_codes, w_scales  [G, N, K/2], [G, N, K/16] when w_layout is
+ *                      NVFP4_LAYOUT_ROWS; when it is NVFP4_LAYOUT_TILED,
+ *                      w_codes is the buffer nvfp4_prepare_weights wrote for
+ *                      the same G, N, K and w_scales is ignored (may be NULL).
+ *                      The two layouts give bit-identical results.
  *   w_gs               [G, n_segs] float32.
  *   n_seg              HOST array of n_segs+1 int32: 0 = n_seg[0] < ... <
  *                      n_seg[n_segs] = N.
@@ -172,19 +180,43 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *   out                [M, ld_out] of out_dtype (F32 or BF16, rounded to
  *                      nearest-even), columns [0, N) written; rows outside
  *                      every group are left untouched.
- * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless
- * 1 <= G <= NVFP4_MAX_EXPERTS, 1 <= n_segs <= NVFP4_MAX_SEGMENTS, M >= 0,
- * N >= 1, K >= 32 with K % 32 == 0, ld_out >= N, a_rows >= 0 (and >= M when
- * a_row_index is NULL), n_seg increasing from 0 to N; EALIGN unless codes
- * and scales are 4-byte aligned and out is 16-byte aligned.
+ * Errors: EINVAL for null pointers, an unknown dtype or layout; ESHAPE
+ * unless 1 <= G <= NVFP4_MAX_EXPERTS, 1 <= n_segs <= NVFP4_MAX_SEGMENTS,
+ * M >= 0, N >= 1, K >= 32 with K % 32 == 0 (K % 256 == 0 for the tiled
+ * layout), ld_out >= N, a_rows >= 1 when M > 0 (and >= M when a_row_index
+ * is NULL), n_seg increasing from 0 to N; EALIGN unless codes (and the tiled
+ * buffer) and out are 16-byte aligned and scales 4-byte aligned.
  */
 int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
                            int64_t a_rows, const int32_t* a_row_index,
-                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gs,
+                           const uint8_t* w_codes, const uint8_t* w_scales, int32_t w_layout,
+                           const float* w_gs,
                            const int32_t* n_seg, int32_t n_segs,
                            const int32_t* group_offsets, int32_t G,
                            int64_t M, int64_t N, int64_t K,
                            void* out, int32_t out_dtype, int64_t ld_out, void* stream);
+
+/*
+ * nvfp4_prepare_weights - rearrange NVFP4 weights [G, N, K] (row-major codes
+ * and scales) into the tiled layout (NVFP4_LAYOUT_TILED) that
+ * nvfp4_grouped_gemm streams with whole-cache-line loads.  It is a pure byte
+ * permutation (plus zero padding of the last 16-row block): the GEMM's
+ * results do not change.  Done once when weights are loaded; the row-major
+ * buffers may be freed afterwards.
+ *   w_codes [G, N, K/2], w_scales [G, N, K/16] (16-byte aligned).
+ *   out     nvfp4_prepared_weight_bytes(G, N, K) bytes, 16-byte aligned.
+ * Layout: rows in blocks of 16 (last block zero-padded), k in steps of 256;
+ * tile (g, block, step) holds 2304 contiguous bytes: for lane l = r + 16q
+ * (r = row in block, q = 0..3), bytes [16l, 16l+16) and [1024+16l, 1024+16l+16)
+ * are code bytes [32q, 32q+16) and [32q+16, 32q+32) of that row's 128 code
+ * bytes of the step, and bytes [2048+4l, 2048+4l+4) its scale bytes
+ * [4q, 4q+4) of the step's 16.
+ * Errors: EINVAL for null pointers; ESHAPE unless G >= 1, N >= 1,
+ * K % 256 == 0 and K >= 256; EALIGN for misaligned pointers.
+ */
+size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K);
+int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t G, int64_t N,
+                              int64_t K, uint8_t* out, void* stream);
 
 /*
  * silu_mul_requant - h = SiLU(gate) * up, re-quantised to NVFP4.

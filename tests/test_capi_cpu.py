@@ -71,12 +71,13 @@ def test_route_validation(L):
 
 def _gemm(L, **kw):
     a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, w_codes=FAKE,
-             w_scales=FAKE, w_gs=FAKE, n_seg=[0, 64], group_offsets=FAKE, G=1, M=8, N=64, K=64,
-             out=FAKE, out_dtype=lib.DTYPE_F32, ld_out=64)
+             w_scales=FAKE, w_layout=lib.LAYOUT_ROWS, w_gs=FAKE, n_seg=[0, 64], group_offsets=FAKE, G=1,
+             M=8, N=64, K=64, out=FAKE, out_dtype=lib.DTYPE_F32, ld_out=64)
     a.update(kw)
     seg = (ctypes.c_int32 * len(a["n_seg"]))(*a["n_seg"])
     return L.nvfp4_grouped_gemm(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"],
-                                a["w_codes"], a["w_scales"], a["w_gs"], seg, len(a["n_seg"]) - 1,
+                                a["w_codes"], a["w_scales"], a["w_layout"], a["w_gs"], seg,
+                                len(a["n_seg"]) - 1,
                                 a["group_offsets"], a["G"], a["M"], a["N"], a["K"], a["out"],
                                 a["out_dtype"], a["ld_out"], NULL)
 
@@ -95,6 +96,17 @@ def test_gemm_validation(L):
     assert _gemm(L, w_codes=NULL) == lib.EINVAL
     assert _gemm(L, out=ctypes.c_void_p(0x1008)) == lib.EALIGN
     assert _gemm(L, M=0, a_codes=NULL, out=NULL) == lib.OK
+    assert _gemm(L, w_layout=2) == lib.EINVAL
+    assert _gemm(L, w_layout=lib.LAYOUT_TILED) == lib.ESHAPE       # K % 256
+    assert _gemm(L, w_layout=lib.LAYOUT_ROWS, w_scales=NULL) == lib.EINVAL
+
+
+def test_prepare_validation_and_size(L):
+    assert L.nvfp4_prepared_weight_bytes(2, 33, 512) == 2 * 3 * 2 * 2304
+    assert L.nvfp4_prepared_weight_bytes(1, 16, 128) == 0
+    assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, 128, FAKE, NULL) == lib.ESHAPE
+    assert L.nvfp4_prepare_weights(NULL, FAKE, 1, 16, 256, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, 256, ctypes.c_void_p(0x1001), NULL) == lib.EALIGN
 
 
 def test_silu_and_combine_validation(L):

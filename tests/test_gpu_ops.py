@@ -142,10 +142,16 @@ def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=
             wc[g, r0:r1], ws[g, r0:r1], wgs[g, s] = c, sc, gg
     d = dev()
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
-    out = ops.grouped_gemm(T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), n_seg, T(off), M,
-                           a_row_index=T(row_index) if gather else None,
-                           out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    args = (T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), n_seg, T(off), M)
+    kw = dict(a_row_index=T(row_index) if gather else None, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    out = ops.grouped_gemm(*args, **kw)
     got = to_np(out)
+    if K % 256 == 0:
+        # the tiled weight layout must give bit-identical results
+        tiled = ops.prepare_weights(T(wc), T(ws))
+        got_t = to_np(ops.grouped_gemm(*args, w_tiled=tiled, **kw))
+        assert np.array_equal(got_t.view(np.uint32) if got_t.dtype == np.float32 else got_t,
+                              got.view(np.uint32) if got.dtype == np.float32 else got), "tiled layout differs"
     # oracle (the definition) and the float64 pieces for the error bound
     ref_o = moe.grouped_gemm(ac, as_, ags, wc, ws, wgs, n_seg, off, a_row_index=row_index,
                              out_dtype="bf16" if out_bf16 else "f32")
@@ -206,6 +212,34 @@ def test_gemm_empty_m():
                            torch.zeros(1, 16, 4, dtype=torch.uint8, device=d), torch.ones(1, 1, device=d),
                            [0, 16], torch.zeros(2, dtype=torch.int32, device=d), 0)
     assert out.shape == (0, 16)
+
+
+def test_prepare_weights_is_the_documented_permutation():
+    log("prepare layout")
+    rng = np.random.default_rng(11)
+    G, N, K = 2, 37, 512
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    ws = rng.integers(0, 127, (G, N, K // 16), dtype=np.uint8)
+    out = to_np(ops.prepare_weights(torch.from_numpy(wc).to(dev()), torch.from_numpy(ws).to(dev())))
+    NB, KS = (N + 15) // 16, K // 256
+    assert out.size == G * NB * KS * 2304
+    t = out.reshape(G, NB, KS, 2304)
+    for g in range(G):
+        for nb in range(NB):
+            for ks in range(KS):
+                for l in range(64):
+                    r, q = l % 16, l // 16
+                    row = nb * 16 + r
+                    c0 = t[g, nb, ks, 16 * l:16 * l + 16]
+                    c1 = t[g, nb, ks, 1024 + 16 * l:1024 + 16 * l + 16]
+                    sc = t[g, nb, ks, 2048 + 4 * l:2048 + 4 * l + 4]
+                    if row < N:
+                        base = ks * 128 + 32 * q
+                        assert np.array_equal(c0, wc[g, row, base:base + 16])
+                        assert np.array_equal(c1, wc[g, row, base + 16:base + 32])
+                        assert np.array_equal(sc, ws[g, row, ks * 16 + 4 * q:ks * 16 + 4 * q + 4])
+                    else:
+                        assert not c0.any() and not c1.any() and not sc.any()
 
 
 def test_gemm_deterministic():
