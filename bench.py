@@ -183,7 +183,7 @@ def roofline(res, bound):
             "kernel_ms": round(l1_ms, 4)}
 
 
-def cpu_baseline(res, n_experts=8):
+def cpu_baseline(res, n_experts=24):
     """The oracle timed on the host on a bounded sample: n_experts of the
     touched experts with all their routed rows (L1, SiLU-requant, L2), plus
     the per-token steps (quantise, route, permute, combine) for the whole
@@ -201,17 +201,23 @@ def cpu_baseline(res, n_experts=8):
     ids, _ = moe.route_topk(logits, wl.k)
     experts = sorted(set(ids.reshape(-1).tolist()))[:n_experts]
     gen = "cuda:0" if wl.weights_on_device else "cpu"
-    w1c, w1s, w1g, w2c, w2s, w2g = [], [], [], [], [], []
-    for e in experts:
-        m1 = workloads.moe_gate_up(wl, e, 0, gen).cpu().numpy()
-        m2 = workloads.moe_down(wl, e, 0, gen).cpu().numpy()
+    mats = [(workloads.moe_gate_up(wl, e, 0, gen).cpu().numpy(), workloads.moe_down(wl, e, 0, gen).cpu().numpy())
+            for e in experts]
+
+    def prep(m):
+        m1, m2 = m
         gg = quant.global_scale(quant.amax(m1[:wl.I]))
         gu = quant.global_scale(quant.amax(m1[wl.I:]))
         cg, sg = quant.quantize(m1[:wl.I], gg)
         cu, su = quant.quantize(m1[wl.I:], gu)
-        w1c.append(np.concatenate([cg, cu])); w1s.append(np.concatenate([sg, su])); w1g.append([gg, gu])
         c2, s2, g2 = moe.quantize_weight(m2)
-        w2c.append(c2); w2s.append(s2); w2g.append([g2])
+        return np.concatenate([cg, cu]), np.concatenate([sg, su]), [gg, gu], c2, s2, [g2]
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:     # setup only, not timed
+        prepared = list(ex.map(prep, mats))
+    del mats
+    w1c, w1s, w1g, w2c, w2s, w2g = (list(z) for z in zip(*prepared))
     w1 = (np.stack(w1c), np.stack(w1s), np.array(w1g, np.float32))
     w2 = (np.stack(w2c), np.stack(w2s), np.array(w2g, np.float32))
     # timed: per-token part over the whole batch
@@ -259,7 +265,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=8)
+    ap.add_argument("--cpu-experts", type=int, default=24)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (x3); used to calibrate the "
                          "HBM byte counters of rocprofv3 against a transfer of known size")
