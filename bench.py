@@ -84,6 +84,10 @@ class Layer:
         ids, w, off, srt, inv = ops.route_permute(warm["logits"].to(device), wl.k)
         gu = self.w1.gemm(xc, xs, self.gs_x, off, xw.shape[0] * wl.k, a_row_index=srt)
         self.gs_h = ops.silu_mul_global_scale(gu)
+        # whether the GEMMs take A's f16 form from its producer (many-row tiles)
+        R = self.x.shape[0] * wl.k
+        self.dq1 = True if self.w1.reads_dq(R, self.x.shape[0]) else None
+        self.dq2 = True if self.w2.reads_dq(R, R) else None
         torch.cuda.synchronize()
 
     def step(self, ev=None):
@@ -96,15 +100,15 @@ class Layer:
         rec = (lambda name: ev[name].append(torch.cuda.Event(enable_timing=True)) or ev[name][-1].record()) \
             if ev is not None else (lambda name: None)
         rec("start")
-        xc, xs = ops.quantize(self.x, self.gs_x)
+        xc, xs, *xdq = ops.quantize(self.x, self.gs_x, dq=self.dq1)
         rec("quantize")
         ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
         rec("route_permute")
-        gu = self.w1.gemm(xc, xs, self.gs_x, off, R, a_row_index=srt)
+        gu = self.w1.gemm(xc, xs, self.gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
         rec("gemm_l1")
-        hc, hs = ops.silu_mul_requant(gu, self.gs_h)
+        hc, hs, *hdq = ops.silu_mul_requant(gu, self.gs_h, dq=self.dq2)
         rec("silu_mul_requant")
-        y = self.w2.gemm(hc, hs, self.gs_h, off, R, out_dtype=torch.bfloat16)
+        y = self.w2.gemm(hc, hs, self.gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
         rec("gemm_l2")
         out = ops.combine(y, inv, w)
         rec("combine")

@@ -58,7 +58,7 @@ const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
 int32_t nvfp4_version(void) { return 100; }
 
 int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                       const float* gs, uint8_t* codes, uint8_t* scales, void* stream) {
+                       const float* gs, uint8_t* codes, uint8_t* scales, uint16_t* dq, void* stream) {
   const int es = elem_size(x_dtype);
   if (!es) return fail(NVFP4_EINVAL, "nvfp4_quantize: unknown dtype %d", x_dtype);
   if (rows < 0 || cols < 0) return fail(NVFP4_ESHAPE, "nvfp4_quantize: negative size");
@@ -66,11 +66,12 @@ int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t col
   if (ld_x < cols) return fail(NVFP4_ESHAPE, "nvfp4_quantize: ld_x < cols");
   if (rows == 0 || cols == 0) return NVFP4_OK;
   if (!x || !gs || !codes || !scales) return fail(NVFP4_EINVAL, "nvfp4_quantize: null pointer");
-  if (!aligned(x, 16) || (ld_x * es) % 16 || !aligned(codes, 8) || !aligned(gs, 4))
-    return fail(NVFP4_EALIGN, "nvfp4_quantize: x and its row pitch must be 16-byte aligned, codes 8-byte");
+  if (!aligned(x, 16) || (ld_x * es) % 16 || !aligned(codes, 8) || !aligned(gs, 4) || !aligned(dq, 16))
+    return fail(NVFP4_EALIGN, "nvfp4_quantize: x, its row pitch and dq must be 16-byte aligned, codes 8-byte");
   hipStream_t s = (hipStream_t)stream;
   return finish("nvfp4_quantize",
-                nvfp4::launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, rows, cols, ld_x, gs, codes, scales, s), s);
+                nvfp4::launch_quantize(x, x_dtype == NVFP4_DTYPE_BF16, rows, cols, ld_x, gs, codes, scales, dq, s),
+                s);
 }
 
 size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n) {
@@ -122,7 +123,8 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
 }
 
 int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                           int64_t a_rows, const int32_t* a_row_index, const uint8_t* w_codes,
+                           int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                           const uint8_t* w_codes,
                            const uint8_t* w_scales, int32_t w_layout, const float* w_gs, const int32_t* n_seg,
                            int32_t n_segs, const int32_t* group_offsets, int32_t G, int64_t M, int64_t N,
                            int64_t K, void* out, int32_t out_dtype, int64_t ld_out, void* stream) {
@@ -152,14 +154,16 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
     return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: null pointer");
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
       !aligned(out, 16) || !aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(group_offsets, 4) ||
-      !aligned(a_row_index, 4))
-    return fail(NVFP4_EALIGN, "nvfp4_grouped_gemm: codes and out must be 16-byte aligned, scales 4-byte");
+      !aligned(a_row_index, 4) || !aligned(a_dq, 16))
+    return fail(NVFP4_EALIGN, "nvfp4_grouped_gemm: codes, a_dq and out must be 16-byte aligned, scales 4-byte");
   nvfp4::GemmArgs a;
   a.a_codes = a_codes;
   a.a_scales = a_scales;
   a.a_gs = a_gs;
   a.a_rows = a_row_index ? a_rows : M;
   a.a_row_index = a_row_index;
+  // the direct-to-LDS loads address A with 32-bit byte offsets
+  a.a_dq = a_dq && (uint64_t)a.a_rows * (uint64_t)K * 2u < ((uint64_t)1 << 32) ? a_dq : nullptr;
   a.w_codes = w_codes;
   a.w_scales = tiled ? nullptr : w_scales;
   a.w_tiled = tiled ? 1 : 0;
@@ -176,6 +180,12 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   a.ld_out = ld_out;
   hipStream_t s = (hipStream_t)stream;
   return finish("nvfp4_grouped_gemm", nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout) {
+  if (G < 1 || M < 1 || K < 256 || K % 256 || a_rows < 1) return 0;
+  if ((uint64_t)a_rows * (uint64_t)K * 2u >= ((uint64_t)1 << 32)) return 0;
+  return nvfp4::gemm_uses_big_tiles(G, M, w_layout == NVFP4_LAYOUT_TILED) ? 1 : 0;
 }
 
 size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K) {
@@ -195,7 +205,7 @@ int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, i
 }
 
 int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I, int64_t ld,
-                         const float* gs_h, uint8_t* h_codes, uint8_t* h_scales, void* stream) {
+                         const float* gs_h, uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* stream) {
   const int es = elem_size(in_dtype);
   if (!es) return fail(NVFP4_EINVAL, "silu_mul_requant: unknown dtype %d", in_dtype);
   if (M < 0 || I < 0) return fail(NVFP4_ESHAPE, "silu_mul_requant: negative size");
@@ -203,12 +213,12 @@ int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64
   if (ld < 2 * I) return fail(NVFP4_ESHAPE, "silu_mul_requant: ld < 2*I");
   if (M == 0 || I == 0) return NVFP4_OK;
   if (!gate_up || !gs_h || !h_codes || !h_scales) return fail(NVFP4_EINVAL, "silu_mul_requant: null pointer");
-  if (!aligned(gate_up, 16) || (ld * es) % 16 || !aligned(h_codes, 8) || !aligned(gs_h, 4))
-    return fail(NVFP4_EALIGN, "silu_mul_requant: gate_up and its pitch must be 16-byte aligned, codes 8-byte");
+  if (!aligned(gate_up, 16) || (ld * es) % 16 || !aligned(h_codes, 8) || !aligned(gs_h, 4) || !aligned(h_dq, 16))
+    return fail(NVFP4_EALIGN, "silu_mul_requant: gate_up, its pitch and h_dq must be 16-byte aligned, codes 8-byte");
   hipStream_t s = (hipStream_t)stream;
   return finish("silu_mul_requant",
                 nvfp4::launch_silu_mul_requant(gate_up, in_dtype == NVFP4_DTYPE_BF16, M, I, ld, gs_h, h_codes,
-                                               h_scales, s),
+                                               h_scales, h_dq, s),
                 s);
 }
 

@@ -4,23 +4,30 @@
 //
 // Both operands arrive as E2M1 codes plus E4M3 block scales.  They are
 // dequantised in registers to f16 (exact: e2m1 * e4m3 has at most five
-// significant bits and lies in [2^-10, 2688]) and multiplied with
-// v_mfma_f32_16x16x32_f16, whose products are exact and whose sums are
-// float32.  The per-tensor global scales are applied once, in the epilogue.
+// significant bits and lies in [2^-10, 2688]) and multiplied on the matrix
+// cores, whose products are exact and whose sums are float32.  The
+// per-tensor global scales are applied once, in the epilogue.
 //
-// MFMA 16x16x32 f16 operand layout (checked on the device): lane l supplies
-// row (l % 16) of the 16x32 left operand and column (l % 16) of the 32x16
-// right operand, eight consecutive k each, k-slot (l / 16); lane l receives
-// D[4 * (l / 16) + i][l % 16], i = 0..3.  Which eight k values a lane feeds is
-// our choice as long as both operands make the same choice, which lets every
-// lane read long contiguous runs of its own row.
+// Matrix-core instructions (lane layouts checked on the device):
+//  * v_mfma_f32_32x32x16_f16: lane l = c + 32 kh supplies row c of the 32x16
+//    left operand and column c of the 16x32 right operand, eight k each (k
+//    half kh); lane l receives D[8 (i / 4) + 4 kh + (i % 4)][c], i = 0..15.
+//    On gfx950 it sustains ~1.9 PFLOP/s, twice the 16x16x32 form, so the
+//    kernels over prepared (tiled) weights use it.
+//  * v_mfma_f32_16x16x32_f16: lane l = r + 16 q supplies row/column r, eight
+//    k each (k slot q); lane l receives D[4 q + i][r].  Used by the fallback
+//    kernels over row-major weights.
+// Which k values a lane feeds is our choice as long as both operands make
+// the same choice, which lets every lane read long contiguous runs.
 //
-// Two kernels:
-//  * gemm_rows16 - 16 rows x (4 waves x NBW x 16) columns per workgroup,
-//    every wave streaming its own columns over the whole K with no shared
-//    memory: the weight-streaming kernel for few rows per group (decode).
-//  * gemm_tile   - 128 x 128 tiles, raw codes staged in LDS with double
-//    buffering, 2 x 2 waves of 64 x 64: the kernel for many rows per group.
+// Kernels:
+//  * gemm_stream32 - prepared weights, 32*RB rows x (4 waves x NBW x 32)
+//    columns per workgroup, every wave streaming its columns of W over the
+//    whole K with no shared memory: the weight-streaming kernel for few rows
+//    per group (decode) and for the rows a 256-row tile leaves over.
+//  * gemm_big32    - prepared weights, 256 x 256 tiles, A dequantised once per
+//    workgroup into LDS, software-pipelined: many rows per group (prefill).
+//  * gemm_stream16 / gemm_tile16 - row-major weights (any K % 32 == 0).
 // A workgroup finds its (group, row range) from the device group offsets, so
 // the launch needs no host-side knowledge of the group sizes; workgroups past
 // the last tile exit at once.
@@ -36,13 +43,16 @@ __device__ __forceinline__ T clampv(T v, T lo, T hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// The `slot`-th row tile when every group g is cut into ceil(rows_g / BM)
-// tiles of BM rows, groups in order.  Executed by a whole wave (all lanes get
-// the result).  Offsets are clamped into [0, M] and forced non-decreasing, so
-// garbage offsets cannot produce rows outside [0, M).
-template <int BM>
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int& g_out,
-                          int64_t& r0, int64_t& r1) {
+// The `slot`-th row tile of a launch.  Every group g (rows [lo, hi) from the
+// device offsets) contributes the rows [start, hi) with start = lo, or, when
+// skip_bm > 0, start = lo + floor((hi - lo) / skip_bm) * skip_bm (the rows a
+// skip_bm-tile launch leaves over); they are cut into tiles of bm rows, the
+// last one partial unless full_only (then partial tiles are dropped).  Groups
+// are taken in order.  Executed by a whole wave (all lanes get the result).
+// Offsets are clamped into [0, M] and forced non-decreasing, so garbage
+// offsets cannot produce rows outside [0, M).
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int bm,
+                          int skip_bm, bool full_only, int& g_out, int64_t& r0, int64_t& r1) {
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int g0 = 0; g0 < G; g0 += 64) {
@@ -53,7 +63,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M,
       lo = clampv<int64_t>(offsets[g], 0, M);
       hi = clampv<int64_t>(offsets[g + 1], 0, M);
       if (hi < lo) hi = lo;
-      tiles = (int32_t)((hi - lo + BM - 1) / BM);
+      if (skip_bm > 0) lo += (hi - lo) / skip_bm * skip_bm;
+      tiles = (int32_t)(full_only ? (hi - lo) / bm : (hi - lo + bm - 1) / bm);
     }
     int32_t incl = tiles;
 #pragma unroll
@@ -71,8 +82,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M,
       const int32_t lo_s = __shfl((int32_t)lo, src, 64);
       const int32_t hi_s = __shfl((int32_t)hi, src, 64);
       const int32_t ex_s = __shfl(excl, src, 64);
-      r0 = lo_s + (slot - base - ex_s) * BM;
-      r1 = r0 + BM < hi_s ? r0 + BM : hi_s;
+      r0 = lo_s + (slot - base - ex_s) * bm;
+      r1 = r0 + bm < hi_s ? r0 + bm : hi_s;
       return true;
     }
     base += total;
@@ -98,13 +109,17 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int64_t m, int64_t 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
 
 // ---------------------------------------------------------------------------
-// gemm_rows16: decode-shaped.  Lane (r = l % 16, q = l / 16).  In the main
-// loop a K-step is 256: lane q feeds k in [kb + 64q, kb + 64q + 64), i.e. 32
-// contiguous bytes of codes and one 4-byte word of scales of its row, and
-// MFMA j (0..7) takes word j of those bytes (block scale byte j / 2).  The
-// tail (K % 256) runs K-steps of 32 with lane q feeding [kt + 8q, kt + 8q + 8).
-template <int NBW, bool kTiled>
-__global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) {
+// gemm_stream16: the weight-streaming kernel over row-major weights
+// (16x16x32 instruction).  A workgroup computes 16*RB rows x (4 waves x NBW x
+// 16) columns; every wave streams its NBW 16-column blocks of W over the
+// whole K with no shared memory and no barriers, one K-step prefetched
+// ahead.  Lane (r = l % 16, q = l / 16).  A K-step is 256: lane q
+// feeds k in [kb + 64q, kb + 64q + 64), i.e. 32 contiguous bytes of codes and
+// one 4-byte word of scales of its row, and MFMA j (0..7) takes word j of
+// those bytes (block scale byte j / 2).  The tail (K % 256) runs K-steps of
+// 32 with lane q feeding [kt + 8q, kt + 8q + 8).
+template <int NBW, int RB>
+__global__ __launch_bounds__(256) void gemm_stream16(GemmArgs p, int64_t n_tiles, int skip_bm) {
   constexpr int BN = 4 * NBW * 16;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -114,103 +129,105 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
   const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
   int g;
   int64_t row0, row1;
-  if (!find_tile<16>(p.group_offsets, p.G, p.M, slot, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, 16 * RB, skip_bm, false, g, row0, row1)) return;
   const int64_t n0 = nt * BN + wave * NBW * 16;
   if (n0 >= p.N) return;
   const int64_t K = p.K;
   const int64_t KB = K / 2;    // code bytes per row
   const int64_t KS = K / 16;   // scale bytes per row
 
-  // A row of this lane
-  const int64_t m = row0 + r;
-  const bool a_valid = m < row1;
-  int64_t a_row = a_valid ? (p.a_row_index ? (int64_t)p.a_row_index[m] : m) : 0;
-  a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
-  const uint8_t* a_c = p.a_codes + a_row * KB;
-  const uint8_t* a_s = p.a_scales + a_row * KS;
+  // A rows of this lane: row0 + 16 rb + r
+  bool a_valid[RB];
+  const uint8_t* a_c[RB];
+  const uint8_t* a_s[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t m = row0 + 16 * rb + r;
+    a_valid[rb] = m < row1;
+    int64_t a_row = a_valid[rb] ? (p.a_row_index ? (int64_t)p.a_row_index[m] : m) : 0;
+    a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
+    a_c[rb] = p.a_codes + a_row * KB;
+    a_s[rb] = p.a_scales + a_row * KS;
+  }
 
-  // W rows (output columns) of this lane.  Row-major: the lane's own row.
-  // Tiled: the first tile of the lane's 16-row block (the lane offset inside
-  // a tile is added at load time); tiles of one block follow each other in k.
+  // W rows (output columns) of this lane
   const uint8_t* w_c[NBW];
   const uint8_t* w_s[NBW];
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
-    if constexpr (kTiled) {
-      const int64_t nb_per_g = (p.N + 15) / 16;
-      int64_t nb = (n0 + cb * 16) / 16;
-      nb = nb < nb_per_g ? nb : nb_per_g - 1;
-      w_c[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes;
-      w_s[cb] = w_c[cb];
-    } else {
-      const int64_t n = clampv<int64_t>(n0 + cb * 16 + r, 0, p.N - 1);
-      const int64_t wr = (int64_t)g * p.N + n;
-      w_c[cb] = p.w_codes + wr * KB;
-      w_s[cb] = p.w_scales + wr * KS;
-    }
+    const int64_t n = clampv<int64_t>(n0 + cb * 16 + r, 0, p.N - 1);
+    const int64_t wr = (int64_t)g * p.N + n;
+    w_c[cb] = p.w_codes + wr * KB;
+    w_s[cb] = p.w_scales + wr * KS;
   }
 
-  floatx4_t acc[NBW];
+  floatx4_t acc[RB][NBW];
 #pragma unroll
-  for (int cb = 0; cb < NBW; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // The 256-step loads one 4-byte word of scales per lane, which needs the
   // scale rows (K/16 bytes) to be 4-byte aligned, i.e. K % 64 == 0.
-  const int64_t K256 = kTiled ? K : (K % 64 == 0 ? K - K % 256 : 0);
+  const int64_t K256 = K % 64 == 0 ? K - K % 256 : 0;
   if (K256 > 0) {
     // software pipeline: the next step's bytes are in flight while the
     // current step is dequantised and multiplied
-    u32x4 ac0, ac1, wc0[NBW], wc1[NBW];
-    uint32_t as, ws[NBW];
-    auto load = [&](int64_t kb, u32x4& c0, u32x4& c1, uint32_t& sc, u32x4 (&d0)[NBW], u32x4 (&d1)[NBW],
-                    uint32_t (&sw)[NBW]) {
+    u32x4 ac0[RB], ac1[RB], wc0[NBW], wc1[NBW];
+    uint32_t as[RB], ws[NBW];
+    auto load = [&](int64_t kb, u32x4 (&c0)[RB], u32x4 (&c1)[RB], uint32_t (&sc)[RB], u32x4 (&d0)[NBW],
+                    u32x4 (&d1)[NBW], uint32_t (&sw)[NBW]) {
       const int64_t cofs = kb / 2 + 32 * q;
       const int64_t sofs = kb / 16 + 4 * q;
-      if (a_valid) {
-        c0 = *(const u32x4*)(a_c + cofs);
-        c1 = *(const u32x4*)(a_c + cofs + 16);
-        sc = *(const uint32_t*)(a_s + sofs);
-      } else {
-        c0 = u32x4{0u, 0u, 0u, 0u};
-        c1 = c0;
-        sc = 0;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (a_valid[rb]) {
+          c0[rb] = *(const u32x4*)(a_c[rb] + cofs);
+          c1[rb] = *(const u32x4*)(a_c[rb] + cofs + 16);
+          sc[rb] = *(const uint32_t*)(a_s[rb] + sofs);
+        } else {
+          c0[rb] = u32x4{0u, 0u, 0u, 0u};
+          c1[rb] = c0[rb];
+          sc[rb] = 0;
+        }
       }
 #pragma unroll
       for (int cb = 0; cb < NBW; ++cb) {
-        if constexpr (kTiled) {
-          const uint8_t* t = w_c[cb] + (kb / 256) * kTileBytes;
-          d0[cb] = *(const u32x4*)(t + 16 * lane);
-          d1[cb] = *(const u32x4*)(t + 1024 + 16 * lane);
-          sw[cb] = *(const uint32_t*)(t + 2048 + 4 * lane);
-        } else {
-          d0[cb] = *(const u32x4*)(w_c[cb] + cofs);
-          d1[cb] = *(const u32x4*)(w_c[cb] + cofs + 16);
-          sw[cb] = *(const uint32_t*)(w_s[cb] + sofs);
-        }
+        d0[cb] = *(const u32x4*)(w_c[cb] + cofs);
+        d1[cb] = *(const u32x4*)(w_c[cb] + cofs + 16);
+        sw[cb] = *(const uint32_t*)(w_s[cb] + sofs);
       }
     };
     load(0, ac0, ac1, as, wc0, wc1, ws);
     for (int64_t kb = 0; kb < K256; kb += 256) {
-      u32x4 nac0, nac1, nwc0[NBW], nwc1[NBW];
-      uint32_t nas, nws[NBW];
+      u32x4 nac0[RB], nac1[RB], nwc0[NBW], nwc1[NBW];
+      uint32_t nas[RB], nws[NBW];
       const bool more = kb + 256 < K256;
       if (more) load(kb + 256, nac0, nac1, nas, nwc0, nwc1, nws);
-      const uint32_t aw[8] = {ac0.x, ac0.y, ac0.z, ac0.w, ac1.x, ac1.y, ac1.z, ac1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const half8_t af = dequant8(aw[j], scale_pair(byte_of(as, j >> 1)));
+        half8_t bf[NBW];
 #pragma unroll
         for (int cb = 0; cb < NBW; ++cb) {
-          const uint32_t ww[8] = {wc0[cb].x, wc0[cb].y, wc0[cb].z, wc0[cb].w,
-                                  wc1[cb].x, wc1[cb].y, wc1[cb].z, wc1[cb].w};
-          const half8_t bf = dequant8(ww[j], scale_pair(byte_of(ws[cb], j >> 1)));
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[cb], 0, 0, 0);
+          const uint32_t w = j < 4 ? wc0[cb][j] : wc1[cb][j - 4];
+          bf[cb] = dequant8(w, scale_pair(byte_of(ws[cb], j >> 1)));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint32_t aw = j < 4 ? ac0[rb][j] : ac1[rb][j - 4];
+          const half8_t af = dequant8(aw, scale_pair(byte_of(as[rb], j >> 1)));
+#pragma unroll
+          for (int cb = 0; cb < NBW; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[rb][cb], 0, 0, 0);
         }
       }
       if (more) {
-        ac0 = nac0;
-        ac1 = nac1;
-        as = nas;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          ac0[rb] = nac0[rb];
+          ac1[rb] = nac1[rb];
+          as[rb] = nas[rb];
+        }
 #pragma unroll
         for (int cb = 0; cb < NBW; ++cb) {
           wc0[cb] = nwc0[cb];
@@ -223,14 +240,20 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
   for (int64_t kt = K256; kt < K; kt += 32) {
     const int64_t cofs = kt / 2 + 4 * q;
     const int64_t sofs = (kt + 8 * q) / 16;
-    const uint32_t aw = a_valid ? *(const uint32_t*)(a_c + cofs) : 0u;
-    const uint32_t asb = a_valid ? (uint32_t)a_s[sofs] : 0u;
-    const half8_t af = dequant8(aw, scale_pair(asb));
+    half8_t bf[NBW];
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
       const uint32_t ww = *(const uint32_t*)(w_c[cb] + cofs);
-      const half8_t bf = dequant8(ww, scale_pair((uint32_t)w_s[cb][sofs]));
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[cb], 0, 0, 0);
+      bf[cb] = dequant8(ww, scale_pair((uint32_t)w_s[cb][sofs]));
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint32_t aw = a_valid[rb] ? *(const uint32_t*)(a_c[rb] + cofs) : 0u;
+      const uint32_t asb = a_valid[rb] ? (uint32_t)a_s[rb][sofs] : 0u;
+      const half8_t af = dequant8(aw, scale_pair(asb));
+#pragma unroll
+      for (int cb = 0; cb < NBW; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[rb][cb], 0, 0, 0);
     }
   }
 
@@ -241,15 +264,17 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
     if (n >= p.N) continue;
     const float alpha = alpha_for(p, g, n, a_gs);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t mm = row0 + 4 * q + i;
-      if (mm < row1) store_out(p, mm, n, alpha * acc[cb][i]);
-    }
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t mm = row0 + 16 * rb + 4 * q + i;
+        if (mm < row1) store_out(p, mm, n, alpha * acc[rb][cb][i]);
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
-// gemm_tile: 128 x 128 output tile per workgroup of 256 threads, K-step 64.
+// gemm_tile16: 128 x 128 output tile per workgroup (row-major weights) of 256 threads, K-step 64.
 // Per step the raw codes (32 B per row) and scales (4 B per row) of the A and
 // W tiles go global -> registers -> LDS (double buffered, one barrier per
 // step); each wave then reads its fragments from LDS and dequantises them.
@@ -258,8 +283,7 @@ __global__ __launch_bounds__(256) void gemm_rows16(GemmArgs p, int64_t n_tiles) 
 // word s of those bytes.
 constexpr int TBM = 128, TBN = 128, TBK = 64;
 
-template <bool kTiled>
-__global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
+__global__ __launch_bounds__(256) void gemm_tile16(GemmArgs p, int64_t n_tiles) {
   __shared__ uint8_t lds_ac[2][TBM * 32];
   __shared__ uint8_t lds_wc[2][TBN * 32];
   __shared__ uint32_t lds_as[2][TBM];
@@ -274,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
   int g;
   int64_t row0, row1;
-  if (!find_tile<TBM>(p.group_offsets, p.G, p.M, slot, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, TBM, 0, false, g, row0, row1)) return;
   const int64_t n0 = nt * TBN;
   const int64_t K = p.K;
   const int64_t KB = K / 2;
@@ -289,22 +313,9 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   int64_t a_row = a_ok ? (p.a_row_index ? (int64_t)p.a_row_index[am] : am) : 0;
   a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
   const uint8_t* a_c = p.a_codes + a_row * KB + 16 * chalf;
-  // W codes: row-major, thread t moves 16 B of row t / 2 like A.  Tiled,
-  // thread t takes 16-row block t / 32, half (t / 16) % 2, row t % 16: the
-  // k-step of 64 is one quarter (q' = ks % 4) of a 256-k tile, whose halves
-  // sit at 256 q' + 16 r and 1024 + 256 q' + 16 r.
-  const int w_lds_row = kTiled ? ((tid >> 5) * 16 + (tid & 15)) : crow;
-  const int w_half = kTiled ? ((tid >> 4) & 1) : chalf;
-  const int64_t nb_per_g = (p.N + 15) / 16;
-  const uint8_t* w_c;
-  if constexpr (kTiled) {
-    int64_t nb = n0 / 16 + (tid >> 5);
-    nb = nb < nb_per_g ? nb : nb_per_g - 1;
-    w_c = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes + 1024 * w_half + 16 * (tid & 15);
-  } else {
-    const int64_t wn_row = (int64_t)g * p.N + clampv<int64_t>(n0 + crow, 0, p.N - 1);
-    w_c = p.w_codes + wn_row * KB + 16 * chalf;
-  }
+  // W codes: thread t moves 16 B of row t / 2 like A
+  const int64_t wn_row = (int64_t)g * p.N + clampv<int64_t>(n0 + crow, 0, p.N - 1);
+  const uint8_t* w_c = p.w_codes + wn_row * KB + 16 * chalf;
   const int srow = tid & 127;
   const uint8_t* s_src;
   if (tid < 128) {
@@ -312,10 +323,6 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
     int64_t sr = sm < row1 ? (p.a_row_index ? (int64_t)p.a_row_index[sm] : sm) : 0;
     sr = clampv<int64_t>(sr, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
     s_src = p.a_scales + sr * KS;
-  } else if constexpr (kTiled) {
-    int64_t nb = n0 / 16 + (srow >> 4);
-    nb = nb < nb_per_g ? nb : nb_per_g - 1;
-    s_src = p.w_codes + ((int64_t)g * nb_per_g + nb) * (K / 256) * kTileBytes + 2048 + 4 * (srow & 15);
   } else {
     s_src = p.w_scales + ((int64_t)g * p.N + clampv<int64_t>(n0 + srow, 0, p.N - 1)) * KS;
   }
@@ -331,19 +338,12 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
   uint32_t rs;
   auto gload = [&](int64_t ks) {
     ra = *(const u32x4*)(a_c + ks * 32);
-    if constexpr (kTiled) {
-      const int64_t tofs = (ks >> 2) * kTileBytes + 256 * (ks & 3);
-      rw = *(const u32x4*)(w_c + tofs);
-      rs = tid < 128 ? *(const uint32_t*)(s_src + ks * 4)
-                     : *(const uint32_t*)(s_src + (ks >> 2) * kTileBytes + 64 * (ks & 3));
-    } else {
-      rw = *(const u32x4*)(w_c + ks * 32);
-      rs = *(const uint32_t*)(s_src + ks * 4);
-    }
+    rw = *(const u32x4*)(w_c + ks * 32);
+    rs = *(const uint32_t*)(s_src + ks * 4);
   };
   auto lstore = [&](int buf) {
     *(u32x4*)(&lds_ac[buf][crow * 32 + 16 * chalf]) = ra;
-    *(u32x4*)(&lds_wc[buf][w_lds_row * 32 + 16 * w_half]) = rw;
+    *(u32x4*)(&lds_wc[buf][crow * 32 + 16 * chalf]) = rw;
     if (tid < 128) lds_as[buf][srow] = rs;
     else lds_ws[buf][srow] = rs;
   };
@@ -401,25 +401,586 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs p, int64_t n_tiles) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernels over prepared (tiled) weights, 32x32x16 instruction.  In half-step
+// h of K-step ks, lane l = c + 32 kh feeds k in [ks*256 + 128h + 64kh, +64):
+// substep j (0..7) takes k [.. + 8j, +8), i.e. code word j of the lane's 32
+// bytes and scale byte j / 2 of its scale word, for A and W alike.
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Row of D held in accumulator element i by a lane of k half kh.
+__device__ __forceinline__ int acc32_row(int i, int kh) { return 8 * (i >> 2) + 4 * kh + (i & 3); }
+
+// gemm_stream32: 32*RB rows x (4 waves x NBW x 32) columns per workgroup; each
+// wave streams its NBW 32-column blocks of W over the whole K, one half-step
+// prefetched ahead, with no shared memory and no barriers.  With skip_bm > 0
+// it takes only the rows a skip_bm-row tile launch leaves over at the end of
+// each group.
+template <int NBW, int RB>
+__global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm) {
+  constexpr int BN = 4 * NBW * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t slot = (int64_t)blockIdx.x / n_tiles;
+  const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
+  int g;
+  int64_t row0, row1;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, skip_bm, false, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t n0 = nt * BN + wave * NBW * 32;
+  if (n0 >= p.N) return;
+  const int64_t K = p.K;
+  const int64_t nks = K / 256;
+  const int64_t KB = K / 2, KS = K / 16;
+
+  bool a_valid[RB];
+  const uint8_t* a_c[RB];
+  const uint8_t* a_s[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t m = row0 + 32 * rb + c;
+    a_valid[rb] = m < row1;
+    int64_t a_row = a_valid[rb] ? (p.a_row_index ? (int64_t)p.a_row_index[m] : m) : 0;
+    a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
+    a_c[rb] = p.a_codes + a_row * KB + 32 * kh;
+    a_s[rb] = p.a_scales + a_row * KS + 4 * kh;
+  }
+  const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
+  const uint8_t* w_t[NBW];
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    int64_t nb = n0 / 32 + cb;
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+  }
+
+  floatx16_t acc[RB][NBW];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = floatx16_t{};
+
+  u32x4 a0[RB], a1[RB], w0[NBW], w1[NBW];
+  uint32_t as[RB], ws[NBW];
+  auto load = [&](int64_t hs, u32x4 (&c0)[RB], u32x4 (&c1)[RB], uint32_t (&sc)[RB], u32x4 (&d0)[NBW],
+                  u32x4 (&d1)[NBW], uint32_t (&sw)[NBW]) {
+    const int64_t ks = hs >> 1, h = hs & 1;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (a_valid[rb]) {
+        c0[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h);
+        c1[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h + 16);
+        sc[rb] = *(const uint32_t*)(a_s[rb] + ks * 16 + 8 * h);
+      } else {
+        c0[rb] = u32x4{0u, 0u, 0u, 0u};
+        c1[rb] = c0[rb];
+        sc[rb] = 0u;
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) {
+      const uint8_t* t = w_t[cb] + ks * kTileBytes;
+      d0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
+      d1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
+      sw[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+    }
+  };
+  load(0, a0, a1, as, w0, w1, ws);
+  const int64_t nhs = 2 * nks;
+  for (int64_t hs = 0; hs < nhs; ++hs) {
+    u32x4 na0[RB], na1[RB], nw0[NBW], nw1[NBW];
+    uint32_t nas[RB], nws[NBW];
+    const bool more = hs + 1 < nhs;
+    if (more) load(hs + 1, na0, na1, nas, nw0, nw1, nws);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half8_t bf[NBW];
+#pragma unroll
+      for (int cb = 0; cb < NBW; ++cb)
+        bf[cb] = dequant8(j < 4 ? w0[cb][j] : w1[cb][j - 4], scale_pair(byte_of(ws[cb], j >> 1)));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const half8_t af = dequant8(j < 4 ? a0[rb][j] : a1[rb][j - 4], scale_pair(byte_of(as[rb], j >> 1)));
+#pragma unroll
+        for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = mfma32(af, bf[cb], acc[rb][cb]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        a0[rb] = na0[rb];
+        a1[rb] = na1[rb];
+        as[rb] = nas[rb];
+      }
+#pragma unroll
+      for (int cb = 0; cb < NBW; ++cb) {
+        w0[cb] = nw0[cb];
+        w1[cb] = nw1[cb];
+        ws[cb] = nws[cb];
+      }
+    }
+  }
+
+  const float a_gs = *p.a_gs;
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    const int64_t n = n0 + 32 * cb + c;
+    if (n >= p.N) continue;
+    const float alpha = alpha_for(p, g, n, a_gs);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t m = row0 + 32 * rb + acc32_row(i, kh);
+        if (m < row1) store_out(p, m, n, alpha * acc[rb][cb][i]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_big32: 256 x 256 output tiles for groups with many rows, 4 waves (one
+// per SIMD), each wave all 256 rows x 64 columns = 8 x 2 blocks of 32 x 32
+// (256 accumulators, held in the accumulation registers).  A W fragment is
+// dequantised once per wave and feeds 8 MFMAs; on gfx950 a 32x32x16 MFMA
+// hides only two or three vector instructions, so the dequantisation work
+// per MFMA is what the layout minimises.
+//  * A (256 rows) is dequantised ONCE per workgroup and half-step into an f16
+//    half-tile in LDS: a row is 16 chunks of 16 B, chunk cc holding k
+//    [8cc, 8cc + 8) of the half-step, so substep j of k half kh reads chunk
+//    8 kh + j.  Chunk cc of row m sits at position cc ^ (m % 16), so the rows
+//    a group of lanes reads or writes together fall in distinct banks.  Two
+//    buffers, one barrier per half-step.  Wave w converts the 16-byte piece w
+//    (chunks 4w..4w+3) of rows lane + 64 pp, pp = 0..3.
+//  * A fragments are read from LDS right after their last use in the
+//    previous substep, a whole row sweep ahead of their next use.
+//  * W goes straight from the tiled layout into registers; the words of the
+//    next half-step are loaded into the registers of the current ones as
+//    soon as those are dead.
+//  * Each of a substep's 16 MFMAs is followed in program order by a slice of
+//    vector work: the next substep's W fragments, and in substeps 2..7 the
+//    conversion and store of chunks of the next A half-tile.
+// Workgroup ids are remapped so that the workgroups resident on one XCD take
+// consecutive logical tiles (same A row tile, neighbouring columns), which
+// keeps the A tile in that XCD's L2.
+constexpr int BIG = 256;
+constexpr int kAHalfBytes = BIG * 256;           // 64 KiB per f16 half-tile
+constexpr int kBigThreads = 256;
+
+__device__ __forceinline__ int swz(int m, int cc) { return m * 256 + ((cc ^ (m & 15)) << 4); }
+
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t n_tiles) {
+  constexpr int RB = 8;     // 256 rows per wave
+  constexpr int CB = 2;     // 64 columns per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+
+  const int64_t total = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t q8 = total / 8, r8 = total % 8;
+  const int64_t xcd = bid % 8, idx = bid / 8;
+  const int64_t logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+  const int64_t slot = logical / n_tiles;
+  const int64_t nt = logical - slot * n_tiles;
+  int g;
+  int64_t row0, row1;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, BIG, 0, true, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t n0 = nt * BIG;
+  const int64_t K = p.K;
+  const int64_t nks = K / 256;
+  const int64_t KB = K / 2, KS = K / 16;
+
+  // A staging: piece pc = wave of rows lane + 64 pp
+  const int pc = wave;
+  const uint8_t* a_c[4];
+  const uint8_t* a_s[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int64_t m = row0 + lane + 64 * pp;             // always < row1 (full tiles)
+    int64_t ar = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
+    ar = clampv<int64_t>(ar, 0, p.a_rows - 1);
+    a_c[pp] = p.a_codes + ar * KB + 16 * pc;
+    a_s[pp] = p.a_scales + ar * KS + 2 * pc;
+  }
+  const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
+  const uint8_t* w_t[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    int64_t nb = n0 / 32 + wave * CB + cb;
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+  }
+
+  floatx16_t acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = floatx16_t{};
+
+  u32x4 ac[4];
+  uint32_t as[4];
+  auto a_load = [&](int64_t hs) {
+    const int64_t ks = hs >> 1, h = hs & 1;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      ac[pp] = *(const u32x4*)(a_c[pp] + ks * 128 + 64 * h);
+      as[pp] = *(const uint16_t*)(a_s[pp] + ks * 16 + 8 * h);
+    }
+  };
+  // W words of the current half-step: w0 (substeps 0-3), w1 (4-7) and the
+  // scale word ws; the next half-step's w0 and scale word (wsn) are loaded
+  // once substep 3 is done with w0, its w1 during substep 7.
+  u32x4 w0[CB], w1[CB];
+  uint32_t ws[CB], wsn[CB];
+  auto w_load0 = [&](int64_t hs) {
+    const int64_t ks = hs >> 1, h = hs & 1;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint8_t* t = w_t[cb] + ks * kTileBytes;
+      w0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
+      wsn[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+    }
+  };
+  auto w_load1 = [&](int64_t hs) {
+    const int64_t ks = hs >> 1, h = hs & 1;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      w1[cb] = *(const u32x4*)(w_t[cb] + ks * kTileBytes + 2048 * h + 1024 + 16 * lane);
+  };
+
+  a_load(0);
+  w_load0(0);
+  w_load1(0);
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      *(half8_t*)(lds + swz(lane + 64 * pp, 4 * pc + d)) =
+          dequant8(ac[pp][d], scale_pair((as[pp] >> (8 * (d >> 1))) & 0xFFu));
+  half8_t bf[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    ws[cb] = wsn[cb];
+    bf[cb] = dequant8(w0[cb][0], scale_pair(byte_of(ws[cb], 0)));
+  }
+  // LDS byte offsets of this lane's A fragments: row block rb at
+  // (32 rb + c) * 256, substep j at chunk_ofs[j]
+  const int x = c & 15;
+  int chunk_ofs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) chunk_ofs[j] = ((8 * kh + j) ^ x) << 4;
+  __syncthreads();
+  const int64_t nhs = 2 * nks;
+  for (int64_t hs = 0; hs < nhs; ++hs) {
+    const int h = (int)(hs & 1);
+    // the last half-step reloads itself instead of reading past K (the
+    // words are converted into the unused buffer and never read)
+    const int64_t hn = hs + 1 < nhs ? hs + 1 : hs;
+    a_load(hn);
+    const uint8_t* abuf = lds + h * kAHalfBytes + c * 256;
+    uint8_t* anext = lds + (h ^ 1) * kAHalfBytes;
+    half8_t af[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j == 4) w_load0(hn);       // w0's last use was substep 3's dequantisation
+      // vector work after the MFMAs, slot s = 2 rb + cb (16 slots):
+      //  - W fragments of the next substep: slots 0-9, five parts per column
+      //    block (part 0: scale, parts 1-4: one f16 pair each); substep 7
+      //    prepares substep 0 of the next half-step;
+      //  - in substeps 2..7, chunks of the next A half-tile, three parts per
+      //    chunk from slot 6 on (substeps 2-5 three chunks, 6-7 two).
+      const int a_first = j < 2 ? 0 : (j < 6 ? 3 * (j - 2) : 12 + 2 * (j - 6));
+      const int a_count = j < 2 ? 0 : (j < 6 ? 3 : 2);
+      half2_t sfn[CB];
+      half8_t bn[CB];
+      half2_t asf;
+      half8_t aval;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[rb][cb] = mfma32(af[rb], bf[cb], acc[rb][cb]);
+          const int s = rb * CB + cb;
+          if (s < 10) {  // W fragment of the next substep
+            const int wc = s / 5, part = s % 5;
+            const uint32_t word = j < 7 ? (j + 1 < 4 ? w0[wc][j + 1] : w1[wc][j + 1 - 4]) : w0[wc][0];
+            if (part == 0) {
+              sfn[wc] = scale_pair(j < 7 ? byte_of(ws[wc], (j + 1) >> 1) : byte_of(wsn[wc], 0));
+            } else {
+              const half2_t v = dequant_pair(word, part - 1, sfn[wc]);
+              bn[wc][2 * (part - 1)] = v[0];
+              bn[wc][2 * (part - 1) + 1] = v[1];
+            }
+          }
+          if (s >= 6 && s - 6 < 3 * a_count) {  // part of a chunk of the next A half-tile
+            const int kk = (s - 6) / 3, part = (s - 6) % 3;
+            const int chunk = a_first + kk, pp = chunk >> 2, d = chunk & 3;
+            if (part == 0) {
+              asf = scale_pair((as[pp] >> (8 * (d >> 1))) & 0xFFu);
+              const half2_t v0 = dequant_pair(ac[pp][d], 0, asf);
+              aval[0] = v0[0];
+              aval[1] = v0[1];
+            } else if (part == 1) {
+              const half2_t v1 = dequant_pair(ac[pp][d], 1, asf);
+              const half2_t v2 = dequant_pair(ac[pp][d], 2, asf);
+              aval[2] = v1[0];
+              aval[3] = v1[1];
+              aval[4] = v2[0];
+              aval[5] = v2[1];
+            } else {
+              const half2_t v3 = dequant_pair(ac[pp][d], 3, asf);
+              aval[6] = v3[0];
+              aval[7] = v3[1];
+              *(half8_t*)(anext + swz(lane + 64 * pp, 4 * pc + d)) = aval;
+            }
+          }
+        }
+        // af[rb] is dead for this substep: fetch it for the next one
+        if (j < 7) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[j + 1]);
+      }
+      if (j == 7) w_load1(hn);       // w1's last use was substep 6's dequantisation
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) bf[cb] = bn[cb];
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) ws[cb] = wsn[cb];
+    __syncthreads();
+  }
+
+  const float a_gs = *p.a_gs;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t n = n0 + (wave * CB + cb) * 32 + c;
+    if (n >= p.N) continue;
+    const float alpha = alpha_for(p, g, n, a_gs);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        store_out(p, row0 + rb * 32 + acc32_row(i, kh), n, alpha * acc[rb][cb][i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_big32_dq: the 256 x 256 tiles of gemm_big32 when A also comes in its
+// exactly dequantised f16 form (a_dq).  A half-tiles then go from global
+// memory straight into local memory (global_load_lds_dwordx4, 1 KiB = four
+// 256-byte rows per wave instruction), so A costs the waves neither vector
+// registers nor conversion work, and the vector unit only dequantises W.
+//  * Wave w copies rows 64 w .. 64 w + 63: its copy i fills rows
+//    64 w + 4 i .. +3, lane l writing physical chunk l % 16 of row
+//    64 w + 4 i + l / 16.  That chunk holds logical chunk (l % 16) ^ (row % 16)
+//    (the swizzle of gemm_big32), so the lane reads those 16 bytes of the row.
+//  * The next half-tile's 16 copies are spread over substeps 0-3; the next
+//    half-step's W words are loaded at substep 0 into a second register set.
+//    Nothing is waited for before substep 7, when the next half-step's first
+//    W fragment is dequantised; the copies have landed by the barrier.
+//    (The compiler waits for all outstanding vector memory operations once
+//    copies into local memory and register loads are both in flight, so no
+//    load is issued after substep 0 that substeps 1-6 would wait for.)
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
+  constexpr int RB = 8;     // 256 rows per wave
+  constexpr int CB = 2;     // 64 columns per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+
+  const int64_t total = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t q8 = total / 8, r8 = total % 8;
+  const int64_t xcd = bid % 8, idx = bid / 8;
+  const int64_t logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+  const int64_t slot = logical / n_tiles;
+  const int64_t nt = logical - slot * n_tiles;
+  int g;
+  int64_t row0, row1;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, BIG, 0, true, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t n0 = nt * BIG;
+  const int64_t K = p.K;
+  const int64_t nks = K / 256;
+
+  // byte offsets in a_dq of this lane's 16 bytes of each copy, less the
+  // half-step's k offset (the host guarantees a_rows * K * 2 < 2^32)
+  uint32_t a_off[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 64 * wave + 4 * i + (lane >> 4);
+    const int64_t m = row0 + r;                          // always < row1 (full tiles)
+    int64_t ar = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
+    ar = clampv<int64_t>(ar, 0, p.a_rows - 1);
+    a_off[i] = (uint32_t)(ar * K * 2 + 16 * ((lane & 15) ^ (r & 15)));
+  }
+  const uint8_t* a_base = (const uint8_t*)p.a_dq;
+  auto a_copy = [&](int64_t hs, int buf, int i) {
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(a_base + hs * 256 + a_off[i]),
+        (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (64 * wave + 4 * i) * 256), 16, 0,
+        0);
+  };
+
+  const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
+  const uint8_t* w_t[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    int64_t nb = n0 / 32 + wave * CB + cb;
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+  }
+  // W words of a half-step: w0 (substeps 0-3), w1 (4-7), scale word ws
+  struct WWords {
+    u32x4 w0[CB], w1[CB];
+    uint32_t ws[CB];
+  };
+  auto w_load = [&](int64_t hs, WWords& d) {
+    const int64_t ks = hs >> 1, h = hs & 1;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint8_t* t = w_t[cb] + ks * kTileBytes;
+      d.w0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
+      d.w1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
+      d.ws[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+    }
+  };
+
+  floatx16_t acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = floatx16_t{};
+
+  WWords cur, nxt;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a_copy(0, 0, i);
+  w_load(0, cur);
+  half8_t bf[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) bf[cb] = dequant8(cur.w0[cb][0], scale_pair(byte_of(cur.ws[cb], 0)));
+  const int x = c & 15;
+  int chunk_ofs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) chunk_ofs[j] = ((8 * kh + j) ^ x) << 4;
+  __builtin_amdgcn_s_waitcnt(0);       // this wave's copies of the first half-tile have landed
+  __syncthreads();
+  const int64_t nhs = 2 * nks;
+  for (int64_t hs = 0; hs < nhs; ++hs) {
+    const int h = (int)(hs & 1);
+    // the last half-step reloads itself (into the unused buffer and registers)
+    const int64_t hn = hs + 1 < nhs ? hs + 1 : hs;
+    w_load(hn, nxt);
+    const uint8_t* abuf = lds + h * kAHalfBytes + c * 256;
+    half8_t af[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half2_t sfn[CB];
+      half8_t bn[CB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[rb][cb] = mfma32(af[rb], bf[cb], acc[rb][cb]);
+          const int s = rb * CB + cb;
+          // the next half-tile: copies 4 j .. 4 j + 3 after slots 3, 7, 11, 15
+          if (j < 4 && (s & 3) == 3) a_copy(hn, h ^ 1, 4 * j + (s >> 2));
+          // W fragment of the next substep in slots 0-9, five parts per
+          // column block (scale, then one f16 pair each); substep 7 prepares
+          // substep 0 of the next half-step
+          if (s < 10) {
+            const int wc = s / 5, part = s % 5;
+            const uint32_t word = j < 7 ? (j + 1 < 4 ? cur.w0[wc][j + 1] : cur.w1[wc][j + 1 - 4]) : nxt.w0[wc][0];
+            if (part == 0) {
+              sfn[wc] = scale_pair(j < 7 ? byte_of(cur.ws[wc], (j + 1) >> 1) : byte_of(nxt.ws[wc], 0));
+            } else {
+              const half2_t v = dequant_pair(word, part - 1, sfn[wc]);
+              bn[wc][2 * (part - 1)] = v[0];
+              bn[wc][2 * (part - 1) + 1] = v[1];
+            }
+          }
+        }
+        // af[rb] is dead for this substep: fetch it for the next one
+        if (j < 7) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[j + 1]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) bf[cb] = bn[cb];
+      // keep each substep's loads and conversions among its own MFMAs (the
+      // scheduler would otherwise move the loads towards their first use)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next half-tile have landed
+    __syncthreads();
+  }
+
+  const float a_gs = *p.a_gs;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t n = n0 + (wave * CB + cb) * 32 + c;
+    if (n >= p.N) continue;
+    const float alpha = alpha_for(p, g, n, a_gs);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        store_out(p, row0 + rb * 32 + acc32_row(i, kh), n, alpha * acc[rb][cb][i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled) { return tiled && M >= BIG && M >= 64 * G; }
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  const bool many_rows = a.M >= (int64_t)64 * a.G && a.K % TBK == 0;
-  if (many_rows) {
+  if (a.w_tiled) {
+    if (gemm_uses_big_tiles(a.G, a.M, true)) {
+      // many rows per group: full 256-row tiles on the matrix-core kernel, the
+      // rows left over at the end of each group on the streaming kernel
+      constexpr int NBW = 2, RB = 2;
+      const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+      const int64_t slots_s = (a.M + 32 * RB - 1) / (32 * RB) + a.G;
+      hipLaunchKernelGGL((gemm_stream32<NBW, RB>), dim3((unsigned)(slots_s * n_tiles_s)), dim3(256), 0, s, a,
+                         n_tiles_s, BIG);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t n_tiles = (a.N + BIG - 1) / BIG;
+      const int64_t slots = a.M / BIG;
+      if (a.a_dq)
+        hipLaunchKernelGGL(gemm_big32_dq, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
+      else
+        hipLaunchKernelGGL(gemm_big32, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
+      return hipGetLastError();
+    }
+    constexpr int NBW = 2;
+    const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+    const int64_t slots = (a.M + 31) / 32 + a.G;
+    hipLaunchKernelGGL((gemm_stream32<NBW, 1>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles, 0);
+    return hipGetLastError();
+  }
+  if (a.M >= (int64_t)64 * a.G && a.K % TBK == 0) {
     const int64_t n_tiles = (a.N + TBN - 1) / TBN;
     const int64_t slots = (a.M + TBM - 1) / TBM + a.G;
-    if (a.w_tiled)
-      hipLaunchKernelGGL(gemm_tile<true>, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
-    else
-      hipLaunchKernelGGL(gemm_tile<false>, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
+    hipLaunchKernelGGL(gemm_tile16, dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
   } else {
     constexpr int NBW = 4;
     const int64_t n_tiles = (a.N + 4 * NBW * 16 - 1) / (4 * NBW * 16);
     const int64_t slots = (a.M + 15) / 16 + a.G;
-    if (a.w_tiled)
-      hipLaunchKernelGGL((gemm_rows16<NBW, true>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles);
-    else
-      hipLaunchKernelGGL((gemm_rows16<NBW, false>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a,
-                         n_tiles);
+    hipLaunchKernelGGL((gemm_stream16<NBW, 1>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles, 0);
   }
   return hipGetLastError();
 }

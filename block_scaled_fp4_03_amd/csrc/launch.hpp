@@ -38,13 +38,14 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
 }
 #endif
 
-// Bytes of one tile of the prepared (tiled) weight layout: 16 rows x 256 k
-// of codes (2048 B) and their scales (256 B).
-constexpr int kTileBytes = 2304;
+// One tile of the prepared (tiled) weight layout: 32 rows x 256 k, codes
+// (4096 B) then scales (512 B).
+constexpr int kTileRows = 32;
+constexpr int kTileBytes = 4608;
 
 // --- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
-                           const float* gs, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                           const float* gs, uint8_t* codes, uint8_t* scales, uint16_t* dq, hipStream_t s);
 int64_t amax_chunks(int64_t n);
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride,
                                float* gs_out, float* partial, hipStream_t s);
@@ -63,6 +64,7 @@ struct GemmArgs {
   const float* a_gs;
   int64_t a_rows;
   const int32_t* a_row_index;  // nullable
+  const uint16_t* a_dq;        // nullable: f16 [a_rows, K], e2m1 * e4m3 of A
   const uint8_t* w_codes;      // row-major codes, or the tiled buffer
   const uint8_t* w_scales;     // row-major scales (unused when tiled)
   int32_t w_tiled;             // 1: w_codes is the prepared tiled layout
@@ -76,10 +78,13 @@ struct GemmArgs {
   int32_t out_bf16;
   int64_t ld_out;
 };
+// true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
+bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_silu_mul_requant(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
-                                   const float* gs_h, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                                   const float* gs_h, uint8_t* codes, uint8_t* scales, uint16_t* dq,
+                                   hipStream_t s);
 int64_t silu_amax_chunks(int64_t M, int64_t I);
 hipError_t launch_silu_mul_global_scale(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
                                         float* gs_out, float* partial, hipStream_t s);

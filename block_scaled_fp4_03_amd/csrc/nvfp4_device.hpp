@@ -161,6 +161,18 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, half2_t sf2) {
   return r;
 }
 
+// Two E2M1 codes (byte `sel` of `codes`) times their block scale, as f16;
+// the pieces dequant8 is made of, for code that spreads them between other
+// instructions.  `sel` must fold to a constant.
+__device__ __forceinline__ half2_t dequant_pair(uint32_t codes, int sel, half2_t sf2) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sf2;
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sf2;
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sf2;
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sf2;
+  }
+}
+
 // E4M3 scale code -> the f16 pair (sf, sf) for dequant8.
 __device__ __forceinline__ half2_t scale_pair(uint32_t code) {
   const _Float16 h = (_Float16)e4m3_decode(code);     // exact: E4M3 values fit f16
@@ -168,6 +180,22 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t code) {
   r[0] = h;
   r[1] = h;
   return r;
+}
+
+// The 16 dequantised values e2m1(code) * e4m3(scale) of a block (without
+// the global scale) as f16, written as 32 contiguous bytes.  Exact: the
+// product has at most five significant bits and lies in [2^-10, 2688].
+__device__ __forceinline__ void store_dq16(void* dst, uint32_t lo, uint32_t hi, uint32_t scale_code) {
+  const half2_t sf2 = scale_pair(scale_code);
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(uint32_t, dequant_pair(lo, i, sf2));
+    b[i] = __builtin_bit_cast(uint32_t, dequant_pair(hi, i, sf2));
+  }
+  ((u32x4v*)dst)[0] = a;
+  ((u32x4v*)dst)[1] = b;
 }
 
 }  // namespace nvfp4

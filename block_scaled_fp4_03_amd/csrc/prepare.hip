@@ -1,17 +1,19 @@
 // Weight preparation: a byte permutation of NVFP4 weights into the tiled
 // layout the grouped GEMM streams with whole-cache-line loads.
 //
-// Tiled layout.  The N rows of each group are cut into blocks of 16 rows
-// (the last block padded with zero bytes) and K into steps of 256.  Tile
-// (g, nb, ks) is 2304 contiguous bytes, tiles ordered by g, then nb, then ks:
-//   [0, 1024)     first 16 bytes of each lane:  lane l = r + 16q holds row
-//                 nb*16 + r, code bytes ks*128 + 32q + [0, 16)
-//   [1024, 2048)  second 16 bytes of each lane: code bytes ks*128 + 32q + [16, 32)
-//   [2048, 2304)  scales: lane l holds scale bytes ks*16 + 4q + [0, 4) of row
-//                 nb*16 + r
-// so a 64-lane wave reads each part with one fully contiguous load, and lane
-// (r, q) ends up with the codes and scales of row r for k in
-// [ks*256 + 64q, ks*256 + 64q + 64).  Requires K % 256 == 0.
+// Tiled layout, built around the 32 x 32 x 16 matrix-core instruction
+// (lane l = c + 32 kh feeds column c and one of two halves kh of each
+// instruction's k range).  The N rows of each group are cut into blocks of
+// 32 rows (the last block padded with zero bytes) and K into steps of 256;
+// a step is two half-steps h of 128.  Tile (g, nb, ks) is 4608 contiguous
+// bytes, tiles ordered by g, then nb, then ks:
+//   codes  [h * 2048 + i * 1024 + 16 l, +16), h, i in {0, 1}: row
+//          nb * 32 + c, code bytes ks * 128 + 64 h + 32 kh + 16 i + [0, 16)
+//   scales [4096 + h * 256 + 4 l, +4): row nb * 32 + c, scale bytes
+//          ks * 16 + 8 h + 4 kh + [0, 4)
+// so a 64-lane wave reads each part with one fully contiguous load, and in
+// half-step h lane (c, kh) holds the 32 code bytes and 4 scales of row c for
+// k in [ks * 256 + 128 h + 64 kh, +64).  Requires K % 256 == 0.
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -21,7 +23,7 @@ namespace nvfp4 {
 __global__ __launch_bounds__(256) void prepare_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, int64_t G, int64_t N,
                                                       int64_t K, uint32_t* __restrict__ out) {
-  const int64_t nb_per_g = (N + 15) / 16;
+  const int64_t nb_per_g = (N + kTileRows - 1) / kTileRows;
   const int64_t ks_per_row = K / 256;
   const int64_t words = G * nb_per_g * ks_per_row * (kTileBytes / 4);
   const int64_t KB = K / 2, KS = K / 16;
@@ -33,23 +35,21 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint8_t* __restrict_
     const int64_t gnb = tile / ks_per_row;
     const int64_t nb = gnb % nb_per_g;
     const int64_t g = gnb / nb_per_g;
-    int l, b;
+    int l;
     bool is_scale;
     int64_t src_ofs;
-    if (o < 2048) {
-      const int half = o >= 1024;
-      const int oo = o - half * 1024;
-      l = oo / 16;
-      b = oo % 16;
+    if (o < 4096) {
+      const int h = o >> 11, i = (o >> 10) & 1, oo = o & 1023;
+      l = oo >> 4;
       is_scale = false;
-      src_ofs = ks * 128 + 32 * (l >> 4) + 16 * half + b;
+      src_ofs = ks * 128 + 64 * h + 32 * (l >> 5) + 16 * i + (oo & 15);
     } else {
-      l = (o - 2048) / 4;
-      b = 0;
+      const int h = (o - 4096) >> 8, oo = (o - 4096) & 255;
+      l = oo >> 2;
       is_scale = true;
-      src_ofs = ks * 16 + 4 * (l >> 4);
+      src_ofs = ks * 16 + 8 * h + 4 * (l >> 5);
     }
-    const int64_t row = nb * 16 + (l & 15);
+    const int64_t row = nb * kTileRows + (l & 31);
     uint32_t v = 0;
     if (row < N) {
       const uint8_t* src = is_scale ? scales + (g * N + row) * KS + src_ofs : codes + (g * N + row) * KB + src_ofs;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint8_t* __restrict_
 }
 
 int64_t prepared_bytes(int64_t G, int64_t N, int64_t K) {
-  return G * ((N + 15) / 16) * (K / 256) * kTileBytes;
+  return G * ((N + kTileRows - 1) / kTileRows) * (K / 256) * kTileBytes;
 }
 
 hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int64_t G, int64_t N, int64_t K,

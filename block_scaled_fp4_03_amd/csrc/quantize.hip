@@ -12,7 +12,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                                                        int64_t blocks_per_row, int64_t ld_x,
                                                        const float* __restrict__ gs_ptr,
                                                        uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       uint16_t* __restrict__ dq) {
   const int64_t nblk = rows * blocks_per_row;
   const float gs = *gs_ptr;
   constexpr int64_t kElem = kBf16 ? 2 : 4;
@@ -26,6 +27,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     const uint32_t sq = quantize_block16(v, gs, lo, hi);
     *(uint2*)(codes + b * 8) = make_uint2(lo, hi);
     scales[b] = (uint8_t)sq;
+    if (dq) store_dq16(dq + b * 16, lo, hi, sq);
   }
 }
 
@@ -87,7 +89,7 @@ int64_t amax_chunks(int64_t n) {
 }
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
-                           const float* gs, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                           const float* gs, uint8_t* codes, uint8_t* scales, uint16_t* dq, hipStream_t s) {
   const int64_t bpr = cols / 16;
   const int64_t nblk = rows * bpr;
   if (nblk == 0) return hipSuccess;
@@ -95,10 +97,10 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
   if (grid > 65536) grid = 65536;
   if (bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, x, rows, bpr,
-                       ld_x, gs, codes, scales);
+                       ld_x, gs, codes, scales, dq);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, x, rows, bpr,
-                       ld_x, gs, codes, scales);
+                       ld_x, gs, codes, scales, dq);
   return hipGetLastError();
 }
 

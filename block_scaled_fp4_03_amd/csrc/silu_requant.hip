@@ -19,7 +19,8 @@ __global__ __launch_bounds__(256) void silu_requant_kernel(const void* __restric
                                                            int64_t I, int64_t ld,
                                                            const float* __restrict__ gs_ptr,
                                                            uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales) {
+                                                           uint8_t* __restrict__ scales,
+                                                           uint16_t* __restrict__ dq) {
   const int64_t bpr = I / 16;
   const int64_t nblk = M * bpr;
   const float gs = *gs_ptr;
@@ -38,6 +39,7 @@ __global__ __launch_bounds__(256) void silu_requant_kernel(const void* __restric
     const uint32_t sq = quantize_block16(h, gs, lo, hi);
     *(uint2*)(codes + r * (I / 2) + c * 8) = make_uint2(lo, hi);
     scales[r * bpr + c] = (uint8_t)sq;
+    if (dq) store_dq16(dq + r * I + c * 16, lo, hi, sq);
   }
 }
 
@@ -84,16 +86,17 @@ int64_t silu_amax_chunks(int64_t M, int64_t I) {
 }
 
 hipError_t launch_silu_mul_requant(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
-                                   const float* gs_h, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                                   const float* gs_h, uint8_t* codes, uint8_t* scales, uint16_t* dq,
+                                   hipStream_t s) {
   const int64_t nblk = M * (I / 16);
   if (nblk == 0) return hipSuccess;
   const int64_t g = grid_for(nblk);
   if (bf16)
     hipLaunchKernelGGL(silu_requant_kernel<true>, dim3((unsigned)g), dim3(256), 0, s, gu, M, I, ld, gs_h,
-                       codes, scales);
+                       codes, scales, dq);
   else
     hipLaunchKernelGGL(silu_requant_kernel<false>, dim3((unsigned)g), dim3(256), 0, s, gu, M, I, ld, gs_h,
-                       codes, scales);
+                       codes, scales, dq);
   return hipGetLastError();
 }
 

@@ -19,15 +19,16 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_version": (_I32, []),
-    "nvfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
-    "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,
+    "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,
                                   _P, _I32, _I64, _I64, _I64, _P, _I32, _I64, _P]),
+    "nvfp4_grouped_gemm_reads_dq": (_I32, [_I32, _I64, _I64, _I64, _I32]),
     "nvfp4_prepared_weight_bytes": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_prepare_weights": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
-    "silu_mul_requant": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "silu_mul_requant": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "silu_mul_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "silu_mul_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "moe_combine": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I64, _P, _P]),

@@ -34,10 +34,22 @@ def _dtype(t):
     return _DT[t.dtype]
 
 
-def quantize(x, gs, codes=None, scales=None):
+def _dq_out(dq, rows, cols, device):
+    if dq is True:
+        return torch.empty(rows, cols, dtype=torch.float16, device=device)
+    if dq is not None and (dq.dtype != torch.float16 or tuple(dq.shape) != (rows, cols)
+                           or not dq.is_contiguous()):
+        raise ValueError("dq must be a contiguous float16 [%d, %d] tensor" % (rows, cols))
+    return dq
+
+
+def quantize(x, gs, codes=None, scales=None, dq=None):
     """x [rows, cols] f32/bf16 (row pitch x.stride(0)), gs: 1-element f32
-    tensor.  Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16])."""
-    _check_dev(x, gs)
+    tensor.  Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16]).
+    With dq (True, or a float16 [rows, cols] tensor to fill) it also writes
+    the dequantised values without the global scale and returns
+    (codes, scales, dq)."""
+    _check_dev(x, gs, None if dq is True else dq)
     rows, cols = x.shape
     if x.stride(1) != 1:
         raise ValueError("x must have unit column stride")
@@ -45,9 +57,11 @@ def quantize(x, gs, codes=None, scales=None):
         codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device)
+    want_dq = dq is not None
+    dq = _dq_out(dq, rows, cols, x.device)
     _lib.call("nvfp4_quantize", _p(x), _dtype(x), rows, cols, x.stride(0), _p(gs), _p(codes),
-              _p(scales), _stream())
-    return codes, scales
+              _p(scales), _p(dq), _stream())
+    return (codes, scales, dq) if want_dq else (codes, scales)
 
 
 def global_scale(x, out=None):
@@ -85,6 +99,12 @@ def route_permute(logits, k):
     return ids, w, off, sorted_ids, inv
 
 
+def gemm_reads_dq(G, M, K, a_rows, tiled):
+    """Whether grouped_gemm with these sizes reads the float16 form of A."""
+    return bool(_lib.load().nvfp4_grouped_gemm_reads_dq(G, M, K, a_rows,
+                                                         _lib.LAYOUT_TILED if tiled else _lib.LAYOUT_ROWS))
+
+
 def prepared_weight_bytes(G, N, K):
     return _lib.load().nvfp4_prepared_weight_bytes(G, N, K)
 
@@ -102,11 +122,12 @@ def prepare_weights(w_codes, w_scales, out=None):
 
 
 def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_offsets, M,
-                 a_row_index=None, out_dtype=torch.float32, out=None, w_tiled=None):
+                 a_row_index=None, out_dtype=torch.float32, out=None, w_tiled=None, a_dq=None):
     """out [M, N] = alpha * A . W^T per group (see nvfp4_grouped_gemm).
     w_codes/w_scales give G, N, K; if w_tiled (the prepare_weights buffer) is
-    passed, the kernel reads the weights from it instead."""
-    _check_dev(a_codes, a_scales, a_gs, w_gs, group_offsets, a_row_index, w_tiled)
+    passed, the kernel reads the weights from it instead.  a_dq is the
+    optional float16 form of A written by quantize / silu_mul_requant."""
+    _check_dev(a_codes, a_scales, a_gs, w_gs, group_offsets, a_row_index, w_tiled, a_dq)
     G, N, K2 = w_codes.shape
     K = 2 * K2
     if out is None:
@@ -117,24 +138,30 @@ def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_
     else:
         _check_dev(w_codes, w_scales)
         wc, ws, layout = w_codes, w_scales, _lib.LAYOUT_ROWS
+    if a_dq is not None and (a_dq.dtype != torch.float16 or tuple(a_dq.shape) != (a_codes.shape[0], K)
+                             or not a_dq.is_contiguous()):
+        raise ValueError("a_dq must be a contiguous float16 [a_rows, K] tensor")
     _lib.call("nvfp4_grouped_gemm", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
-              _p(a_row_index), _p(wc), _p(ws), layout, _p(w_gs), seg, len(n_seg) - 1,
+              _p(a_row_index), _p(a_dq), _p(wc), _p(ws), layout, _p(w_gs), seg, len(n_seg) - 1,
               _p(group_offsets), G, M, N, K, _p(out), _dtype(out), out.stride(0), _stream())
     return out
 
 
-def silu_mul_requant(gate_up, gs_h, codes=None, scales=None):
-    """gate_up [M, 2I] f32/bf16 -> NVFP4 h (codes [M, I/2], scales [M, I/16])."""
-    _check_dev(gate_up, gs_h)
+def silu_mul_requant(gate_up, gs_h, codes=None, scales=None, dq=None):
+    """gate_up [M, 2I] f32/bf16 -> NVFP4 h (codes [M, I/2], scales [M, I/16]);
+    dq as in quantize."""
+    _check_dev(gate_up, gs_h, None if dq is True else dq)
     M, I2 = gate_up.shape
     I = I2 // 2
     if codes is None:
         codes = torch.empty(M, I // 2, dtype=torch.uint8, device=gate_up.device)
     if scales is None:
         scales = torch.empty(M, I // 16, dtype=torch.uint8, device=gate_up.device)
+    want_dq = dq is not None
+    dq = _dq_out(dq, M, I, gate_up.device)
     _lib.call("silu_mul_requant", _p(gate_up), _dtype(gate_up), M, I, gate_up.stride(0), _p(gs_h),
-              _p(codes), _p(scales), _stream())
-    return codes, scales
+              _p(codes), _p(scales), _p(dq), _stream())
+    return (codes, scales, dq) if want_dq else (codes, scales)
 
 
 def silu_mul_global_scale(gate_up, out=None):

@@ -46,6 +46,11 @@ class NVFP4Weights:
                 self.scales = torch.empty(self.scales.shape, dtype=torch.uint8, device="meta")
         return self
 
+    def reads_dq(self, M, a_rows):
+        """Whether a GEMM of M rows (A stored in a_rows rows) reads A's f16 form."""
+        G, _, K2 = self.codes.shape
+        return ops.gemm_reads_dq(G, M, 2 * K2, a_rows, self.tiled is not None)
+
     def gemm(self, a_codes, a_scales, a_gs, group_offsets, M, **kw):
         return ops.grouped_gemm(a_codes, a_scales, a_gs, self.codes, self.scales, self.gs, self.n_seg,
                                 group_offsets, M, w_tiled=self.tiled, **kw)
@@ -101,13 +106,15 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
     1-element f32 tensors.  Returns out [T, H] bf16 (and the stages)."""
     T, H = x.shape
-    I2 = w1.codes.shape[1]
-    xc, xs = ops.quantize(x, gs_x)
-    ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
     R = T * k
-    gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=sorted_ids, out_dtype=torch.float32)
-    hc, hs = ops.silu_mul_requant(gu, gs_h)
-    y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16)
+    # the many-row GEMM tiles read A in exactly dequantised f16 form, which the
+    # producers write alongside the codes when it will be read
+    xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) else None)
+    ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
+    gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=sorted_ids, out_dtype=torch.float32,
+                 a_dq=xdq[0] if xdq else None)
+    hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=True if w2.reads_dq(R, R) else None)
+    y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
     out = ops.combine(y, inv, w)
     if keep:
         return out, dict(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv,
@@ -119,10 +126,10 @@ def shared_expert(x, w1, w2, gs_x, gs_h, keep=False):
     """Shared expert: one group, no routing.  Returns y [T, H] bf16."""
     T = x.shape[0]
     off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
-    xc, xs = ops.quantize(x, gs_x)
-    gu = w1.gemm(xc, xs, gs_x, off, T)
-    hc, hs = ops.silu_mul_requant(gu, gs_h)
-    y = w2.gemm(hc, hs, gs_h, off, T, out_dtype=torch.bfloat16)
+    xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(T, T) else None)
+    gu = w1.gemm(xc, xs, gs_x, off, T, a_dq=xdq[0] if xdq else None)
+    hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=True if w2.reads_dq(T, T) else None)
+    y = w2.gemm(hc, hs, gs_h, off, T, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
     if keep:
         return y, dict(xc=xc, xs=xs, gate_up=gu, hc=hc, hs=hs)
     return y
@@ -133,8 +140,8 @@ def mla_projections(x1, x2, w_qakv, w_qb, gs_x1, gs_x2):
     global scales), x2 [T, 1536] through q_b.  Both outputs bf16."""
     T = x1.shape[0]
     off = torch.tensor([0, T], dtype=torch.int32, device=x1.device)
-    c1, s1 = ops.quantize(x1, gs_x1)
-    o1 = w_qakv.gemm(c1, s1, gs_x1, off, T, out_dtype=torch.bfloat16)
-    c2, s2 = ops.quantize(x2, gs_x2)
-    o2 = w_qb.gemm(c2, s2, gs_x2, off, T, out_dtype=torch.bfloat16)
+    c1, s1, *d1 = ops.quantize(x1, gs_x1, dq=True if w_qakv.reads_dq(T, T) else None)
+    o1 = w_qakv.gemm(c1, s1, gs_x1, off, T, out_dtype=torch.bfloat16, a_dq=d1[0] if d1 else None)
+    c2, s2, *d2 = ops.quantize(x2, gs_x2, dq=True if w_qb.reads_dq(T, T) else None)
+    o2 = w_qb.gemm(c2, s2, gs_x2, off, T, out_dtype=torch.bfloat16, a_dq=d2[0] if d2 else None)
     return o1, o2

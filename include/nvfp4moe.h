@@ -92,6 +92,11 @@ int32_t nvfp4_version(void);
  *   gs       device pointer to ONE float32, the global scale (dequantisation
  *            direction, > 0).
  *   codes    out [rows, cols/2], scales out [rows, cols/16], both dense.
+ *   dq       out [rows, cols] f16 (uint16 storage, 16-byte aligned) or NULL:
+ *            the dequantised values e2m1(code) * e4m3(scale) WITHOUT the
+ *            global scale.  They are exact in f16 (at most five significant
+ *            bits, magnitudes in [2^-10, 2688]).  nvfp4_grouped_gemm can read
+ *            A in this form (a_dq) instead of decoding it itself.
  * Per 16-element block (each step one IEEE float32 operation, no fused
  * multiply-add): bamax = max|x_i|; s = bamax / (6*gs); sq = E4M3(s), rounded
  * to nearest-even and saturated at 448; sf = value(sq).  If sf == 0 every
@@ -104,7 +109,7 @@ int32_t nvfp4_version(void);
  */
 int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
                        int64_t ld_x, const float* gs, uint8_t* codes, uint8_t* scales,
-                       void* stream);
+                       uint16_t* dq, void* stream);
 
 /*
  * nvfp4_global_scale - per-slice global scales from the amax of each slice:
@@ -168,11 +173,22 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *   a_row_index        [M] int32 or NULL: logical row m reads stored row
  *                      a_row_index[m] (the gather by sorted_token_ids);
  *                      NULL means row m is stored row m (then a_rows >= M).
+ *   a_dq               [a_rows, K] f16 (uint16 storage) or NULL: the same A
+ *                      dequantised without its global scale, as the dq
+ *                      output of nvfp4_quantize or silu_mul_requant writes
+ *                      it.  It MUST agree with a_codes/a_scales: a kernel
+ *                      reads whichever form suits it (the 256-row tiles of
+ *                      the tiled layout copy it straight into local memory),
+ *                      and both give the same products.  Ignored when
+ *                      a_rows * K * 2 >= 2^32.
  *   w_codes, w_scales  [G, N, K/2], [G, N, K/16] when w_layout is
  *                      NVFP4_LAYOUT_ROWS; when it is NVFP4_LAYOUT_TILED,
  *                      w_codes is the buffer nvfp4_prepare_weights wrote for
  *                      the same G, N, K and w_scales is ignored (may be NULL).
- *                      The two layouts give bit-identical results.
+ *                      Both layouts give results within the float32
+ *                      summation bound of the exact contraction (groups
+ *                      with many rows may run on a different kernel, so
+ *                      the two are not bitwise equal).
  *   w_gs               [G, n_segs] float32.
  *   n_seg              HOST array of n_segs+1 int32: 0 = n_seg[0] < ... <
  *                      n_seg[n_segs] = N.
@@ -185,16 +201,25 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  * M >= 0, N >= 1, K >= 32 with K % 32 == 0 (K % 256 == 0 for the tiled
  * layout), ld_out >= N, a_rows >= 1 when M > 0 (and >= M when a_row_index
  * is NULL), n_seg increasing from 0 to N; EALIGN unless codes (and the tiled
- * buffer) and out are 16-byte aligned and scales 4-byte aligned.
+ * buffer), a_dq and out are 16-byte aligned and scales 4-byte aligned.
  */
 int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                           int64_t a_rows, const int32_t* a_row_index,
+                           int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
                            const uint8_t* w_codes, const uint8_t* w_scales, int32_t w_layout,
                            const float* w_gs,
                            const int32_t* n_seg, int32_t n_segs,
                            const int32_t* group_offsets, int32_t G,
                            int64_t M, int64_t N, int64_t K,
                            void* out, int32_t out_dtype, int64_t ld_out, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_reads_dq - 1 if nvfp4_grouped_gemm with these sizes
+ * (G groups, M rows, depth K, a_rows stored A rows) and weight layout reads
+ * a_dq when it is given (its 256-row tiles do), else 0.  Lets a caller
+ * produce the f16 form of A only where it is used.  Pure host function; it
+ * neither fails nor sets the last error.
+ */
+int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout);
 
 /*
  * nvfp4_prepare_weights - rearrange NVFP4 weights [G, N, K] (row-major codes
@@ -205,12 +230,13 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
  * buffers may be freed afterwards.
  *   w_codes [G, N, K/2], w_scales [G, N, K/16] (16-byte aligned).
  *   out     nvfp4_prepared_weight_bytes(G, N, K) bytes, 16-byte aligned.
- * Layout: rows in blocks of 16 (last block zero-padded), k in steps of 256;
- * tile (g, block, step) holds 2304 contiguous bytes: for lane l = r + 16q
- * (r = row in block, q = 0..3), bytes [16l, 16l+16) and [1024+16l, 1024+16l+16)
- * are code bytes [32q, 32q+16) and [32q+16, 32q+32) of that row's 128 code
- * bytes of the step, and bytes [2048+4l, 2048+4l+4) its scale bytes
- * [4q, 4q+4) of the step's 16.
+ * Layout: rows in blocks of 32 (last block zero-padded), k in steps of 256,
+ * each step two half-steps h of 128; tile (g, block, step) holds 4608
+ * contiguous bytes, tiles ordered by g, block, step.  With lane
+ * l = c + 32 kh (c = row in block, kh = 0, 1): bytes
+ * [2048h + 1024i + 16l, +16) are code bytes [64h + 32kh + 16i, +16) of that
+ * row's 128 code bytes of the step (i = 0, 1), and bytes
+ * [4096 + 256h + 4l, +4) its scale bytes [8h + 4kh, +4) of the step's 16.
  * Errors: EINVAL for null pointers; ESHAPE unless G >= 1, N >= 1,
  * K % 256 == 0 and K >= 256; EALIGN for misaligned pointers.
  */
@@ -224,6 +250,8 @@ int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, i
  *            [I, 2I) (the stacked gate_up order).
  *   gs_h     ONE float32, the global scale of h.
  *   h_codes  out [M, I/2]; h_scales out [M, I/16].
+ *   h_dq     out [M, I] f16 or NULL: h dequantised without gs_h, as the dq
+ *            output of nvfp4_quantize.
  * Per element in float32, each step one IEEE operation: e = exp(-g) (the
  * same exponential as moe_route_permute, +Inf above 88), s = g / (1 + e),
  * h = s * u; then the quantisation of nvfp4_quantize with gs_h.
@@ -233,7 +261,7 @@ int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, i
  */
 int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64_t I,
                          int64_t ld, const float* gs_h, uint8_t* h_codes, uint8_t* h_scales,
-                         void* stream);
+                         uint16_t* h_dq, void* stream);
 
 /*
  * silu_mul_global_scale - gs_out = fp32(amax(SiLU(gate)*up) / 2688) (1.0 if

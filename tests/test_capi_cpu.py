@@ -48,35 +48,37 @@ def _err(L):
 
 
 def test_quantize_validation(L):
-    assert L.nvfp4_quantize(FAKE, 7, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
-    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 24, 24, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert L.nvfp4_quantize(FAKE, 7, 4, 32, 32, FAKE, FAKE, FAKE, NULL, NULL) == lib.EINVAL
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 24, 24, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
     assert "multiple of 16" in _err(L)
-    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 32, 16, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert L.nvfp4_quantize(NULL, lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 32, 16, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert L.nvfp4_quantize(NULL, lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE, NULL, NULL) == lib.EINVAL
     assert L.nvfp4_quantize(ctypes.c_void_p(0x1004), lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE,
+                            NULL, NULL) == lib.EALIGN
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 0, 32, 32, NULL, NULL, NULL, NULL, NULL) == lib.OK
+    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 4, 32, 32, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1008),
                             NULL) == lib.EALIGN
-    assert L.nvfp4_quantize(FAKE, lib.DTYPE_BF16, 0, 32, 32, NULL, NULL, NULL, NULL) == lib.OK
 
 
 def test_route_validation(L):
     f = L.moe_route_permute
-    assert f(FAKE, 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert f(FAKE, 4, 2000, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert f(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert f(FAKE, 4, 384, 17, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert f(FAKE, -1, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert f(NULL, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert f(FAKE, 4, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 2000, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert f(FAKE, 4, 384, 17, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert f(FAKE, -1, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert f(NULL, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, NULL) == lib.EINVAL
     assert f(FAKE, 4, 8, 2, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == lib.EINVAL
 
 
 def _gemm(L, **kw):
-    a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, w_codes=FAKE,
+    a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, a_dq=NULL, w_codes=FAKE,
              w_scales=FAKE, w_layout=lib.LAYOUT_ROWS, w_gs=FAKE, n_seg=[0, 64], group_offsets=FAKE, G=1,
              M=8, N=64, K=64, out=FAKE, out_dtype=lib.DTYPE_F32, ld_out=64)
     a.update(kw)
     seg = (ctypes.c_int32 * len(a["n_seg"]))(*a["n_seg"])
     return L.nvfp4_grouped_gemm(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"],
-                                a["w_codes"], a["w_scales"], a["w_layout"], a["w_gs"], seg,
+                                a["a_dq"], a["w_codes"], a["w_scales"], a["w_layout"], a["w_gs"], seg,
                                 len(a["n_seg"]) - 1,
                                 a["group_offsets"], a["G"], a["M"], a["N"], a["K"], a["out"],
                                 a["out_dtype"], a["ld_out"], NULL)
@@ -95,14 +97,25 @@ def test_gemm_validation(L):
     assert _gemm(L, out_dtype=5) == lib.EINVAL
     assert _gemm(L, w_codes=NULL) == lib.EINVAL
     assert _gemm(L, out=ctypes.c_void_p(0x1008)) == lib.EALIGN
+    assert _gemm(L, a_dq=ctypes.c_void_p(0x1008)) == lib.EALIGN
     assert _gemm(L, M=0, a_codes=NULL, out=NULL) == lib.OK
     assert _gemm(L, w_layout=2) == lib.EINVAL
     assert _gemm(L, w_layout=lib.LAYOUT_TILED) == lib.ESHAPE       # K % 256
     assert _gemm(L, w_layout=lib.LAYOUT_ROWS, w_scales=NULL) == lib.EINVAL
 
 
+def test_reads_dq_query(L):
+    q = L.nvfp4_grouped_gemm_reads_dq
+    assert q(1, 8192, 7168, 8192, lib.LAYOUT_TILED) == 1
+    assert q(1, 8192, 7168, 8192, lib.LAYOUT_ROWS) == 0
+    assert q(384, 1536, 7168, 256, lib.LAYOUT_TILED) == 0      # few rows per group
+    assert q(1, 255, 256, 255, lib.LAYOUT_TILED) == 0          # no full 256-row tile
+    assert q(1, 4096, 160, 4096, lib.LAYOUT_TILED) == 0        # K % 256
+    assert q(1, 1 << 20, 4096, 1 << 19, lib.LAYOUT_TILED) == 0  # a_rows * K * 2 >= 2^32
+
+
 def test_prepare_validation_and_size(L):
-    assert L.nvfp4_prepared_weight_bytes(2, 33, 512) == 2 * 3 * 2 * 2304
+    assert L.nvfp4_prepared_weight_bytes(2, 33, 512) == 2 * 2 * 2 * 4608
     assert L.nvfp4_prepared_weight_bytes(1, 16, 128) == 0
     assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, 128, FAKE, NULL) == lib.ESHAPE
     assert L.nvfp4_prepare_weights(NULL, FAKE, 1, 16, 256, FAKE, NULL) == lib.EINVAL
@@ -110,9 +123,11 @@ def test_prepare_validation_and_size(L):
 
 
 def test_silu_and_combine_validation(L):
-    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 24, 48, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 32, 32, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
-    assert L.silu_mul_requant(FAKE, 3, 4, 32, 64, FAKE, FAKE, FAKE, NULL) == lib.EINVAL
+    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 24, 48, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 32, 64, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004),
+                              NULL) == lib.EALIGN
+    assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 32, 32, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
+    assert L.silu_mul_requant(FAKE, 3, 4, 32, 64, FAKE, FAKE, FAKE, NULL, NULL) == lib.EINVAL
     assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 0, 64, FAKE, NULL) == lib.ESHAPE
     assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 2, 60, FAKE, NULL) == lib.ESHAPE
     assert L.moe_combine(FAKE, lib.DTYPE_BF16, NULL, FAKE, 4, 2, 64, FAKE, NULL) == lib.EINVAL

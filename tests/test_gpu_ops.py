@@ -39,6 +39,10 @@ def test_quantize_bit_exact(rows, cols, dtype):
     c, s = ops.quantize(xt, gst)
     assert np.array_equal(to_np(c), c_ref)
     assert np.array_equal(to_np(s), s_ref)
+    # with the f16 form: same codes, and dq = e2m1 * e4m3 exactly
+    c2, s2, dq = ops.quantize(xt, gst, dq=True)
+    assert np.array_equal(to_np(c2), c_ref) and np.array_equal(to_np(s2), s_ref)
+    assert np.array_equal(to_np(dq).astype(np.float64), quant.dequantize_blocks(c_ref, s_ref))
 
 
 def test_quantize_saturation_and_tiny_gs():
@@ -146,12 +150,20 @@ def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=
     kw = dict(a_row_index=T(row_index) if gather else None, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
     out = ops.grouped_gemm(*args, **kw)
     got = to_np(out)
+    outs = [("rows", got)]
     if K % 256 == 0:
-        # the tiled weight layout must give bit-identical results
+        # the tiled weight layout (which may route many-row groups to another
+        # kernel) is checked against the same bound
         tiled = ops.prepare_weights(T(wc), T(ws))
-        got_t = to_np(ops.grouped_gemm(*args, w_tiled=tiled, **kw))
-        assert np.array_equal(got_t.view(np.uint32) if got_t.dtype == np.float32 else got_t,
-                              got.view(np.uint32) if got.dtype == np.float32 else got), "tiled layout differs"
+        outs.append(("tiled", to_np(ops.grouped_gemm(*args, w_tiled=tiled, **kw))))
+        if ops.gemm_reads_dq(G, M, K, a_rows, True):
+            # A also in f16 form (from the oracle's dequantisation): the
+            # many-row tiles copy it instead of decoding the codes, with the
+            # same products in the same order, so the output is identical
+            a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16))
+            o_dq = to_np(ops.grouped_gemm(*args, w_tiled=tiled, a_dq=a_dq, **kw))
+            assert np.array_equal(o_dq, outs[-1][1])
+            outs.append(("tiled+dq", o_dq))
     # oracle (the definition) and the float64 pieces for the error bound
     ref_o = moe.grouped_gemm(ac, as_, ags, wc, ws, wgs, n_seg, off, a_row_index=row_index,
                              out_dtype="bf16" if out_bf16 else "f32")
@@ -165,11 +177,12 @@ def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=
         alpha = np.empty(N)
         for s in range(S):
             alpha[n_seg[s]:n_seg[s + 1]] = float(F32(F32(ags) * wgs[g, s]))
-        worst = max(worst, check_gemm(got[r0:r1], ex, ab, alpha[None, :], K, out_bf16, "group %d" % g))
-        # and against the oracle's own rounded output
-        assert np.allclose(got[r0:r1], ref_o[r0:r1], rtol=2 ** -7 if out_bf16 else 1e-4,
-                           atol=np.abs(ref_o[r0:r1]).max() * 1e-4 + 1e-30)
-    log("  max err / rms = %.3g" % worst)
+        for name, o in outs:
+            worst = max(worst, check_gemm(o[r0:r1], ex, ab, alpha[None, :], K, out_bf16, "%s group %d" % (name, g)))
+            # and against the oracle's own rounded output
+            assert np.allclose(o[r0:r1], ref_o[r0:r1], rtol=2 ** -7 if out_bf16 else 1e-4,
+                               atol=np.abs(ref_o[r0:r1]).max() * 1e-4 + 1e-30)
+    log("  max err / rms = %.3g (%s)" % (worst, ", ".join(n for n, _ in outs)))
     return got
 
 
@@ -195,9 +208,16 @@ def test_gemm_k_tails():
 
 
 def test_gemm_tile_kernel_shapes():
-    # enough rows per group for the LDS-tiled kernel; ragged M and N tails
+    # enough rows per group for the tiled kernels; ragged M and N tails
     _gemm_case([300, 130, 0, 77], 200, 256, [0, 64, 200], 5, gather=True)
     _gemm_case([513], 384, 512, [0, 384], 6, out_bf16=True)
+
+
+def test_gemm_big_tiles_with_remainders():
+    # full 256-row tiles plus left-over rows of 1..255 in several groups,
+    # column tiles with a partial last one, two segments
+    _gemm_case([456, 3, 256, 0, 611, 70], 520, 512, [0, 260, 520], 12, gather=True)
+    _gemm_case([1024, 255, 257], 256, 768, [0, 256], 13, out_bf16=True)
 
 
 def test_gemm_four_segments_and_bf16():
@@ -221,25 +241,27 @@ def test_prepare_weights_is_the_documented_permutation():
     wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
     ws = rng.integers(0, 127, (G, N, K // 16), dtype=np.uint8)
     out = to_np(ops.prepare_weights(torch.from_numpy(wc).to(dev()), torch.from_numpy(ws).to(dev())))
-    NB, KS = (N + 15) // 16, K // 256
-    assert out.size == G * NB * KS * 2304
-    t = out.reshape(G, NB, KS, 2304)
+    NB, KS = (N + 31) // 32, K // 256
+    assert out.size == G * NB * KS * 4608
+    t = out.reshape(G, NB, KS, 4608)
     for g in range(G):
         for nb in range(NB):
             for ks in range(KS):
-                for l in range(64):
-                    r, q = l % 16, l // 16
-                    row = nb * 16 + r
-                    c0 = t[g, nb, ks, 16 * l:16 * l + 16]
-                    c1 = t[g, nb, ks, 1024 + 16 * l:1024 + 16 * l + 16]
-                    sc = t[g, nb, ks, 2048 + 4 * l:2048 + 4 * l + 4]
-                    if row < N:
-                        base = ks * 128 + 32 * q
-                        assert np.array_equal(c0, wc[g, row, base:base + 16])
-                        assert np.array_equal(c1, wc[g, row, base + 16:base + 32])
-                        assert np.array_equal(sc, ws[g, row, ks * 16 + 4 * q:ks * 16 + 4 * q + 4])
-                    else:
-                        assert not c0.any() and not c1.any() and not sc.any()
+                for h in range(2):
+                    for l in range(64):
+                        c, kh = l % 32, l // 32
+                        row = nb * 32 + c
+                        c0 = t[g, nb, ks, 2048 * h + 16 * l:2048 * h + 16 * l + 16]
+                        c1 = t[g, nb, ks, 2048 * h + 1024 + 16 * l:2048 * h + 1024 + 16 * l + 16]
+                        sc = t[g, nb, ks, 4096 + 256 * h + 4 * l:4096 + 256 * h + 4 * l + 4]
+                        if row < N:
+                            base = ks * 128 + 64 * h + 32 * kh
+                            assert np.array_equal(c0, wc[g, row, base:base + 16])
+                            assert np.array_equal(c1, wc[g, row, base + 16:base + 32])
+                            sb = ks * 16 + 8 * h + 4 * kh
+                            assert np.array_equal(sc, ws[g, row, sb:sb + 4])
+                        else:
+                            assert not c0.any() and not c1.any() and not sc.any()
 
 
 def test_gemm_deterministic():
@@ -267,6 +289,9 @@ def test_silu_mul_requant_bit_exact(M, I, dtype):
     c, s = ops.silu_mul_requant(t, torch.tensor([gs], device=dev()))
     assert np.array_equal(to_np(c), c_ref)
     assert np.array_equal(to_np(s), s_ref)
+    c2, s2, dq = ops.silu_mul_requant(t, torch.tensor([gs], device=dev()), dq=True)
+    assert np.array_equal(to_np(c2), c_ref) and np.array_equal(to_np(s2), s_ref)
+    assert np.array_equal(to_np(dq).astype(np.float64), quant.dequantize_blocks(c_ref, s_ref))
     g = to_np(ops.silu_mul_global_scale(t))
     assert g[0] == quant.global_scale(quant.amax(h))
 
