@@ -44,15 +44,17 @@ __device__ __forceinline__ T clampv(T v, T lo, T hi) {
 }
 
 // The `slot`-th row tile of a launch.  Every group g (rows [lo, hi) from the
-// device offsets) contributes the rows [start, hi) with start = lo, or, when
-// skip_bm > 0, start = lo + floor((hi - lo) / skip_bm) * skip_bm (the rows a
-// skip_bm-tile launch leaves over); they are cut into tiles of bm rows, the
-// last one partial unless full_only (then partial tiles are dropped).  Groups
-// are taken in order.  Executed by a whole wave (all lanes get the result).
-// Offsets are clamped into [0, M] and forced non-decreasing, so garbage
-// offsets cannot produce rows outside [0, M).
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int bm,
-                          int skip_bm, bool full_only, int& g_out, int64_t& r0, int64_t& r1) {
+// device offsets) contributes the rows [start, hi): start = lo, or, when
+// skip_bm > 0, the rows another launch leaves over, which tiles skip_bm rows
+// at a time and takes the last partial tile too if it has at least skip_min
+// rows.  They are cut into tiles of bm rows; a last partial tile is kept if
+// it has at least last_min rows (1: always, bm: never).  Groups are taken in
+// order.  Executed by a whole wave (all lanes get the result).  Offsets are
+// clamped into [0, M] and forced non-decreasing, so garbage offsets cannot
+// produce rows outside [0, M).
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int bm,
+                                          int last_min, int skip_bm, int skip_min, int& g_out, int64_t& r0,
+                                          int64_t& r1) {
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int g0 = 0; g0 < G; g0 += 64) {
@@ -63,8 +65,74 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int64_t M,
       lo = clampv<int64_t>(offsets[g], 0, M);
       hi = clampv<int64_t>(offsets[g + 1], 0, M);
       if (hi < lo) hi = lo;
-      if (skip_bm > 0) lo += (hi - lo) / skip_bm * skip_bm;
-      tiles = (int32_t)(full_only ? (hi - lo) / bm : (hi - lo + bm - 1) / bm);
+      if (skip_bm > 0) {
+        const int64_t rest = (hi - lo) % skip_bm;
+        lo = rest >= skip_min ? hi : hi - rest;
+      }
+      tiles = (int32_t)((hi - lo) / bm + ((hi - lo) % bm >= last_min ? 1 : 0));
+    }
+    int32_t incl = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const int32_t excl = incl - tiles;
+    const int32_t total = __shfl(incl, 63, 64);
+    if (slot < base + total) {
+      const bool mine = g < G && slot >= base + excl && slot < base + incl;
+      const uint64_t mask = __ballot(mine);
+      const int src = __ffsll((unsigned long long)mask) - 1;
+      g_out = __shfl(g, src, 64);
+      const int32_t lo_s = __shfl((int32_t)lo, src, 64);
+      const int32_t hi_s = __shfl((int32_t)hi, src, 64);
+      const int32_t ex_s = __shfl(excl, src, 64);
+      r0 = lo_s + (slot - base - ex_s) * bm;
+      r1 = r0 + bm < hi_s ? r0 + bm : hi_s;
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// find_tile with every offset loaded before the scan (one memory round trip
+// instead of one per 64 groups), for kernels with registers to spare at the
+// start of a tile.
+constexpr int kMaxChunks = 16;   // groups in chunks of 64, up to 1024 groups
+
+__device__ __forceinline__ bool find_tile_batched(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int bm,
+                                          int last_min, int skip_bm, int skip_min, int& g_out, int64_t& r0,
+                                          int64_t& r1) {
+  const int lane = threadIdx.x & 63;
+  // all the offsets first (one memory round trip), then the scan
+  int32_t lo_c[kMaxChunks], hi_c[kMaxChunks];
+#pragma unroll
+  for (int ch = 0; ch < kMaxChunks; ++ch) {
+    const int g = ch * 64 + lane;
+    lo_c[ch] = 0;
+    hi_c[ch] = 0;
+    if (ch * 64 < G && g < G) {
+      lo_c[ch] = offsets[g];
+      hi_c[ch] = offsets[g + 1];
+    }
+  }
+  int64_t base = 0;
+#pragma unroll
+  for (int ch = 0; ch < kMaxChunks; ++ch) {
+    if (ch * 64 >= G) break;
+    const int g = ch * 64 + lane;
+    int64_t lo = 0, hi = 0;
+    int32_t tiles = 0;
+    if (g < G) {
+      lo = clampv<int64_t>(lo_c[ch], 0, M);
+      hi = clampv<int64_t>(hi_c[ch], 0, M);
+      if (hi < lo) hi = lo;
+      if (skip_bm > 0) {
+        const int64_t rest = (hi - lo) % skip_bm;
+        lo = rest >= skip_min ? hi : hi - rest;
+      }
+      tiles = (int32_t)((hi - lo) / bm + ((hi - lo) % bm >= last_min ? 1 : 0));
     }
     int32_t incl = tiles;
 #pragma unroll
@@ -129,7 +197,7 @@ __global__ __launch_bounds__(256) void gemm_stream16(GemmArgs p, int64_t n_tiles
   const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
   int g;
   int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, 16 * RB, skip_bm, false, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, 16 * RB, 1, skip_bm, skip_bm, g, row0, row1)) return;
   const int64_t n0 = nt * BN + wave * NBW * 16;
   if (n0 >= p.N) return;
   const int64_t K = p.K;
@@ -298,7 +366,7 @@ __global__ __launch_bounds__(256) void gemm_tile16(GemmArgs p, int64_t n_tiles) 
   const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
   int g;
   int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, TBM, 0, false, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, TBM, 1, 0, 0, g, row0, row1)) return;
   const int64_t n0 = nt * TBN;
   const int64_t K = p.K;
   const int64_t KB = K / 2;
@@ -421,18 +489,11 @@ __device__ __forceinline__ int acc32_row(int i, int kh) { return 8 * (i >> 2) + 
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
 template <int NBW, int RB>
-__global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm) {
+__device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
+                                              int wave, int lane) {
   constexpr int BN = 4 * NBW * 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31;
   const int kh = lane >> 5;
-  const int64_t slot = (int64_t)blockIdx.x / n_tiles;
-  const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
-  int g;
-  int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, skip_bm, false, g, row0, row1)) return;
-  g = __builtin_amdgcn_readfirstlane(g);
   const int64_t n0 = nt * BN + wave * NBW * 32;
   if (n0 >= p.N) return;
   const int64_t K = p.K;
@@ -543,6 +604,24 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
   }
 }
 
+// One tile per workgroup, slot-major (the grid is an upper bound; workgroups
+// without a tile exit after one pass over the group offsets).
+template <int NBW, int RB, bool BATCHED>
+__global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm, int skip_min) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t slot = (int64_t)blockIdx.x / n_tiles;
+  const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
+  int g;
+  int64_t row0, row1;
+  const bool found =
+      BATCHED ? find_tile_batched(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)
+              : find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1);
+  if (!found) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  stream32_tile<NBW, RB>(p, g, row0, row1, nt, wave, lane);
+}
+
 // ---------------------------------------------------------------------------
 // gemm_big32: 256 x 256 output tiles for groups with many rows, 4 waves (one
 // per SIMD), each wave all 256 rows x 64 columns = 8 x 2 blocks of 32 x 32
@@ -565,10 +644,24 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
 //  * Each of a substep's 16 MFMAs is followed in program order by a slice of
 //    vector work: the next substep's W fragments, and in substeps 2..7 the
 //    conversion and store of chunks of the next A half-tile.
-// Workgroup ids are remapped so that the workgroups resident on one XCD take
-// consecutive logical tiles (same A row tile, neighbouring columns), which
-// keeps the A tile in that XCD's L2.
+// Workgroups are mapped to tiles by xcd_tile.
+// Workgroup -> (row slot, column tile) for the 256 x 256 kernels.  The
+// hardware sends workgroup b to XCD b % 8; XCD x takes slots x, x + 8, ...,
+// each with all its column tiles in turn, so a slot's A rows stay in one
+// XCD's L2 while its neighbours' run on the others, and slots without a tile
+// (the grid is an upper bound) fall evenly on all XCDs.  The grid holds a
+// multiple of 8 slots.
+__device__ __forceinline__ void xcd_tile(int64_t bid, int64_t n_tiles, int64_t& slot, int64_t& nt) {
+  const int64_t xcd = bid % 8, idx = bid / 8;
+  slot = idx / n_tiles * 8 + xcd;
+  nt = idx % n_tiles;
+}
+
 constexpr int BIG = 256;
+// with A in f16 form, the last tile of a group goes to the 256-row kernel
+// when it has at least this many rows (fewer: the streaming kernel, for
+// which a short tile's weight stream is not latency-bound)
+constexpr int kBigMinLast = 129;
 constexpr int kAHalfBytes = BIG * 256;           // 64 KiB per f16 half-tile
 constexpr int kBigThreads = 256;
 
@@ -584,16 +677,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t
   const int c = lane & 31;
   const int kh = lane >> 5;
 
-  const int64_t total = gridDim.x;
-  const int64_t bid = blockIdx.x;
-  const int64_t q8 = total / 8, r8 = total % 8;
-  const int64_t xcd = bid % 8, idx = bid / 8;
-  const int64_t logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-  const int64_t slot = logical / n_tiles;
-  const int64_t nt = logical - slot * n_tiles;
+  int64_t slot, nt;
+  xcd_tile(blockIdx.x, n_tiles, slot, nt);
   int g;
   int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, BIG, 0, true, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, BIG, BIG, 0, 0, g, row0, row1)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   const int64_t n0 = nt * BIG;
   const int64_t K = p.K;
@@ -775,63 +863,60 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t
 
 // ---------------------------------------------------------------------------
 // gemm_big32_dq: the 256 x 256 tiles of gemm_big32 when A also comes in its
-// exactly dequantised f16 form (a_dq).  A half-tiles then go from global
-// memory straight into local memory (global_load_lds_dwordx4, 1 KiB = four
-// 256-byte rows per wave instruction), so A costs the waves neither vector
-// registers nor conversion work, and the vector unit only dequantises W.
-//  * Wave w copies rows 64 w .. 64 w + 63: its copy i fills rows
-//    64 w + 4 i .. +3, lane l writing physical chunk l % 16 of row
-//    64 w + 4 i + l / 16.  That chunk holds logical chunk (l % 16) ^ (row % 16)
-//    (the swizzle of gemm_big32), so the lane reads those 16 bytes of the row.
-//  * The next half-tile's 16 copies are spread over substeps 0-3; the next
+// exactly dequantised f16 form (a_dq), for every row of every group: the
+// last tile of a group may be partial.  A half-tiles go from global memory
+// straight into local memory (global_load_lds_dwordx4, 1 KiB = four 256-byte
+// rows per wave instruction), so A costs the waves neither vector registers
+// nor conversion work, and the vector unit only dequantises W.
+//  * A tile of R = 32 RB rows (RB = 8, or 4, 2, 1 for the last tile of a
+//    group with at most 128, 64, 32 rows) is copied by the four waves, wave w
+//    taking rows 8 RB w .. 8 RB w + 8 RB - 1 in 2 RB copies: copy i fills
+//    rows 8 RB w + 4 i .. +3, lane l writing physical chunk l % 16 of row
+//    8 RB w + 4 i + l / 16.  That chunk holds logical chunk (l % 16) ^ (row %
+//    16) (the swizzle of gemm_big32), so the lane reads those 16 bytes of
+//    the row.  Rows past the group's end copy its last row; their results
+//    are not stored.
+//  * The next half-tile's copies are spread over substeps 0-3; the next
 //    half-step's W words are loaded at substep 0 into a second register set.
 //    Nothing is waited for before substep 7, when the next half-step's first
 //    W fragment is dequantised; the copies have landed by the barrier.
 //    (The compiler waits for all outstanding vector memory operations once
 //    copies into local memory and register loads are both in flight, so no
 //    load is issued after substep 0 that substeps 1-6 would wait for.)
-__global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
-  constexpr int RB = 8;     // 256 rows per wave
-  constexpr int CB = 2;     // 64 columns per wave
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+template <int RB>
+__device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
+                                            int64_t n0, int wave, int lane) {
+  constexpr int CB = 2;            // 64 columns per wave
+  constexpr int NC = 2 * RB;       // copies per wave and half-step
   const int c = lane & 31;
   const int kh = lane >> 5;
-
-  const int64_t total = gridDim.x;
-  const int64_t bid = blockIdx.x;
-  const int64_t q8 = total / 8, r8 = total % 8;
-  const int64_t xcd = bid % 8, idx = bid / 8;
-  const int64_t logical = xcd < r8 ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-  const int64_t slot = logical / n_tiles;
-  const int64_t nt = logical - slot * n_tiles;
-  int g;
-  int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, BIG, 0, true, g, row0, row1)) return;
-  g = __builtin_amdgcn_readfirstlane(g);
-  const int64_t n0 = nt * BIG;
   const int64_t K = p.K;
   const int64_t nks = K / 256;
 
   // byte offsets in a_dq of this lane's 16 bytes of each copy, less the
   // half-step's k offset (the host guarantees a_rows * K * 2 < 2^32)
-  uint32_t a_off[16];
+  // (lane l < 8 RB looks up the stored row of the wave's row l once; the
+  // copies take it from that lane)
+  int32_t ar_l;
+  {
+    const int64_t m = clampv<int64_t>(row0 + 8 * RB * wave + (lane < 8 * RB ? lane : 0), row0, row1 - 1);
+    const int64_t ar = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
+    ar_l = (int32_t)clampv<int64_t>(ar, 0, p.a_rows - 1);
+  }
+  uint32_t a_off[NC];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 64 * wave + 4 * i + (lane >> 4);
-    const int64_t m = row0 + r;                          // always < row1 (full tiles)
-    int64_t ar = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
-    ar = clampv<int64_t>(ar, 0, p.a_rows - 1);
-    a_off[i] = (uint32_t)(ar * K * 2 + 16 * ((lane & 15) ^ (r & 15)));
+  for (int i = 0; i < NC; ++i) {
+    const int r = 4 * i + (lane >> 4);             // row within the wave's rows
+    const int tr = 8 * RB * wave + r;               // row within the tile (sets the swizzle)
+    const uint32_t ar = (uint32_t)__shfl(ar_l, r, 64);
+    a_off[i] = ar * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (tr & 15));
   }
   const uint8_t* a_base = (const uint8_t*)p.a_dq;
   auto a_copy = [&](int64_t hs, int buf, int i) {
     __builtin_amdgcn_global_load_lds(
         (const void*)(a_base + hs * 256 + a_off[i]),
-        (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (64 * wave + 4 * i) * 256), 16, 0,
-        0);
+        (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (8 * RB * wave + 4 * i) * 256), 16,
+        0, 0);
   };
 
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
@@ -866,7 +951,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
 
   WWords cur, nxt;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a_copy(0, 0, i);
+  for (int i = 0; i < NC; ++i) a_copy(0, 0, i);
   w_load(0, cur);
   half8_t bf[CB];
 #pragma unroll
@@ -897,25 +982,29 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
         for (int cb = 0; cb < CB; ++cb) {
           acc[rb][cb] = mfma32(af[rb], bf[cb], acc[rb][cb]);
           const int s = rb * CB + cb;
-          // the next half-tile: copies 4 j .. 4 j + 3 after slots 3, 7, 11, 15
-          if (j < 4 && (s & 3) == 3) a_copy(hn, h ^ 1, 4 * j + (s >> 2));
-          // W fragment of the next substep in slots 0-9, five parts per
-          // column block (scale, then one f16 pair each); substep 7 prepares
-          // substep 0 of the next half-step
-          if (s < 10) {
-            const int wc = s / 5, part = s % 5;
-            const uint32_t word = j < 7 ? (j + 1 < 4 ? cur.w0[wc][j + 1] : cur.w1[wc][j + 1 - 4]) : nxt.w0[wc][0];
-            if (part == 0) {
-              sfn[wc] = scale_pair(j < 7 ? byte_of(cur.ws[wc], (j + 1) >> 1) : byte_of(nxt.ws[wc], 0));
-            } else {
-              const half2_t v = dequant_pair(word, part - 1, sfn[wc]);
-              bn[wc][2 * (part - 1)] = v[0];
-              bn[wc][2 * (part - 1) + 1] = v[1];
-            }
+          // the next half-tile's copies: NC / 4 per substep in substeps 0-3
+          // after slots 3, 7, ... (RB = 1: one in substeps 0 and 1)
+          if constexpr (RB >= 2) {
+            if (j < 4 && (s & 3) == 3) a_copy(hn, h ^ 1, j * (RB / 2) + (s >> 2));
+          } else {
+            if (j < 2 && s == 1) a_copy(hn, h ^ 1, j);
           }
         }
         // af[rb] is dead for this substep: fetch it for the next one
         if (j < 7) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[j + 1]);
+      }
+      // W fragments of the next substep (substep 7 prepares substep 0 of the
+      // next half-step), interleaved by the scheduler with the MFMAs above
+#pragma unroll
+      for (int wc = 0; wc < CB; ++wc) {
+        const uint32_t word = j < 7 ? (j + 1 < 4 ? cur.w0[wc][j + 1] : cur.w1[wc][j + 1 - 4]) : nxt.w0[wc][0];
+        sfn[wc] = scale_pair(j < 7 ? byte_of(cur.ws[wc], (j + 1) >> 1) : byte_of(nxt.ws[wc], 0));
+#pragma unroll
+        for (int part = 0; part < 4; ++part) {
+          const half2_t v = dequant_pair(word, part, sfn[wc]);
+          bn[wc][2 * part] = v[0];
+          bn[wc][2 * part + 1] = v[1];
+        }
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) bf[cb] = bn[cb];
@@ -937,8 +1026,38 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        store_out(p, row0 + rb * 32 + acc32_row(i, kh), n, alpha * acc[rb][cb][i]);
+      for (int i = 0; i < 16; ++i) {
+        const int64_t m = row0 + rb * 32 + acc32_row(i, kh);
+        if (m < row1) store_out(p, m, n, alpha * acc[rb][cb][i]);
+      }
+  }
+}
+
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t slot, nt;
+  xcd_tile(blockIdx.x, n_tiles, slot, nt);
+  int g;
+  int64_t row0, row1;
+  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG, kBigMinLast, 0, 0, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane((int)row0);
+  row1 = __builtin_amdgcn_readfirstlane((int)row1);
+  const int64_t n0 = nt * BIG;
+  const int64_t rows = row1 - row0;
+  if constexpr (kBigMinLast > 128) {
+    big_dq_tile<8>(p, lds, g, row0, row1, n0, wave, lane);
+  } else {
+    if (rows > 128)
+      big_dq_tile<8>(p, lds, g, row0, row1, n0, wave, lane);
+    else if (rows > 64 || kBigMinLast > 64)
+      big_dq_tile<4>(p, lds, g, row0, row1, n0, wave, lane);
+    else if (rows > 32 || kBigMinLast > 32)
+      big_dq_tile<2>(p, lds, g, row0, row1, n0, wave, lane);
+    else
+      big_dq_tile<1>(p, lds, g, row0, row1, n0, wave, lane);
   }
 }
 
@@ -949,18 +1068,23 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (a.w_tiled) {
     if (gemm_uses_big_tiles(a.G, a.M, true)) {
-      // many rows per group: full 256-row tiles on the matrix-core kernel, the
-      // rows left over at the end of each group on the streaming kernel
+      // many rows per group: 256-row tiles on the matrix-core kernel (with A
+      // in f16 form also a group's last tile if it has kBigMinLast rows or
+      // more), the rows left over at the end of each group on the streaming
+      // kernel.  Tile counts are upper bounds (the group sizes are on the
+      // device); workgroups without a tile exit.
+      const bool dq = a.a_dq != nullptr;
+      const int skip_min = dq ? kBigMinLast : BIG;
       constexpr int NBW = 2, RB = 2;
       const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-      const int64_t slots_s = (a.M + 32 * RB - 1) / (32 * RB) + a.G;
-      hipLaunchKernelGGL((gemm_stream32<NBW, RB>), dim3((unsigned)(slots_s * n_tiles_s)), dim3(256), 0, s, a,
-                         n_tiles_s, BIG);
+      const int64_t work_s = ((a.M + 32 * RB - 1) / (32 * RB) + a.G) * n_tiles_s;
+      hipLaunchKernelGGL((gemm_stream32<NBW, RB, true>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s, BIG,
+                         skip_min);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-      const int64_t slots = a.M / BIG;
-      if (a.a_dq)
+      const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
+      if (dq)
         hipLaunchKernelGGL(gemm_big32_dq, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
       else
         hipLaunchKernelGGL(gemm_big32, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
@@ -968,8 +1092,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
     }
     constexpr int NBW = 2;
     const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-    const int64_t slots = (a.M + 31) / 32 + a.G;
-    hipLaunchKernelGGL((gemm_stream32<NBW, 1>), dim3((unsigned)(slots * n_tiles)), dim3(256), 0, s, a, n_tiles, 0);
+    const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
+    hipLaunchKernelGGL((gemm_stream32<NBW, 1, false>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0);
     return hipGetLastError();
   }
   if (a.M >= (int64_t)64 * a.G && a.K % TBK == 0) {

@@ -158,11 +158,15 @@ def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=
         outs.append(("tiled", to_np(ops.grouped_gemm(*args, w_tiled=tiled, **kw))))
         if ops.gemm_reads_dq(G, M, K, a_rows, True):
             # A also in f16 form (from the oracle's dequantisation): the
-            # many-row tiles copy it instead of decoding the codes, with the
-            # same products in the same order, so the output is identical
+            # many-row kernel copies it instead of decoding the codes.  Rows in
+            # full 256-row tiles see the same products in the same order as
+            # without it, so they are identical; the rest (the last tile of
+            # each group) is checked against the bound below
             a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16))
             o_dq = to_np(ops.grouped_gemm(*args, w_tiled=tiled, a_dq=a_dq, **kw))
-            assert np.array_equal(o_dq, outs[-1][1])
+            for g in range(G):
+                full = (off[g + 1] - off[g]) // 256 * 256
+                assert np.array_equal(o_dq[off[g]:off[g] + full], outs[-1][1][off[g]:off[g] + full]), g
             outs.append(("tiled+dq", o_dq))
     # oracle (the definition) and the float64 pieces for the error bound
     ref_o = moe.grouped_gemm(ac, as_, ags, wc, ws, wgs, n_seg, off, a_row_index=row_index,
@@ -218,6 +222,12 @@ def test_gemm_big_tiles_with_remainders():
     # column tiles with a partial last one, two segments
     _gemm_case([456, 3, 256, 0, 611, 70], 520, 512, [0, 260, 520], 12, gather=True)
     _gemm_case([1024, 255, 257], 256, 768, [0, 256], 13, out_bf16=True)
+
+
+def test_gemm_big_tiles_every_last_tile_height():
+    # group sizes whose last tile takes each of the 256/128/64/32-row forms
+    # (1, 31, 32, 33, 64, 65, 128, 129, 255 left-over rows)
+    _gemm_case([257, 287, 288, 289, 320, 321, 384, 385, 511, 256], 96, 256, [0, 40, 96], 14, gather=True)
 
 
 def test_gemm_four_segments_and_bf16():
