@@ -1075,7 +1075,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
       // device); workgroups without a tile exit.
       const bool dq = a.a_dq != nullptr;
       const int skip_min = dq ? kBigMinLast : BIG;
-      constexpr int NBW = 2, RB = 2;
+      constexpr int NBW = 2, RB = 1;
       const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
       const int64_t work_s = ((a.M + 32 * RB - 1) / (32 * RB) + a.G) * n_tiles_s;
       hipLaunchKernelGGL((gemm_stream32<NBW, RB, true>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s, BIG,
