@@ -90,8 +90,11 @@ class Layer:
         self.dq2 = True if self.w2.reads_dq(R, R) else None
         torch.cuda.synchronize()
 
-    def step(self, ev=None):
-        """One layer pass; if ev is given, record events around each op."""
+    def step(self, ev=None, dynamic=False):
+        """One layer pass; if ev is given, record events around each op.  With
+        `dynamic`, the activation global scales come from this batch on the
+        device (amax of x before quantising it, amax of SiLU(g)*u before the
+        re-quantisation) instead of the warmup scalars."""
         from block_scaled_fp4_03_amd import ops
         import torch
         wl = self.wl
@@ -100,15 +103,17 @@ class Layer:
         rec = (lambda name: ev[name].append(torch.cuda.Event(enable_timing=True)) or ev[name][-1].record()) \
             if ev is not None else (lambda name: None)
         rec("start")
-        xc, xs, *xdq = ops.quantize(self.x, self.gs_x, dq=self.dq1)
+        gs_x = ops.global_scale(self.x.reshape(1, -1)) if dynamic else self.gs_x
+        xc, xs, *xdq = ops.quantize(self.x, gs_x, dq=self.dq1)
         rec("quantize")
         ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
         rec("route_permute")
-        gu = self.w1.gemm(xc, xs, self.gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
+        gu = self.w1.gemm(xc, xs, gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
         rec("gemm_l1")
-        hc, hs, *hdq = ops.silu_mul_requant(gu, self.gs_h, dq=self.dq2)
+        gs_h = ops.silu_mul_global_scale(gu) if dynamic else self.gs_h
+        hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=self.dq2)
         rec("silu_mul_requant")
-        y = self.w2.gemm(hc, hs, self.gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
+        y = self.w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
         rec("gemm_l2")
         out = ops.combine(y, inv, w)
         rec("combine")
@@ -121,10 +126,12 @@ class Layer:
         return int((np.diff(off) > 0).sum())
 
 
-def time_layer(layer, steps, warmup):
+def time_layer(layer, steps, warmup, dynamic=False):
+    """Mean ms per step over `steps` back-to-back steps (after `warmup`), the
+    mean per-op ms, and the p10/p50/p90 of the per-step times."""
     import torch
     for _ in range(warmup):
-        layer.step()
+        layer.step(dynamic=dynamic)
     torch.cuda.synchronize()
     names = ["start", "quantize", "route_permute", "gemm_l1", "silu_mul_requant", "gemm_l2", "combine"]
     ev = {n: [] for n in names}
@@ -133,7 +140,7 @@ def time_layer(layer, steps, warmup):
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(steps):
-        layer.step(ev)
+        layer.step(ev, dynamic=dynamic)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -141,7 +148,10 @@ def time_layer(layer, steps, warmup):
     for i in range(1, len(names)):
         a, b = names[i - 1], names[i]
         per_op[b] = float(np.mean([ev[a][s].elapsed_time(ev[b][s]) for s in range(steps)]))
-    return total_ms / steps, per_op
+    per_step = [ev["start"][s].elapsed_time(ev["combine"][s]) for s in range(steps)]
+    pct = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+           "p90": float(np.percentile(per_step, 90))}
+    return total_ms / steps, per_op, pct
 
 
 def algorithmic(wl, n_touched):
@@ -164,11 +174,15 @@ def run_gpu(workload, steps, warmup):
     layer = Layer(wl, dev)
     print("[bench] %s: weights ready in %.1fs, timing %d+%d steps" % (workload, layer.weight_setup_s, warmup, steps),
           file=sys.stderr, flush=True)
-    ms, per_op = time_layer(layer, steps, warmup)
+    ms, per_op, pct = time_layer(layer, steps, warmup)
     n_touched = layer.touched_experts()
     flops, l1_bytes, l1_flops = algorithmic(wl, n_touched)
-    res = dict(ms=ms, per_op_ms=per_op, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
+    res = dict(ms=ms, per_op_ms=per_op, step_pct=pct, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
                tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl)
+    # the same layer with per-batch activation global scales computed on the
+    # device (two extra amax passes), timed the same way
+    dms, dper_op, _ = time_layer(layer, steps, warmup, dynamic=True)
+    res["dynamic"] = dict(ms=dms, per_op_ms=dper_op, tokens_per_s=wl.T / (dms * 1e-3))
     return res
 
 
@@ -312,7 +326,10 @@ def main():
             "tokens": wl.T, "experts_touched": main_res["n_touched"],
             "weights": "NVFP4 (E2M1 codes, E4M3 scale per 16, FP32 global scale per projection)"},
         "tflops": round(main_res["tflops"], 2),
+        "ms_per_step_pct": {k: round(v, 4) for k, v in main_res["step_pct"].items()},
         "per_op_ms": {k: round(v, 4) for k, v in main_res["per_op_ms"].items()},
+        "dynamic_activation_scales": {"value": round(main_res["dynamic"]["tokens_per_s"], 1), "unit": "tokens/s",
+                                      "ms_per_step": round(main_res["dynamic"]["ms"], 4)},
         "roofline": roofline(main_res, bound),
     }
     if not args.no_cpu_baseline:
@@ -324,6 +341,10 @@ def main():
         pre = run_gpu("prefill", max(3, args.steps // 4), max(1, args.warmup // 2))
         line["prefill"] = {"value": round(pre["tokens_per_s"], 1), "unit": "tokens/s",
                            "ms_per_step": round(pre["ms"], 4), "tflops": round(pre["tflops"], 2),
+                           "ms_per_step_pct": {k: round(v, 4) for k, v in pre["step_pct"].items()},
+                           "dynamic_activation_scales": {"value": round(pre["dynamic"]["tokens_per_s"], 1),
+                                                         "unit": "tokens/s",
+                                                         "ms_per_step": round(pre["dynamic"]["ms"], 4)},
                            "experts_touched": pre["n_touched"],
                            "per_op_ms": {k: round(v, 4) for k, v in pre["per_op_ms"].items()},
                            "roofline": roofline(pre, "mfma")}

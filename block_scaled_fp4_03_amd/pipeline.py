@@ -104,21 +104,29 @@ def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False):
 
 def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
-    1-element f32 tensors.  Returns out [T, H] bf16 (and the stages)."""
+    1-element f32 tensors: static activation global scales (from a warmup
+    batch), or None for dynamic ones computed on the device from this batch
+    (gs_x = amax(x)/2688 before quantising x, gs_h = amax(SiLU(g)*u)/2688
+    between the two GEMMs; the host never waits for them).  Returns out
+    [T, H] bf16 (and the stages)."""
     T, H = x.shape
     R = T * k
+    if gs_x is None:
+        gs_x = ops.global_scale(x.reshape(1, -1))
     # the many-row GEMM tiles read A in exactly dequantised f16 form, which the
     # producers write alongside the codes when it will be read
     xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) else None)
     ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
     gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=sorted_ids, out_dtype=torch.float32,
                  a_dq=xdq[0] if xdq else None)
+    if gs_h is None:
+        gs_h = ops.silu_mul_global_scale(gu)
     hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=True if w2.reads_dq(R, R) else None)
     y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
     out = ops.combine(y, inv, w)
     if keep:
         return out, dict(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv,
-                         gate_up=gu, hc=hc, hs=hs, y=y)
+                         gate_up=gu, hc=hc, hs=hs, y=y, gs_x=gs_x, gs_h=gs_h)
     return out
 
 

@@ -77,8 +77,7 @@ def _expert_rows_check(wl, e, rows, tokens, xq, gs_x, gs_h, o1, o2, g_gu, g_hc, 
 
 # --- tiny: the whole layer, every stage -------------------------------------------
 
-def test_tiny_layer_end_to_end():
-    log("pipeline tiny")
+def _tiny_setup():
     wl = workloads.WORKLOADS["tiny"]
     d = dev()
     w1, w2 = pipeline.moe_weights(wl, d)
@@ -88,14 +87,13 @@ def test_tiny_layer_end_to_end():
         _check_weights(w2, e, ow[e][1])
     W1 = (np.stack([o[0][0] for o in ow]), np.stack([o[0][1] for o in ow]), np.stack([o[0][2] for o in ow]))
     W2 = (np.stack([o[1][0] for o in ow]), np.stack([o[1][1] for o in ow]), np.stack([o[1][2] for o in ow]))
-    warm = workloads.warmup_batch(wl)
-    gs_x = quant.global_scale(quant.amax(warm["x"].numpy()))
-    _, wst = moe.moe_layer(warm["x"].numpy(), warm["logits"].numpy(), wl.k, W1, W2, gs_x, F32(1), return_stages=True)
-    gs_h = quant.global_scale(quant.amax(wst["h"]))
-    b = workloads.batch(wl)
+    return wl, d, w1, w2, ow, W1, W2
+
+
+def _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g):
+    """Every stage of the GPU layer (out, stages g) against the oracle layer
+    run with the same activation global scales."""
     ref, st = moe.moe_layer(b["x"].numpy(), b["logits"].numpy(), wl.k, W1, W2, gs_x, gs_h, return_stages=True)
-    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
-                                torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d), keep=True)
     assert np.array_equal(to_np(g["xc"]), st["xq"][0]) and np.array_equal(to_np(g["xs"]), st["xq"][1])
     for k_ in ("ids", "offsets", "sorted_ids", "inv"):
         assert np.array_equal(to_np(g[k_]), st[k_]), k_
@@ -111,10 +109,42 @@ def test_tiny_layer_end_to_end():
     o = to_np(out)
     c = cosine(o, ref)
     rel = np.abs(o - ref).max() / np.sqrt(np.mean(ref.astype(np.float64) ** 2))
-    log("  tiny: cosine %.7f, max-abs/rms %.3g, audited flips %d" % (c, rel, flips))
     assert c >= 0.999
     if flips == 0:
         assert np.array_equal(o, ref) or rel <= 2e-2
+    return c, rel, flips
+
+
+def test_tiny_layer_end_to_end():
+    log("pipeline tiny")
+    wl, d, w1, w2, ow, W1, W2 = _tiny_setup()
+    warm = workloads.warmup_batch(wl)
+    gs_x = quant.global_scale(quant.amax(warm["x"].numpy()))
+    _, wst = moe.moe_layer(warm["x"].numpy(), warm["logits"].numpy(), wl.k, W1, W2, gs_x, F32(1), return_stages=True)
+    gs_h = quant.global_scale(quant.amax(wst["h"]))
+    b = workloads.batch(wl)
+    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
+                                torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d), keep=True)
+    c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g)
+    log("  tiny: cosine %.7f, max-abs/rms %.3g, audited flips %d" % (c, rel, flips))
+
+
+def test_tiny_layer_dynamic_activation_scales():
+    # gs_x and gs_h from this batch, on the device: gs_x must equal the
+    # oracle's amax(x)/2688 of the same bf16 x, and gs_h the oracle's
+    # amax(SiLU(g)*u)/2688 of the GPU's own L1 output (the stage's input);
+    # the layer is then checked stage by stage with those scales
+    log("pipeline tiny, dynamic activation scales")
+    wl, d, w1, w2, ow, W1, W2 = _tiny_setup()
+    b = workloads.batch(wl)
+    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2, None, None,
+                                keep=True)
+    gs_x = to_np(g["gs_x"])[0]
+    gs_h = to_np(g["gs_h"])[0]
+    assert gs_x == quant.global_scale(quant.amax(b["x"].numpy()))
+    assert gs_h == quant.global_scale(quant.amax(moe.silu_mul(to_np(g["gate_up"]))))
+    c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g)
+    log("  tiny dynamic: gs_x %.6g, gs_h %.6g, cosine %.7f, audited flips %d" % (gs_x, gs_h, c, flips))
 
 
 # --- shared expert: full size -----------------------------------------------------
