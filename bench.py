@@ -90,11 +90,12 @@ class Layer:
         self.dq2 = True if self.w2.reads_dq(R, R) else None
         torch.cuda.synchronize()
 
-    def step(self, ev=None, dynamic=False):
+    def step(self, ev=None, dynamic=False, fused=False):
         """One layer pass; if ev is given, record events around each op.  With
         `dynamic`, the activation global scales come from this batch on the
         device (amax of x before quantising it, amax of SiLU(g)*u before the
-        re-quantisation) instead of the warmup scalars."""
+        re-quantisation) instead of the warmup scalars; with `fused`, SiLU-requant
+        runs in the first GEMM's epilogue (static scales only)."""
         from block_scaled_fp4_03_amd import ops
         import torch
         wl = self.wl
@@ -108,11 +109,19 @@ class Layer:
         rec("quantize")
         ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
         rec("route_permute")
-        gu = self.w1.gemm(xc, xs, gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
-        rec("gemm_l1")
-        gs_h = ops.silu_mul_global_scale(gu) if dynamic else self.gs_h
-        hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=self.dq2)
-        rec("silu_mul_requant")
+        if not fused:
+            gu = self.w1.gemm(xc, xs, gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
+            rec("gemm_l1")
+            gs_h = ops.silu_mul_global_scale(gu) if dynamic else self.gs_h
+            hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=self.dq2)
+            rec("silu_mul_requant")
+        else:
+            # static gs_h: SiLU-requant runs in the first GEMM's epilogue
+            gs_h = self.gs_h
+            hc, hs, *hdq = self.w1.gemm_silu_requant(xc, xs, gs_x, off, R, gs_h, a_row_index=srt,
+                                                     a_dq=xdq[0] if xdq else None, dq=self.dq2)
+            rec("gemm_l1")
+            rec("silu_mul_requant")
         y = self.w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
         rec("gemm_l2")
         out = ops.combine(y, inv, w)
@@ -126,12 +135,12 @@ class Layer:
         return int((np.diff(off) > 0).sum())
 
 
-def time_layer(layer, steps, warmup, dynamic=False):
+def time_layer(layer, steps, warmup, dynamic=False, fused=False):
     """Mean ms per step over `steps` back-to-back steps (after `warmup`), the
     mean per-op ms, and the p10/p50/p90 of the per-step times."""
     import torch
     for _ in range(warmup):
-        layer.step(dynamic=dynamic)
+        layer.step(dynamic=dynamic, fused=fused)
     torch.cuda.synchronize()
     names = ["start", "quantize", "route_permute", "gemm_l1", "silu_mul_requant", "gemm_l2", "combine"]
     ev = {n: [] for n in names}
@@ -140,7 +149,7 @@ def time_layer(layer, steps, warmup, dynamic=False):
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(steps):
-        layer.step(ev, dynamic=dynamic)
+        layer.step(ev, dynamic=dynamic, fused=fused)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -154,13 +163,16 @@ def time_layer(layer, steps, warmup, dynamic=False):
     return total_ms / steps, per_op, pct
 
 
-def algorithmic(wl, n_touched):
-    """Algorithmic FLOPs of one layer and bytes of one L1 launch."""
+def algorithmic(wl, n_touched, fused):
+    """Algorithmic FLOPs of one layer and bytes of one L1 launch: the touched
+    experts' W1, x in NVFP4, and the launch's output (h in NVFP4 when
+    SiLU-requant runs in its epilogue, else gate_up in float32)."""
     T, H, I, k = wl.T, wl.H, wl.I, wl.k
     R = T * k
     flops = 6.0 * R * H * I
     w1_bytes = 2 * I * H * NVFP4_BYTES_PER_ELEM
-    l1_bytes = n_touched * w1_bytes + T * H * NVFP4_BYTES_PER_ELEM + R * 2 * I * 4
+    out_bytes = R * I * NVFP4_BYTES_PER_ELEM if fused else R * 2 * I * 4
+    l1_bytes = n_touched * w1_bytes + T * H * NVFP4_BYTES_PER_ELEM + out_bytes
     l1_flops = 4.0 * R * H * I
     return flops, l1_bytes, l1_flops
 
@@ -176,13 +188,18 @@ def run_gpu(workload, steps, warmup):
           file=sys.stderr, flush=True)
     ms, per_op, pct = time_layer(layer, steps, warmup)
     n_touched = layer.touched_experts()
-    flops, l1_bytes, l1_flops = algorithmic(wl, n_touched)
+    flops, l1_bytes, l1_flops = algorithmic(wl, n_touched, False)
     res = dict(ms=ms, per_op_ms=per_op, step_pct=pct, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
                tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl)
     # the same layer with per-batch activation global scales computed on the
     # device (two extra amax passes), timed the same way
     dms, dper_op, _ = time_layer(layer, steps, warmup, dynamic=True)
     res["dynamic"] = dict(ms=dms, per_op_ms=dper_op, tokens_per_s=wl.T / (dms * 1e-3))
+    # and with SiLU-requant in the first GEMM's epilogue (one launch fewer,
+    # no float32 gate_up in memory)
+    if layer.w1.can_fuse_silu():
+        fms, fper_op, _ = time_layer(layer, steps, warmup, fused=True)
+        res["fused"] = dict(ms=fms, l1_ms=fper_op["gemm_l1"], tokens_per_s=wl.T / (fms * 1e-3))
     return res
 
 
@@ -275,6 +292,14 @@ def cpu_baseline(res, n_experts=24):
                           os.cpu_count())}
 
 
+def fused_line(res):
+    f = res.get("fused")
+    if f is None:
+        return None
+    return {"value": round(f["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(f["ms"], 4),
+            "gemm_l1_ms": round(f["l1_ms"], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +355,7 @@ def main():
         "per_op_ms": {k: round(v, 4) for k, v in main_res["per_op_ms"].items()},
         "dynamic_activation_scales": {"value": round(main_res["dynamic"]["tokens_per_s"], 1), "unit": "tokens/s",
                                       "ms_per_step": round(main_res["dynamic"]["ms"], 4)},
+        "fused_silu_epilogue": fused_line(main_res),
         "roofline": roofline(main_res, bound),
     }
     if not args.no_cpu_baseline:
@@ -345,6 +371,7 @@ def main():
                            "dynamic_activation_scales": {"value": round(pre["dynamic"]["tokens_per_s"], 1),
                                                          "unit": "tokens/s",
                                                          "ms_per_step": round(pre["dynamic"]["ms"], 4)},
+                           "fused_silu_epilogue": fused_line(pre),
                            "experts_touched": pre["n_touched"],
                            "per_op_ms": {k: round(v, 4) for k, v in pre["per_op_ms"].items()},
                            "roofline": roofline(pre, "mfma")}

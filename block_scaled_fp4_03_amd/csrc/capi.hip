@@ -156,7 +156,7 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
       !aligned(out, 16) || !aligned(a_gs, 4) || !aligned(w_gs, 4) || !aligned(group_offsets, 4) ||
       !aligned(a_row_index, 4) || !aligned(a_dq, 16))
     return fail(NVFP4_EALIGN, "nvfp4_grouped_gemm: codes, a_dq and out must be 16-byte aligned, scales 4-byte");
-  nvfp4::GemmArgs a;
+  nvfp4::GemmArgs a{};
   a.a_codes = a_codes;
   a.a_scales = a_scales;
   a.a_gs = a_gs;
@@ -180,6 +180,58 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   a.ld_out = ld_out;
   hipStream_t s = (hipStream_t)stream;
   return finish("nvfp4_grouped_gemm", nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                        int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                                        const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets,
+                                        int32_t G, int64_t M, int64_t I, int64_t K, const float* h_gs,
+                                        uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* stream) {
+  const char* who = "nvfp4_grouped_gemm_silu_requant";
+  if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
+  if (M < 0 || I < 32 || I % 32 || K < 256 || K % 256)
+    return fail(NVFP4_ESHAPE, "%s: need M >= 0, I >= 32 with I %% 32 == 0, K >= 256 with K %% 256 == 0", who);
+  if (M >= ((int64_t)1 << 31) || 2 * I >= ((int64_t)1 << 31))
+    return fail(NVFP4_ESHAPE, "%s: M and 2 I must be below 2^31", who);
+  if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
+    return fail(NVFP4_ESHAPE, "%s: a_rows too small", who);
+  if (M == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_gs || !w_tiled || !w_gs || !group_offsets || !h_gs || !h_codes || !h_scales)
+    return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(a_codes, 16) || !aligned(w_tiled, 16) || !aligned(a_scales, 4) || !aligned(a_gs, 4) ||
+      !aligned(w_gs, 4) || !aligned(group_offsets, 4) || !aligned(a_row_index, 4) || !aligned(a_dq, 16) ||
+      !aligned(h_gs, 4) || !aligned(h_codes, 16) || !aligned(h_dq, 16))
+    return fail(NVFP4_EALIGN, "%s: codes, a_dq, h_codes and h_dq must be 16-byte aligned, scales 4-byte", who);
+  nvfp4::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.a_gs = a_gs;
+  a.a_rows = a_row_index ? a_rows : M;
+  a.a_row_index = a_row_index;
+  a.a_dq = a_dq && (uint64_t)a.a_rows * (uint64_t)K * 2u < ((uint64_t)1 << 32) ? a_dq : nullptr;
+  a.w_codes = w_tiled;
+  a.w_scales = nullptr;
+  a.w_tiled = 1;
+  a.w_gs = w_gs;
+  a.n_seg[0] = 0;
+  a.n_seg[1] = (int32_t)I;
+  for (int i = 2; i < 5; ++i) a.n_seg[i] = (int32_t)(2 * I);
+  a.n_segs = 2;
+  a.group_offsets = group_offsets;
+  a.G = G;
+  a.M = M;
+  a.N = 2 * I;
+  a.K = K;
+  a.out = nullptr;
+  a.out_bf16 = 0;
+  a.ld_out = 2 * I;
+  a.fuse = 1;
+  a.h_gs = h_gs;
+  a.h_codes = h_codes;
+  a.h_scales = h_scales;
+  a.h_dq = h_dq;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_grouped_gemm(a, s), s);
 }
 
 int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout) {

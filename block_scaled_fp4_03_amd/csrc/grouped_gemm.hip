@@ -483,19 +483,90 @@ __device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c)
 // Row of D held in accumulator element i by a lane of k half kh.
 __device__ __forceinline__ int acc32_row(int i, int kh) { return 8 * (i >> 2) + 4 * kh + (i & 3); }
 
+// Fused epilogue of the first GEMM: the wave holds gate column block j in
+// acc[rb][0] and up column block I/32 + j in acc[rb][1] (32x32 accumulator
+// layout: lane l = c + 32 kh has column c, rows 32 rb + acc32_row(i, kh)).
+// Each value is formed exactly as the unfused GEMM stores it (alpha times
+// the sum, float32), then h = SiLU(gate) * up and its NVFP4 re-quantisation
+// follow the operation sequence of silu_mul_requant, so codes, scales and
+// the f16 copy are identical to the unfused pair of launches.  A 16-element
+// block of h (one row, columns 16 q .. 16 q + 15) lies in the 16 lanes
+// c = 16 q .. 16 q + 15 of one half of the wave: its amax is a 4-step
+// exchange, and lanes c % 8 == 0 store 8 codes as one 32-bit word.
+// One 32-row block (gate accumulators gacc, up accumulators uacc) of the
+// fused epilogue.
+__device__ __forceinline__ void silu_requant_block(const GemmArgs& p, const floatx16_t& gacc, const floatx16_t& uacc,
+                                                   int64_t rbase, int64_t row1, int64_t I, int64_t hcol, int c,
+                                                   int kh, float alpha_g, float alpha_u, float gs) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t m = rbase + acc32_row(i, kh);
+    const float gv = alpha_g * gacc[i];
+    const float uv = alpha_u * uacc[i];
+    const float h = silu_mul(gv, uv);
+    float bmax = __builtin_fabsf(h);
+    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 1, 64));
+    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 2, 64));
+    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 4, 64));
+    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 8, 64));
+    float r;
+    bool zero;
+    const uint32_t sq = block_scale(bmax, gs, r, zero);
+    const uint32_t code = e2m1_code(h, r, zero);
+    uint32_t word = code << (4 * (c & 7));
+    word |= __shfl_xor(word, 1, 64);
+    word |= __shfl_xor(word, 2, 64);
+    word |= __shfl_xor(word, 4, 64);
+    if (m < row1) {
+      if ((c & 7) == 0) *(uint32_t*)(p.h_codes + m * (I / 2) + hcol / 2) = word;
+      if ((c & 15) == 0) p.h_scales[m * (I / 16) + hcol / 16] = (uint8_t)sq;
+      if (p.h_dq) p.h_dq[m * I + hcol] = dq_f16(code, e4m3_decode(sq));
+    }
+  }
+}
+
+// The row blocks rb = RB0 .. RB - 1, by compile-time recursion so that every
+// accumulator index is a constant (a loop the compiler did not unroll would
+// index the accumulators at run time and move them to scratch memory).
+template <int RB, int RB0>
+__device__ __forceinline__ void silu_requant_rows(const GemmArgs& p, const floatx16_t (&acc)[RB][2], int64_t row0,
+                                                  int64_t row1, int64_t I, int64_t hcol, int c, int kh,
+                                                  float alpha_g, float alpha_u, float gs) {
+  if constexpr (RB0 < RB) {
+    silu_requant_block(p, acc[RB0][0], acc[RB0][1], row0 + 32 * RB0, row1, I, hcol, c, kh, alpha_g, alpha_u, gs);
+    silu_requant_rows<RB, RB0 + 1>(p, acc, row0, row1, I, hcol, c, kh, alpha_g, alpha_u, gs);
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const floatx16_t (&acc)[RB][2], int g,
+                                                      int64_t row0, int64_t row1, int64_t j, int lane) {
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t I = p.N / 2;
+  if (32 * j >= I) return;  // uniform in the wave
+  const float a_gs = *p.a_gs;
+  const float alpha_g = a_gs * p.w_gs[(int64_t)g * 2];
+  const float alpha_u = a_gs * p.w_gs[(int64_t)g * 2 + 1];
+  silu_requant_rows<RB, 0>(p, acc, row0, row1, I, 32 * j + c, c, kh, alpha_g, alpha_u, *p.h_gs);
+}
+
 // gemm_stream32: 32*RB rows x (4 waves x NBW x 32) columns per workgroup; each
 // wave streams its NBW 32-column blocks of W over the whole K, one half-step
 // prefetched ahead, with no shared memory and no barriers.  With skip_bm > 0
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
-template <int NBW, int RB>
+template <int NBW, int RB, bool FUSE>
 __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
                                               int wave, int lane) {
+  static_assert(!FUSE || NBW == 2, "the fused epilogue pairs one gate and one up column block");
   constexpr int BN = 4 * NBW * 32;
   const int c = lane & 31;
   const int kh = lane >> 5;
   const int64_t n0 = nt * BN + wave * NBW * 32;
-  if (n0 >= p.N) return;
+  // fused: the wave's h column block j, from gate block j and up block I/32 + j
+  const int64_t j = nt * 4 + wave;
+  if (FUSE ? 64 * j >= p.N : n0 >= p.N) return;
   const int64_t K = p.K;
   const int64_t nks = K / 256;
   const int64_t KB = K / 2, KS = K / 16;
@@ -516,7 +587,7 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   const uint8_t* w_t[NBW];
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
-    int64_t nb = n0 / 32 + cb;
+    int64_t nb = FUSE ? j + cb * (p.N / 64) : n0 / 32 + cb;
     nb = nb < nb_per_g ? nb : nb_per_g - 1;
     w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
   }
@@ -588,6 +659,10 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     }
   }
 
+  if constexpr (FUSE) {
+    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
+    return;
+  }
   const float a_gs = *p.a_gs;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
@@ -606,7 +681,7 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
 
 // One tile per workgroup, slot-major (the grid is an upper bound; workgroups
 // without a tile exit after one pass over the group offsets).
-template <int NBW, int RB, bool BATCHED>
+template <int NBW, int RB, bool BATCHED, bool FUSE>
 __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm, int skip_min) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -619,7 +694,7 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
               : find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1);
   if (!found) return;
   g = __builtin_amdgcn_readfirstlane(g);
-  stream32_tile<NBW, RB>(p, g, row0, row1, nt, wave, lane);
+  stream32_tile<NBW, RB, FUSE>(p, g, row0, row1, nt, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,7 +958,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t
 //    (The compiler waits for all outstanding vector memory operations once
 //    copies into local memory and register loads are both in flight, so no
 //    load is issued after substep 0 that substeps 1-6 would wait for.)
-template <int RB>
+template <int RB, bool FUSE>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
                                             int64_t n0, int wave, int lane) {
   constexpr int CB = 2;            // 64 columns per wave
@@ -920,10 +995,12 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   };
 
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
+  // fused: the wave's h column block j, from gate block j and up block I/32 + j
+  const int64_t j = n0 / 64 + wave;
   const uint8_t* w_t[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    int64_t nb = n0 / 32 + wave * CB + cb;
+    int64_t nb = FUSE ? j + cb * (p.N / 64) : n0 / 32 + wave * CB + cb;
     nb = nb < nb_per_g ? nb : nb_per_g - 1;
     w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
   }
@@ -1017,6 +1094,10 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     __syncthreads();
   }
 
+  if constexpr (FUSE) {
+    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
+    return;
+  }
   const float a_gs = *p.a_gs;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -1033,6 +1114,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   }
 }
 
+template <bool FUSE>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
   const int lane = threadIdx.x & 63;
@@ -1048,54 +1130,61 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
   const int64_t n0 = nt * BIG;
   const int64_t rows = row1 - row0;
   if constexpr (kBigMinLast > 128) {
-    big_dq_tile<8>(p, lds, g, row0, row1, n0, wave, lane);
+    big_dq_tile<8, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
   } else {
     if (rows > 128)
-      big_dq_tile<8>(p, lds, g, row0, row1, n0, wave, lane);
+      big_dq_tile<8, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
     else if (rows > 64 || kBigMinLast > 64)
-      big_dq_tile<4>(p, lds, g, row0, row1, n0, wave, lane);
+      big_dq_tile<4, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
     else if (rows > 32 || kBigMinLast > 32)
-      big_dq_tile<2>(p, lds, g, row0, row1, n0, wave, lane);
+      big_dq_tile<2, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
     else
-      big_dq_tile<1>(p, lds, g, row0, row1, n0, wave, lane);
+      big_dq_tile<1, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
   }
 }
 
 // ---------------------------------------------------------------------------
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled) { return tiled && M >= BIG && M >= 64 * G; }
 
-hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
-  if (a.M == 0) return hipSuccess;
-  if (a.w_tiled) {
-    if (gemm_uses_big_tiles(a.G, a.M, true)) {
-      // many rows per group: 256-row tiles on the matrix-core kernel (with A
-      // in f16 form also a group's last tile if it has kBigMinLast rows or
-      // more), the rows left over at the end of each group on the streaming
-      // kernel.  Tile counts are upper bounds (the group sizes are on the
-      // device); workgroups without a tile exit.
-      const bool dq = a.a_dq != nullptr;
-      const int skip_min = dq ? kBigMinLast : BIG;
-      constexpr int NBW = 2, RB = 1;
-      const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-      const int64_t work_s = ((a.M + 32 * RB - 1) / (32 * RB) + a.G) * n_tiles_s;
-      hipLaunchKernelGGL((gemm_stream32<NBW, RB, true>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s, BIG,
-                         skip_min);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-      const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
-      if (dq)
-        hipLaunchKernelGGL(gemm_big32_dq, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
-      else
-        hipLaunchKernelGGL(gemm_big32, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
-      return hipGetLastError();
-    }
-    constexpr int NBW = 2;
-    const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-    const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
-    hipLaunchKernelGGL((gemm_stream32<NBW, 1, false>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0);
+template <bool FUSE>
+hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+  // a workgroup covers 256 weight rows: 256 output columns, or (fused) 128
+  // columns of h from 128 gate and 128 up rows
+  if (gemm_uses_big_tiles(a.G, a.M, true) && (a.a_dq || !FUSE)) {
+    // many rows per group: 256-row tiles on the matrix-core kernel (with A
+    // in f16 form also a group's last tile if it has kBigMinLast rows or
+    // more), the rows left over at the end of each group on the streaming
+    // kernel.  Tile counts are upper bounds (the group sizes are on the
+    // device); workgroups without a tile exit.
+    const bool dq = a.a_dq != nullptr;
+    const int skip_min = dq ? kBigMinLast : BIG;
+    constexpr int NBW = 2, RB = 1;
+    const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+    const int64_t work_s = ((a.M + 32 * RB - 1) / (32 * RB) + a.G) * n_tiles_s;
+    hipLaunchKernelGGL((gemm_stream32<NBW, RB, true, FUSE>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s,
+                       BIG, skip_min);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n_tiles = (a.N + BIG - 1) / BIG;
+    const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
+    if (dq)
+      hipLaunchKernelGGL(gemm_big32_dq<FUSE>, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a,
+                         n_tiles);
+    else if constexpr (!FUSE)
+      hipLaunchKernelGGL(gemm_big32, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
     return hipGetLastError();
   }
+  constexpr int NBW = 2;
+  const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+  const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
+  hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  if (a.w_tiled) return a.fuse ? launch_tiled<true>(a, s) : launch_tiled<false>(a, s);
+  if (a.fuse) return hipErrorInvalidValue;  // the fused epilogue runs on the tiled kernels only
   if (a.M >= (int64_t)64 * a.G && a.K % TBK == 0) {
     const int64_t n_tiles = (a.N + TBN - 1) / TBN;
     const int64_t slots = (a.M + TBM - 1) / TBM + a.G;

@@ -77,6 +77,14 @@ struct GemmArgs {
   void* out;
   int32_t out_bf16;
   int64_t ld_out;
+  // fused SiLU-requant epilogue (fuse = 1, tiled weights): N = 2 I with the
+  // gate in columns [0, I) and the up projection in [I, 2 I); instead of
+  // `out`, h = SiLU(gate) * up is written re-quantised with h_gs
+  int32_t fuse;
+  const float* h_gs;
+  uint8_t* h_codes;    // [M, I/2]
+  uint8_t* h_scales;   // [M, I/16]
+  uint16_t* h_dq;      // nullable: [M, I] f16, e2m1 * e4m3 of h
 };
 // true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);

@@ -56,23 +56,41 @@ __device__ __forceinline__ float e4m3_decode(uint32_t code) {
 
 // Quantise one 16-element block.  x: 16 finite floats.  Returns the scale code
 // and writes the 16 packed codes (element 2i in the low nibble) as two words.
+// Scale code of a block whose largest magnitude is bamax, with the
+// reciprocal r that maps its elements onto the E2M1 grid; `zero` when the
+// scale decodes to 0 (then every code of the block is 0x0).  Each step is
+// one IEEE float32 operation, in this order.
+__device__ __forceinline__ uint32_t block_scale(float bamax, float gs, float& r, bool& zero) {
+  const float d = 6.0f * gs;
+  const float s = bamax / d;
+  const uint32_t sq = e4m3_encode(s);
+  const float sf = e4m3_decode(sq);
+  zero = sf == 0.0f;
+  r = zero ? 0.0f : 1.0f / (sf * gs);
+  return sq;
+}
+
+// E2M1 code of x in a block with reciprocal r: the sign bit of x plus the
+// magnitude nearest to |x * r|.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float r, bool zero) {
+  if (zero) return 0u;
+  const float v = x * r;
+  return e2m1_index(__builtin_fabsf(v)) | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 __device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float gs,
                                                      uint32_t& lo, uint32_t& hi) {
   float bamax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) bamax = __builtin_fmaxf(bamax, __builtin_fabsf(x[i]));
-  const float d = 6.0f * gs;
-  const float s = bamax / d;
-  const uint32_t sq = e4m3_encode(s);
-  const float sf = e4m3_decode(sq);
+  float r;
+  bool zero;
+  const uint32_t sq = block_scale(bamax, gs, r, zero);
   lo = 0u;
   hi = 0u;
-  if (sf == 0.0f) return 0u;
-  const float r = 1.0f / (sf * gs);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float v = x[i] * r;
-    const uint32_t c = e2m1_index(__builtin_fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+    const uint32_t c = e2m1_code(x[i], r, zero);
     if (i < 8) lo |= c << (4 * i);
     else hi |= c << (4 * (i - 8));
   }
@@ -105,6 +123,14 @@ __device__ __forceinline__ float exp_f32(float x) {
   p = p * r + 1.0f;                                    // 1/1!
   p = p * r + 1.0f;                                    // 1/0!
   return __builtin_ldexpf(p, (int)n);
+}
+
+// SiLU(g) * u with exp_f32, one IEEE op per step.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = exp_f32(-g);
+  const float den = 1.0f + e;
+  const float s = g / den;
+  return s * u;
 }
 
 // ---------------------------------------------------------------------------
@@ -196,6 +222,17 @@ __device__ __forceinline__ void store_dq16(void* dst, uint32_t lo, uint32_t hi, 
   }
   ((u32x4v*)dst)[0] = a;
   ((u32x4v*)dst)[1] = b;
+}
+
+// Value of an E2M1 code times a decoded block scale, as f16 (exact: at most
+// five significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ uint16_t dq_f16(uint32_t code, float sf) {
+  // magnitude index i: 0 -> 0, 1 -> 0.5, i >= 2 -> 2^(i/2 - 1) * (1 + (i & 1) / 2)
+  const uint32_t i = code & 7u;
+  const float m = i >= 2u ? __uint_as_float(((126u + (i >> 1)) << 23) | ((i & 1u) << 22)) : (i == 1u ? 0.5f : 0.0f);
+  float v = m * sf;
+  v = (code & 8u) ? -v : v;
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
 }  // namespace nvfp4

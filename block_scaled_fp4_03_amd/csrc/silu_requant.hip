@@ -5,14 +5,6 @@
 
 namespace nvfp4 {
 
-// SiLU(g) * u with the library's exponential, one IEEE op per step.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = exp_f32(-g);
-  const float den = 1.0f + e;
-  const float s = g / den;
-  return s * u;
-}
-
 // One thread per 16-element block of h (16 gate + 16 up inputs).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void silu_requant_kernel(const void* __restrict__ gu, int64_t M,

@@ -25,6 +25,8 @@ SIGNATURES = {
     "moe_route_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,
                                   _P, _I32, _I64, _I64, _I64, _P, _I32, _I64, _P]),
+    "nvfp4_grouped_gemm_silu_requant": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
+                                               _P, _P, _P, _P, _P]),
     "nvfp4_grouped_gemm_reads_dq": (_I32, [_I32, _I64, _I64, _I64, _I32]),
     "nvfp4_prepared_weight_bytes": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_prepare_weights": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),

@@ -147,6 +147,29 @@ def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_
     return out
 
 
+def grouped_gemm_silu_requant(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, M, I, K, gs_h,
+                              a_row_index=None, a_dq=None, dq=None, codes=None, scales=None):
+    """First GEMM of the expert MLP with SiLU(gate)*up re-quantised in its
+    epilogue: the same codes and scales (and f16 copy with dq) as
+    silu_mul_requant over grouped_gemm's float32 [M, 2I] output, without
+    that output.  w_tiled: prepare_weights buffer of the stacked [G, 2I, K]
+    weights; w_gs [G, 2]."""
+    _check_dev(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, gs_h, a_row_index, a_dq,
+               None if dq is True else dq)
+    G = w_gs.shape[0]
+    dev = a_codes.device
+    if codes is None:
+        codes = torch.empty(M, I // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(M, I // 16, dtype=torch.uint8, device=dev)
+    want_dq = dq is not None
+    dq = _dq_out(dq, M, I, dev)
+    _lib.call("nvfp4_grouped_gemm_silu_requant", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
+              _p(a_row_index), _p(a_dq), _p(w_tiled), _p(w_gs), _p(group_offsets), G, M, I, K, _p(gs_h),
+              _p(codes), _p(scales), _p(dq), _stream())
+    return (codes, scales, dq) if want_dq else (codes, scales)
+
+
 def silu_mul_requant(gate_up, gs_h, codes=None, scales=None, dq=None):
     """gate_up [M, 2I] f32/bf16 -> NVFP4 h (codes [M, I/2], scales [M, I/16]);
     dq as in quantize."""

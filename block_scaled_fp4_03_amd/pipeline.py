@@ -55,6 +55,18 @@ class NVFP4Weights:
         return ops.grouped_gemm(a_codes, a_scales, a_gs, self.codes, self.scales, self.gs, self.n_seg,
                                 group_offsets, M, w_tiled=self.tiled, **kw)
 
+    def can_fuse_silu(self):
+        """Whether this stacked gate_up stack runs the GEMM with the SiLU
+        re-quantisation in its epilogue (tiled layout, I % 32 == 0)."""
+        G, N, K2 = self.codes.shape
+        return self.tiled is not None and len(self.n_seg) == 3 and N == 2 * self.n_seg[1] and \
+            self.n_seg[1] % 32 == 0 and (2 * K2) % 256 == 0
+
+    def gemm_silu_requant(self, a_codes, a_scales, a_gs, group_offsets, M, gs_h, **kw):
+        G, N, K2 = self.codes.shape
+        return ops.grouped_gemm_silu_requant(a_codes, a_scales, a_gs, self.tiled, self.gs, group_offsets, M,
+                                             N // 2, 2 * K2, gs_h, **kw)
+
 
 def quantize_stack(mats, n_seg, device):
     """Quantise float32 matrices (each [N, K], one global scale per column
@@ -102,13 +114,42 @@ def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False):
     return w1, w2
 
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
+def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xdq=None, fused=None):
+    """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` (static
+    gs_h and a fusable W1) the re-quantisation runs in the L1 epilogue, with
+    identical results and no float32 gate_up in memory; by default it runs as
+    its own kernel, which measures faster on MI355X (the epilogue's vector
+    work stalls the matrix cores of the 256-row tiles).  gs_h None computes
+    it from this batch's gate_up.  Returns (y bf16, stages)."""
+    if fused is None:
+        fused = False
+    if fused and (gs_h is None or not w1.can_fuse_silu()):
+        raise ValueError("the fused epilogue needs a static gs_h and tiled W1 with I % 32 == 0")
+    dq2 = True if w2.reads_dq(R, R) else None
+    st = {}
+    if fused:
+        hc, hs, *hdq = w1.gemm_silu_requant(xc, xs, gs_x, off, R, gs_h, a_row_index=a_row_index, a_dq=xdq,
+                                            dq=dq2)
+    else:
+        gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=a_row_index, out_dtype=torch.float32, a_dq=xdq)
+        if gs_h is None:
+            gs_h = ops.silu_mul_global_scale(gu)
+        hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=dq2)
+        st["gate_up"] = gu
+    y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
+    st.update(hc=hc, hs=hs, y=y, gs_h=gs_h)
+    return y, st
+
+
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
     1-element f32 tensors: static activation global scales (from a warmup
     batch), or None for dynamic ones computed on the device from this batch
     (gs_x = amax(x)/2688 before quantising x, gs_h = amax(SiLU(g)*u)/2688
-    between the two GEMMs; the host never waits for them).  Returns out
-    [T, H] bf16 (and the stages)."""
+    between the two GEMMs; the host never waits for them).  `fused` runs
+    SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant);
+    the results are identical either way.  Returns out [T, H] bf16 (and the
+    stages)."""
     T, H = x.shape
     R = T * k
     if gs_x is None:
@@ -117,29 +158,24 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False):
     # producers write alongside the codes when it will be read
     xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) else None)
     ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
-    gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=sorted_ids, out_dtype=torch.float32,
-                 a_dq=xdq[0] if xdq else None)
-    if gs_h is None:
-        gs_h = ops.silu_mul_global_scale(gu)
-    hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=True if w2.reads_dq(R, R) else None)
-    y = w2.gemm(hc, hs, gs_h, off, R, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
+    y, st = _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, T, a_row_index=sorted_ids,
+                        xdq=xdq[0] if xdq else None, fused=fused)
     out = ops.combine(y, inv, w)
     if keep:
-        return out, dict(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv,
-                         gate_up=gu, hc=hc, hs=hs, y=y, gs_x=gs_x, gs_h=gs_h)
+        st.update(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv, gs_x=gs_x)
+        return out, st
     return out
 
 
-def shared_expert(x, w1, w2, gs_x, gs_h, keep=False):
+def shared_expert(x, w1, w2, gs_x, gs_h, keep=False, fused=None):
     """Shared expert: one group, no routing.  Returns y [T, H] bf16."""
     T = x.shape[0]
     off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
     xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(T, T) else None)
-    gu = w1.gemm(xc, xs, gs_x, off, T, a_dq=xdq[0] if xdq else None)
-    hc, hs, *hdq = ops.silu_mul_requant(gu, gs_h, dq=True if w2.reads_dq(T, T) else None)
-    y = w2.gemm(hc, hs, gs_h, off, T, out_dtype=torch.bfloat16, a_dq=hdq[0] if hdq else None)
+    y, st = _expert_mlp(xc, xs, gs_x, off, T, w1, w2, gs_h, T, xdq=xdq[0] if xdq else None, fused=fused)
     if keep:
-        return y, dict(xc=xc, xs=xs, gate_up=gu, hc=hc, hs=hs)
+        st.update(xc=xc, xs=xs)
+        return y, st
     return y
 
 

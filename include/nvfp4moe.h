@@ -213,6 +213,38 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            void* out, int32_t out_dtype, int64_t ld_out, void* stream);
 
 /*
+ * nvfp4_grouped_gemm_silu_requant - the first grouped GEMM of the expert MLP
+ * with SiLU(gate) * up and its NVFP4 re-quantisation in the epilogue: the
+ * stacked gate_up projection (page e8b289e, "Phase 1": grouped GEMM, SiLU,
+ * re-quant) without the float32 [M, 2I] intermediate.
+ *   Equivalent to nvfp4_grouped_gemm(a_*, w_tiled, NVFP4_LAYOUT_TILED, w_gs,
+ *   n_seg = {0, I, 2I}, group_offsets, G, M, N = 2I, K, out f32 [M, 2I])
+ *   followed by silu_mul_requant(out, F32, M, I, 2I, h_gs, h_codes,
+ *   h_scales, h_dq): every value of gate and up is formed as that GEMM
+ *   writes it and goes through the same float32 steps, so codes, scales
+ *   and h_dq are identical to the pair of calls.
+ *   a_codes ... a_dq   as for nvfp4_grouped_gemm.
+ *   w_tiled            the nvfp4_prepare_weights buffer of the stacked
+ *                      [G, 2I, K] weights (gate rows [0, I), up rows
+ *                      [I, 2I)); w_gs [G, 2] (gate, up).
+ *   h_gs               ONE float32, the global scale of h.
+ *   h_codes, h_scales  out [M, I/2], [M, I/16]; h_dq out [M, I] f16 or NULL
+ *                      (as silu_mul_requant writes them).  Rows outside every
+ *                      group are left untouched.
+ * Errors: EINVAL for null pointers; ESHAPE unless 1 <= G <=
+ * NVFP4_MAX_EXPERTS, M >= 0, I >= 32 with I % 32 == 0, K >= 256 with
+ * K % 256 == 0, a_rows as for nvfp4_grouped_gemm; EALIGN unless codes,
+ * w_tiled, a_dq, h_codes and h_dq are 16-byte aligned and scales and global
+ * scales 4-byte aligned.
+ */
+int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                        int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                                        const uint8_t* w_tiled, const float* w_gs,
+                                        const int32_t* group_offsets, int32_t G, int64_t M, int64_t I,
+                                        int64_t K, const float* h_gs, uint8_t* h_codes, uint8_t* h_scales,
+                                        uint16_t* h_dq, void* stream);
+
+/*
  * nvfp4_grouped_gemm_reads_dq - 1 if nvfp4_grouped_gemm with these sizes
  * (G groups, M rows, depth K, a_rows stored A rows) and weight layout reads
  * a_dq when it is given (its 256-row tiles do), else 0.  Lets a caller

@@ -104,6 +104,26 @@ def test_gemm_validation(L):
     assert _gemm(L, w_layout=lib.LAYOUT_ROWS, w_scales=NULL) == lib.EINVAL
 
 
+def test_fused_gemm_silu_validation(L):
+    f = L.nvfp4_grouped_gemm_silu_requant
+
+    def call(**kw):
+        a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, a_dq=NULL, w=FAKE,
+                 w_gs=FAKE, off=FAKE, G=1, M=8, I=64, K=256, h_gs=FAKE, hc=FAKE, hs=FAKE, hdq=NULL)
+        a.update(kw)
+        return f(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"], a["a_dq"], a["w"],
+                 a["w_gs"], a["off"], a["G"], a["M"], a["I"], a["K"], a["h_gs"], a["hc"], a["hs"], a["hdq"], NULL)
+    assert call(I=48) == lib.ESHAPE            # I % 32
+    assert call(K=384) == lib.ESHAPE           # K % 256
+    assert call(G=0) == lib.ESHAPE
+    assert call(a_rows=4) == lib.ESHAPE
+    assert call(h_gs=NULL) == lib.EINVAL
+    assert call(w=NULL) == lib.EINVAL
+    assert call(hc=ctypes.c_void_p(0x1004)) == lib.EALIGN
+    assert call(hdq=ctypes.c_void_p(0x1008)) == lib.EALIGN
+    assert call(M=0, a_codes=NULL, hc=NULL) == lib.OK
+
+
 def test_reads_dq_query(L):
     q = L.nvfp4_grouped_gemm_reads_dq
     assert q(1, 8192, 7168, 8192, lib.LAYOUT_TILED) == 1

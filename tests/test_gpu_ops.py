@@ -280,6 +280,67 @@ def test_gemm_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+# --- fused first GEMM + SiLU-requant ----------------------------------------------
+
+def _fused_case(counts, I, K, seed, gather=True, use_dq=False):
+    """nvfp4_grouped_gemm_silu_requant against the unfused pair (grouped
+    GEMM to float32, then silu_mul_requant): codes, scales and the f16 copy
+    must be identical."""
+    log("fused gemm+silu", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq)
+    rng = np.random.default_rng(seed)
+    G, M = len(counts), int(sum(counts))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a_rows = M + 5 if gather else M
+    ac, as_, ags = oracle_nvfp4(_x(a_rows, K, seed, outliers=True))
+    row_index = rng.integers(0, a_rows, M).astype(np.int32) if gather else None
+    N = 2 * I
+    wc = np.empty((G, N, K // 2), np.uint8)
+    ws = np.empty((G, N, K // 16), np.uint8)
+    wgs = np.empty((G, 2), np.float32)
+    for g in range(G):
+        wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        for sg in range(2):
+            c, sc, gg = oracle_nvfp4(wf[sg * I:(sg + 1) * I])
+            wc[g, sg * I:(sg + 1) * I], ws[g, sg * I:(sg + 1) * I], wgs[g, sg] = c, sc, gg
+    d = dev()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    tiled = ops.prepare_weights(T(wc), T(ws))
+    a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16)) if use_dq else None
+    ri = T(row_index) if gather else None
+    args = (T(ac), T(as_), torch.tensor([ags], device=d))
+    gu = ops.grouped_gemm(*args, T(wc), T(ws), T(wgs), [0, I, N], T(off), M, a_row_index=ri, w_tiled=tiled,
+                          a_dq=a_dq)
+    gs_h = ops.silu_mul_global_scale(gu)
+    hc, hs, hdq = ops.silu_mul_requant(gu, gs_h, dq=True)
+    fc, fs, fdq = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
+                                                a_dq=a_dq, dq=True)
+    assert np.array_equal(to_np(fc), to_np(hc)), "codes"
+    assert np.array_equal(to_np(fs), to_np(hs)), "scales"
+    assert np.array_equal(to_np(fdq).view(np.uint16), to_np(hdq).view(np.uint16)), "f16 copy"
+    fc2, fs2 = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
+                                             a_dq=a_dq)
+    assert np.array_equal(to_np(fc2), to_np(hc)) and np.array_equal(to_np(fs2), to_np(hs))
+
+
+def test_fused_silu_requant_decode_shaped():
+    rng = np.random.default_rng(21)
+    counts = rng.integers(0, 12, 40).tolist()
+    counts[5] = 0
+    _fused_case(counts, 160, 512, 21)
+
+
+def test_fused_silu_requant_big_tiles():
+    # 256-row tiles, last tiles of every size class, with and without A's f16 form
+    counts = [456, 3, 256, 0, 611, 70, 385]
+    _fused_case(counts, 256, 512, 22, use_dq=True)
+    _fused_case(counts, 256, 512, 23, use_dq=False)
+
+
+def test_fused_silu_requant_one_group_no_gather():
+    _fused_case([300], 96, 768, 24, gather=False, use_dq=True)
+    _fused_case([17], 128, 256, 25, gather=False)
+
+
 # --- SiLU-requant and combine ---------------------------------------------------
 
 @pytest.mark.parametrize("M,I,dtype", [(1, 16, "f32"), (37, 128, "f32"), (200, 3072, "f32"), (64, 512, "bf16")])

@@ -77,6 +77,20 @@ def _expert_rows_check(wl, e, rows, tokens, xq, gs_x, gs_h, o1, o2, g_gu, g_hc, 
 
 # --- tiny: the whole layer, every stage -------------------------------------------
 
+def _fused_same(unfused, fused):
+    """The layer with SiLU-requant in the first GEMM's epilogue must give the
+    unfused layer's intermediate and output bit for bit."""
+    (o0, g0), (o1, g1) = unfused, fused
+    assert "gate_up" not in g1 and "gate_up" in g0    # the two paths really differ
+    assert g1["hc"].data_ptr() != g0["hc"].data_ptr()
+    for k_ in ("hc", "hs"):
+        assert np.array_equal(to_np(g0[k_]), to_np(g1[k_])), k_
+    assert np.array_equal(to_np(o0).view(np.uint32) if o0.dtype == torch.float32 else
+                          o0.view(torch.int16).cpu().numpy(),
+                          to_np(o1).view(np.uint32) if o1.dtype == torch.float32 else
+                          o1.view(torch.int16).cpu().numpy())
+
+
 def _tiny_setup():
     wl = workloads.WORKLOADS["tiny"]
     d = dev()
@@ -123,10 +137,13 @@ def test_tiny_layer_end_to_end():
     _, wst = moe.moe_layer(warm["x"].numpy(), warm["logits"].numpy(), wl.k, W1, W2, gs_x, F32(1), return_stages=True)
     gs_h = quant.global_scale(quant.amax(wst["h"]))
     b = workloads.batch(wl)
-    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
-                                torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d), keep=True)
+    run = lambda fused: pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
+                                           torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
+                                           keep=True, fused=fused)
+    out, g = run(False)
     c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g)
-    log("  tiny: cosine %.7f, max-abs/rms %.3g, audited flips %d" % (c, rel, flips))
+    _fused_same((out, g), run(True))
+    log("  tiny: cosine %.7f, max-abs/rms %.3g, audited flips %d; fused epilogue identical" % (c, rel, flips))
 
 
 def test_tiny_layer_dynamic_activation_scales():
@@ -165,8 +182,10 @@ def test_shared_expert_full_size():
     _, wst = moe.shared_expert(warm["x"].numpy(), W1, W2, gs_x, F32(1), return_stages=True)
     gs_h = quant.global_scale(quant.amax(wst["h"]))
     ref, st = moe.shared_expert(b["x"].numpy(), W1, W2, gs_x, gs_h, return_stages=True)
-    y, g = pipeline.shared_expert(b["x"].to(d, torch.bfloat16), w1, w2, torch.tensor([gs_x], device=d),
-                                  torch.tensor([gs_h], device=d), keep=True)
+    run = lambda fused: pipeline.shared_expert(b["x"].to(d, torch.bfloat16), w1, w2, torch.tensor([gs_x], device=d),
+                                               torch.tensor([gs_h], device=d), keep=True, fused=fused)
+    y, g = run(False)
+    _fused_same((y, g), run(True))
     assert np.array_equal(to_np(g["xc"]), st["xq"][0]) and np.array_equal(to_np(g["xs"]), st["xq"][1])
     rows = np.arange(wl.T)
     flips = _expert_rows_check(wl, 0, rows, rows, st["xq"], gs_x, gs_h, o1, o2, to_np(g["gate_up"]),
@@ -246,8 +265,11 @@ def _routed_full(name, max_rows_per_expert):
         gu = (ex * _l1_alpha(gs_x, ow[e][0][2], wl.I)[None, :]).astype(np.float32)
         hs_all.append(moe.silu_mul(gu))
     gs_h = quant.global_scale(max(quant.amax(h) for h in hs_all))
-    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
-                                torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d), keep=True)
+    run = lambda fused: pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
+                                           torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
+                                           keep=True, fused=fused)
+    out, g = run(False)
+    _fused_same((out, g), run(True))
     torch.cuda.synchronize()
     assert np.array_equal(to_np(g["xc"]), xq[0]) and np.array_equal(to_np(g["xs"]), xq[1])
     assert np.array_equal(to_np(g["ids"]), ids)
