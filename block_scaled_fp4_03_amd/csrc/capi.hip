@@ -127,7 +127,8 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            const uint8_t* w_codes,
                            const uint8_t* w_scales, int32_t w_layout, const float* w_gs, const int32_t* n_seg,
                            int32_t n_segs, const int32_t* group_offsets, int32_t G, int64_t M, int64_t N,
-                           int64_t K, void* out, int32_t out_dtype, int64_t ld_out, void* stream) {
+                           int64_t K, void* out, int32_t out_dtype, int64_t ld_out, void* workspace,
+                           size_t ws_bytes, void* stream) {
   if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
     return fail(NVFP4_EINVAL, "nvfp4_grouped_gemm: unknown out dtype %d", out_dtype);
   if (w_layout != NVFP4_LAYOUT_ROWS && w_layout != NVFP4_LAYOUT_TILED)
@@ -178,8 +179,19 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
   a.out = out;
   a.out_bf16 = out_dtype == NVFP4_DTYPE_BF16;
   a.ld_out = ld_out;
+  // split-K only with a large enough, aligned workspace (else one pass)
+  const size_t need = nvfp4::gemm_splitk_bytes(G, M, N, K, tiled);
+  if (need && workspace && ws_bytes >= need && aligned(workspace, 16)) {
+    a.splits = nvfp4::gemm_splitk_splits(G, M, N, K, tiled);
+    a.ws = (float*)workspace;
+  }
   hipStream_t s = (hipStream_t)stream;
   return finish("nvfp4_grouped_gemm", nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+size_t nvfp4_grouped_gemm_workspace_size(int32_t G, int64_t M, int64_t N, int64_t K, int32_t w_layout) {
+  if (G < 1 || M < 1 || N < 1 || K < 32) return 0;
+  return nvfp4::gemm_splitk_bytes(G, M, N, K, w_layout == NVFP4_LAYOUT_TILED);
 }
 
 int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,

@@ -31,6 +31,8 @@
 // A workgroup finds its (group, row range) from the device group offsets, so
 // the launch needs no host-side knowledge of the group sizes; workgroups past
 // the last tile exit at once.
+#include <algorithm>
+
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -556,9 +558,9 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
 // prefetched ahead, with no shared memory and no barriers.  With skip_bm > 0
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
-template <int NBW, int RB, bool FUSE>
+template <int NBW, int RB, bool FUSE, bool SPLIT>
 __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
-                                              int wave, int lane) {
+                                              int wave, int lane, int64_t ks0, int64_t ks1, int split) {
   static_assert(!FUSE || NBW == 2, "the fused epilogue pairs one gate and one up column block");
   constexpr int BN = 4 * NBW * 32;
   const int c = lane & 31;
@@ -623,9 +625,10 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
       sw[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
     }
   };
-  load(0, a0, a1, as, w0, w1, ws);
-  const int64_t nhs = 2 * nks;
-  for (int64_t hs = 0; hs < nhs; ++hs) {
+  // half-steps 2 ks0 .. 2 ks1 - 1 (all of K unless split)
+  const int64_t nhs = 2 * ks1;
+  load(2 * ks0, a0, a1, as, w0, w1, ws);
+  for (int64_t hs = 2 * ks0; hs < nhs; ++hs) {
     u32x4 na0[RB], na1[RB], nw0[NBW], nw1[NBW];
     uint32_t nas[RB], nws[NBW];
     const bool more = hs + 1 < nhs;
@@ -663,6 +666,23 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
     return;
   }
+  if constexpr (SPLIT) {
+    // raw partial sums of this split's K range
+    float* part = p.ws + (int64_t)split * p.M * p.N;
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) {
+      const int64_t n = n0 + 32 * cb + c;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t m = row0 + 32 * rb + acc32_row(i, kh);
+          if (m < row1) part[m * p.N + n] = acc[rb][cb][i];
+        }
+    }
+    return;
+  }
   const float a_gs = *p.a_gs;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
@@ -681,12 +701,16 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
 
 // One tile per workgroup, slot-major (the grid is an upper bound; workgroups
 // without a tile exit after one pass over the group offsets).
-template <int NBW, int RB, bool BATCHED, bool FUSE>
+template <int NBW, int RB, bool BATCHED, bool FUSE, bool SPLIT = false>
 __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm, int skip_min) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t slot = (int64_t)blockIdx.x / n_tiles;
-  const int64_t nt = (int64_t)blockIdx.x - slot * n_tiles;
+  // split-K: the grid is splits x (slots x column tiles), split-major
+  const int64_t work = SPLIT ? gridDim.x / p.splits : gridDim.x;
+  const int split = SPLIT ? (int)(blockIdx.x / work) : 0;
+  const int64_t t = SPLIT ? (int64_t)blockIdx.x - split * work : (int64_t)blockIdx.x;
+  const int64_t slot = t / n_tiles;
+  const int64_t nt = t - slot * n_tiles;
   int g;
   int64_t row0, row1;
   const bool found =
@@ -694,7 +718,129 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
               : find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1);
   if (!found) return;
   g = __builtin_amdgcn_readfirstlane(g);
-  stream32_tile<NBW, RB, FUSE>(p, g, row0, row1, nt, wave, lane);
+  const int64_t nks = p.K / 256;
+  const int64_t ks0 = SPLIT ? nks * split / p.splits : 0;
+  const int64_t ks1 = SPLIT ? nks * (split + 1) / p.splits : nks;
+  stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+}
+
+// Split-K tile for ranges of at most two 256-k steps (32 rows, 4 waves x
+// NBW column blocks): every load of the range is issued before the first
+// MFMA, so a workgroup costs one memory round trip instead of a pipeline
+// fill per step.  Loads past the range's end repeat its last half-step and
+// are not used; rows past the group's end read its last row (not stored).
+template <int NBW>
+__device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
+                                                 int wave, int lane, int64_t ks0, int64_t ks1, int split) {
+  constexpr int NH = 4;   // half-steps held at once
+  constexpr int BN = 4 * NBW * 32;
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t n0 = nt * BN + wave * NBW * 32;
+  if (n0 >= p.N) return;
+  const int64_t K = p.K;
+  const int64_t nks = K / 256;
+  const int64_t m_a = clampv<int64_t>(row0 + c, row0, row1 - 1);
+  int64_t a_row = p.a_row_index ? (int64_t)p.a_row_index[m_a] : m_a;
+  a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
+  const uint8_t* a_c = p.a_codes + a_row * (K / 2) + 32 * kh;
+  const uint8_t* a_s = p.a_scales + a_row * (K / 16) + 4 * kh;
+  const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
+  const uint8_t* w_t[NBW];
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    int64_t nb = n0 / 32 + cb;
+    nb = nb < nb_per_g ? nb : nb_per_g - 1;
+    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+  }
+  const int64_t hs0 = 2 * ks0;
+  const int nh = (int)(2 * (ks1 - ks0));
+  u32x4 a0[NH], a1[NH], w0[NH][NBW], w1[NH][NBW];
+  uint32_t as[NH], ws[NH][NBW];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int64_t hs = hs0 + (h < nh ? h : nh - 1);
+    const int64_t ks = hs >> 1, hh = hs & 1;
+    a0[h] = *(const u32x4*)(a_c + ks * 128 + 64 * hh);
+    a1[h] = *(const u32x4*)(a_c + ks * 128 + 64 * hh + 16);
+    as[h] = *(const uint32_t*)(a_s + ks * 16 + 8 * hh);
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) {
+      const uint8_t* t = w_t[cb] + ks * kTileBytes;
+      w0[h][cb] = *(const u32x4*)(t + 2048 * hh + 16 * lane);
+      w1[h][cb] = *(const u32x4*)(t + 2048 * hh + 1024 + 16 * lane);
+      ws[h][cb] = *(const uint32_t*)(t + 4096 + 256 * hh + 4 * lane);
+    }
+  }
+  floatx16_t acc[NBW];
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) acc[cb] = floatx16_t{};
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    if (h >= nh) break;   // uniform
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const half8_t af = dequant8(j < 4 ? a0[h][j] : a1[h][j - 4], scale_pair(byte_of(as[h], j >> 1)));
+#pragma unroll
+      for (int cb = 0; cb < NBW; ++cb) {
+        const half8_t bf = dequant8(j < 4 ? w0[h][cb][j] : w1[h][cb][j - 4], scale_pair(byte_of(ws[h][cb], j >> 1)));
+        acc[cb] = mfma32(af, bf, acc[cb]);
+      }
+    }
+  }
+  float* part = p.ws + (int64_t)split * p.M * p.N;
+#pragma unroll
+  for (int cb = 0; cb < NBW; ++cb) {
+    const int64_t n = n0 + 32 * cb + c;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = row0 + acc32_row(i, kh);
+      if (m < row1) part[m * p.N + n] = acc[cb][i];
+    }
+  }
+}
+
+template <int NBW>
+__global__ __launch_bounds__(256) void gemm_splitk_short(GemmArgs p, int64_t n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t work = gridDim.x / p.splits;
+  const int split = (int)(blockIdx.x / work);
+  const int64_t t = (int64_t)blockIdx.x - split * work;
+  const int64_t slot = t / n_tiles;
+  const int64_t nt = t - slot * n_tiles;
+  int g;
+  int64_t row0, row1;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, 32, 1, 0, 0, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t nks = p.K / 256;
+  split_short_tile<NBW>(p, g, row0, row1, nt, wave, lane, nks * split / p.splits, nks * (split + 1) / p.splits,
+                        split);
+}
+
+// Split-K reduction: out[m, n] = alpha(g, n) * (part_0 + part_1 + ...) in
+// split order, for the rows m of every group (rows outside all groups are
+// left untouched).  Block (x, y): row y, columns 256 x .. 256 x + 255.
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
+  const int64_t m = blockIdx.y;
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  // the group holding row m: the last g with offsets[g] <= m (clamped,
+  // non-decreasing offsets as find_tile reads them)
+  int lo = 0, hi = p.G;                   // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    const int64_t om = clampv<int64_t>(p.group_offsets[mid], 0, p.M);
+    if (om <= m) lo = mid;
+    else hi = mid;
+  }
+  const int64_t g0 = clampv<int64_t>(p.group_offsets[lo], 0, p.M);
+  const int64_t g1 = clampv<int64_t>(p.group_offsets[lo + 1], 0, p.M);
+  if (m < g0 || m >= g1) return;
+  float sum = p.ws[m * p.N + n];
+  for (int sp = 1; sp < p.splits; ++sp) sum += p.ws[((int64_t)sp * p.M + m) * p.N + n];
+  store_out(p, m, n, alpha_for(p, lo, n, *p.a_gs) * sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,8 +1323,41 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   constexpr int NBW = 2;
   const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
   const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
+  if constexpr (!FUSE) {
+    if (a.splits > 1 && a.ws) {
+      // few workgroups for the chip: split K, then reduce in split order
+      const int64_t nks = a.K / 256;
+      if ((nks + a.splits - 1) / a.splits <= 2)
+        hipLaunchKernelGGL(gemm_splitk_short<NBW>, dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a, n_tiles);
+      else
+        hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, false, true>), dim3((unsigned)(work * a.splits)),
+                           dim3(256), 0, s, a, n_tiles, 0, 0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0);
   return hipGetLastError();
+}
+
+int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled) {
+  // the streaming path with fewer than 512 workgroups (two per compute unit)
+  // splits K; the reduction's grid has one row per block
+  if (!tiled || M < 1 || M > 65535 || K % 256 || gemm_uses_big_tiles(G, M, tiled)) return 1;
+  const int64_t base = ((M + 31) / 32 + G) * ((N + 255) / 256);
+  if (base >= 512) return 1;
+  // ranges of at most two 256-k steps where 16 of them cover K (the
+  // short-range kernel), else 16 ranges
+  const int64_t nks = K / 256;
+  const int64_t sp = std::min<int64_t>(16, (nks + 1) / 2);
+  return sp > 1 ? (int32_t)sp : 1;
+}
+
+size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled) {
+  const int32_t sp = gemm_splitk_splits(G, M, N, K, tiled);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {

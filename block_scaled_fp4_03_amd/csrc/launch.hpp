@@ -85,7 +85,15 @@ struct GemmArgs {
   uint8_t* h_codes;    // [M, I/2]
   uint8_t* h_scales;   // [M, I/16]
   uint16_t* h_dq;      // nullable: [M, I] f16, e2m1 * e4m3 of h
+  // split-K (splits > 1): raw partial sums [splits, M, N] float32 in ws,
+  // added in split order and scaled by alpha by a second kernel
+  int32_t splits;
+  float* ws;
 };
+// split-K factor the launcher uses for these sizes (1: none) and the bytes
+// of partial sums it needs
+int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled);
+size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled);
 // true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);

@@ -105,6 +105,12 @@ def gemm_reads_dq(G, M, K, a_rows, tiled):
                                                          _lib.LAYOUT_TILED if tiled else _lib.LAYOUT_ROWS))
 
 
+def gemm_workspace_size(G, M, N, K, tiled):
+    """Bytes of split-K workspace grouped_gemm uses for these sizes (0: none)."""
+    return _lib.load().nvfp4_grouped_gemm_workspace_size(G, M, N, K,
+                                                          _lib.LAYOUT_TILED if tiled else _lib.LAYOUT_ROWS)
+
+
 def prepared_weight_bytes(G, N, K):
     return _lib.load().nvfp4_prepared_weight_bytes(G, N, K)
 
@@ -122,11 +128,14 @@ def prepare_weights(w_codes, w_scales, out=None):
 
 
 def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_offsets, M,
-                 a_row_index=None, out_dtype=torch.float32, out=None, w_tiled=None, a_dq=None):
+                 a_row_index=None, out_dtype=torch.float32, out=None, w_tiled=None, a_dq=None, workspace=None):
     """out [M, N] = alpha * A . W^T per group (see nvfp4_grouped_gemm).
     w_codes/w_scales give G, N, K; if w_tiled (the prepare_weights buffer) is
     passed, the kernel reads the weights from it instead.  a_dq is the
-    optional float16 form of A written by quantize / silu_mul_requant."""
+    optional float16 form of A written by quantize / silu_mul_requant.
+    workspace: None allocates the split-K workspace the library asks for
+    (nvfp4_grouped_gemm_workspace_size), False runs without one, or a uint8
+    tensor to use."""
     _check_dev(a_codes, a_scales, a_gs, w_gs, group_offsets, a_row_index, w_tiled, a_dq)
     G, N, K2 = w_codes.shape
     K = 2 * K2
@@ -141,9 +150,15 @@ def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_
     if a_dq is not None and (a_dq.dtype != torch.float16 or tuple(a_dq.shape) != (a_codes.shape[0], K)
                              or not a_dq.is_contiguous()):
         raise ValueError("a_dq must be a contiguous float16 [a_rows, K] tensor")
+    ws_bytes = _lib.load().nvfp4_grouped_gemm_workspace_size(G, M, N, K, layout) if (workspace is None and M > 0) \
+        else (0 if workspace is None or workspace is False else workspace.numel())
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=out.device)
+    wsp = workspace if workspace is not None and workspace is not False else None
     _lib.call("nvfp4_grouped_gemm", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
               _p(a_row_index), _p(a_dq), _p(wc), _p(ws), layout, _p(w_gs), seg, len(n_seg) - 1,
-              _p(group_offsets), G, M, N, K, _p(out), _dtype(out), out.stride(0), _stream())
+              _p(group_offsets), G, M, N, K, _p(out), _dtype(out), out.stride(0), _p(wsp),
+              ws_bytes if wsp is not None else 0, _stream())
     return out
 
 

@@ -167,10 +167,25 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None):
     return out
 
 
+_OFFSETS = {}
+
+
+def one_group_offsets(T, device):
+    """Device tensor [0, T] (int32) for one-group GEMMs, made once per (T,
+    device) so that repeated calls (and graph capture) copy nothing from the
+    host."""
+    key = (int(T), str(device))
+    t = _OFFSETS.get(key)
+    if t is None:
+        t = torch.tensor([0, T], dtype=torch.int32, device=device)
+        _OFFSETS[key] = t
+    return t
+
+
 def shared_expert(x, w1, w2, gs_x, gs_h, keep=False, fused=None):
     """Shared expert: one group, no routing.  Returns y [T, H] bf16."""
     T = x.shape[0]
-    off = torch.tensor([0, T], dtype=torch.int32, device=x.device)
+    off = one_group_offsets(T, x.device)
     xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(T, T) else None)
     y, st = _expert_mlp(xc, xs, gs_x, off, T, w1, w2, gs_h, T, xdq=xdq[0] if xdq else None, fused=fused)
     if keep:
@@ -183,7 +198,7 @@ def mla_projections(x1, x2, w_qakv, w_qb, gs_x1, gs_x2):
     """MLA projections: x1 [T, 7168] through fused q_a+kv (two segments, two
     global scales), x2 [T, 1536] through q_b.  Both outputs bf16."""
     T = x1.shape[0]
-    off = torch.tensor([0, T], dtype=torch.int32, device=x1.device)
+    off = one_group_offsets(T, x1.device)
     c1, s1, *d1 = ops.quantize(x1, gs_x1, dq=True if w_qakv.reads_dq(T, T) else None)
     o1 = w_qakv.gemm(c1, s1, gs_x1, off, T, out_dtype=torch.bfloat16, a_dq=d1[0] if d1 else None)
     c2, s2, *d2 = ops.quantize(x2, gs_x2, dq=True if w_qb.reads_dq(T, T) else None)

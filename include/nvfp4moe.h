@@ -196,6 +196,9 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *   out                [M, ld_out] of out_dtype (F32 or BF16, rounded to
  *                      nearest-even), columns [0, N) written; rows outside
  *                      every group are left untouched.
+ *   workspace          device memory of ws_bytes (16-byte aligned) or NULL:
+ *                      see nvfp4_grouped_gemm_workspace_size.  Caller-owned;
+ *                      calls that share one workspace must not overlap.
  * Errors: EINVAL for null pointers, an unknown dtype or layout; ESHAPE
  * unless 1 <= G <= NVFP4_MAX_EXPERTS, 1 <= n_segs <= NVFP4_MAX_SEGMENTS,
  * M >= 0, N >= 1, K >= 32 with K % 32 == 0 (K % 256 == 0 for the tiled
@@ -210,7 +213,20 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            const int32_t* n_seg, int32_t n_segs,
                            const int32_t* group_offsets, int32_t G,
                            int64_t M, int64_t N, int64_t K,
-                           void* out, int32_t out_dtype, int64_t ld_out, void* stream);
+                           void* out, int32_t out_dtype, int64_t ld_out,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_workspace_size - bytes of device workspace with which
+ * nvfp4_grouped_gemm of these sizes and weight layout splits K (0: it never
+ * does).  With few workgroups for the chip (few groups and rows, the tiled
+ * layout), K is cut into up to 16 ranges whose raw float32 partial sums are
+ * written to the workspace and then added in range order by a second kernel
+ * (deterministic), which applies alpha once.  A NULL or smaller workspace
+ * runs the GEMM in one pass; results differ only by float32 summation order
+ * (both within the documented bound).  Pure host function.
+ */
+size_t nvfp4_grouped_gemm_workspace_size(int32_t G, int64_t M, int64_t N, int64_t K, int32_t w_layout);
 
 /*
  * nvfp4_grouped_gemm_silu_requant - the first grouped GEMM of the expert MLP

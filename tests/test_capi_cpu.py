@@ -81,7 +81,7 @@ def _gemm(L, **kw):
                                 a["a_dq"], a["w_codes"], a["w_scales"], a["w_layout"], a["w_gs"], seg,
                                 len(a["n_seg"]) - 1,
                                 a["group_offsets"], a["G"], a["M"], a["N"], a["K"], a["out"],
-                                a["out_dtype"], a["ld_out"], NULL)
+                                a["out_dtype"], a["ld_out"], NULL, 0, NULL)
 
 
 def test_gemm_validation(L):
@@ -122,6 +122,18 @@ def test_fused_gemm_silu_validation(L):
     assert call(hc=ctypes.c_void_p(0x1004)) == lib.EALIGN
     assert call(hdq=ctypes.c_void_p(0x1008)) == lib.EALIGN
     assert call(M=0, a_codes=NULL, hc=NULL) == lib.OK
+
+
+def test_workspace_size_query(L):
+    q = L.nvfp4_grouped_gemm_workspace_size
+    # one group of 128 rows (the shared expert): K is split
+    n = q(1, 128, 6144, 7168, lib.LAYOUT_TILED)
+    assert n > 0 and n % (128 * 6144 * 4) == 0 and 2 <= n // (128 * 6144 * 4) <= 16
+    assert q(1, 128, 6144, 7168, lib.LAYOUT_ROWS) == 0        # streaming split only on the tiled layout
+    assert q(384, 1536, 6144, 7168, lib.LAYOUT_TILED) == 0    # decode: enough workgroups already
+    assert q(1, 8192, 6144, 7168, lib.LAYOUT_TILED) == 0      # 256-row tiles
+    assert q(1, 128, 6144, 256, lib.LAYOUT_TILED) == 0        # K too short to split
+    assert q(0, 128, 6144, 7168, lib.LAYOUT_TILED) == 0
 
 
 def test_reads_dq_query(L):

@@ -230,6 +230,32 @@ def test_gemm_big_tiles_every_last_tile_height():
     _gemm_case([257, 287, 288, 289, 320, 321, 384, 385, 511, 256], 96, 256, [0, 40, 96], 14, gather=True)
 
 
+def test_gemm_split_k_one_small_group():
+    # few workgroups: the tiled path splits K (4 ranges here) and reduces in
+    # order; checked against the bound in both output dtypes, without the
+    # workspace too, and for determinism
+    _gemm_case([100], 320, 2048, [0, 160, 320], 15, gather=False)
+    _gemm_case([61, 40], 256, 2048, [0, 256], 16, gather=True, out_bf16=True)
+    d = dev()
+    rng = np.random.default_rng(17)
+    ac, as_, ags = oracle_nvfp4(_x(100, 2048, 17))
+    wf = (rng.standard_normal((320, 2048)) * 0.02).astype(np.float32)
+    wc, ws, wg = oracle_nvfp4(wf)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    tiled = ops.prepare_weights(T(wc[None]), T(ws[None]))
+    args = (T(ac), T(as_), torch.tensor([ags], dtype=torch.float32, device=d), T(wc[None]), T(ws[None]),
+            torch.tensor([[wg]], dtype=torch.float32, device=d),
+            [0, 320], torch.tensor([0, 100], dtype=torch.int32, device=d), 100)
+    assert ops.gemm_workspace_size(1, 100, 320, 2048, True) > 0
+    a1 = to_np(ops.grouped_gemm(*args, w_tiled=tiled))
+    a2 = to_np(ops.grouped_gemm(*args, w_tiled=tiled))
+    a3 = to_np(ops.grouped_gemm(*args, w_tiled=tiled, workspace=False))
+    assert np.array_equal(a1, a2)                       # deterministic
+    ex, ab = exact_gemm_rows(ac, as_, wc, ws)
+    for o in (a1, a3):
+        check_gemm(o, ex, ab, float(F32(F32(ags) * wg)), 2048, False, "split-K")
+
+
 def test_gemm_four_segments_and_bf16():
     _gemm_case([70, 70], 256, 128, [0, 32, 100, 160, 256], 7, out_bf16=True)
 

@@ -195,6 +195,37 @@ def test_shared_expert_full_size():
     assert c >= 0.999
 
 
+def test_shared_expert_graph_replays_match_eager():
+    # the shared expert captured in a HIP graph (as the bench times it: split-K
+    # GEMMs, their reductions, quantise and SiLU-requant) gives the eager
+    # result on every replay, with eager work and synchronisation in between
+    log("pipeline shared expert: graph replays vs eager")
+    wl = workloads.WORKLOADS["shared"]
+    d = dev()
+    w1, w2 = pipeline.moe_weights(wl, d, experts=1)
+    x = workloads.batch(wl)["x"].to(d, torch.bfloat16)
+    gs_x = ops.global_scale(x.reshape(1, -1))
+    off = pipeline.one_group_offsets(wl.T, d)
+    xc, xs = ops.quantize(x, gs_x)
+    gs_h = ops.silu_mul_global_scale(w1.gemm(xc, xs, gs_x, off, wl.T))
+    ref = to_np(pipeline.shared_expert(x, w1, w2, gs_x, gs_h).view(torch.int16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pipeline.shared_expert(x, w1, w2, gs_x, gs_h)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y = pipeline.shared_expert(x, w1, w2, gs_x, gs_h)
+    for r in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(y.view(torch.int16)), ref), "replay %d" % r
+        pipeline.shared_expert(x, w1, w2, gs_x, gs_h)     # eager work between replays
+        torch.cuda.synchronize()
+
+
 # --- MLA projections: full size, sampled rows ----------------------------------
 
 def test_mla_projections_full_size():
