@@ -14,6 +14,8 @@ What it computes is written from definitions, in numpy, slowly and plainly:
   (Cody-Waite reduction plus a Taylor polynomial), one IEEE operation at a time.
 * ``quant``    - NVFP4 quantisation (16-element blocks, E4M3 block scale, FP32
   global scale in the dequantisation direction) and dequantisation.
+* ``fp8``      - the FP8 weight-only projection of the attention output path
+  (E4M3 weights with one float32 scale per 128 x 128 block, bf16 inputs).
 * ``moe``      - top-k routing, the stable group-by-expert permutation, the
   grouped GEMM of two NVFP4 operands, SiLU(gate)*up with re-quantisation, the
   weighted combine, and the three compositions: the routed MoE layer, the
@@ -37,4 +39,4 @@ The absolute end-to-end values at the full-size workloads have no printed
 worked example on the pages: they are pinned only through the pinned parts
 (parity unpinned in the sense that no external number states them).
 """
-from . import formats, expf, quant, moe  # noqa: F401
+from . import formats, expf, quant, moe, fp8  # noqa: F401
