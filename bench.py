@@ -383,6 +383,35 @@ def run_mla(steps, warmup):
         T, H, wl.n_qa, wl.n_kv, wl.q_lora, n2), ms, p10, p90, flops, bytes_)
 
 
+def run_attn_out(steps, warmup):
+    """Attention output path, T=4096: wo_a (FP8 weight-only, 65536 -> 1024)
+    then wo_b (NVFP4, 1024 -> 7168); and wo_a alone."""
+    import torch
+    from block_scaled_fp4_03_amd import ops, pipeline, workloads
+    wl = workloads.WORKLOADS["attn_out"]
+    dev = torch.device("cuda:0")
+    fa, fb = workloads.attn_out_weights(wl, device=dev)
+    codes, scales = ops.fp8_quantize_weight(fa)
+    del fa
+    w_ob = pipeline.quantize_stack([fb], (0, wl.H), dev)
+    del fb
+    xw = workloads.warmup_batch(wl)["x"].to(dev, torch.bfloat16)
+    gs_o = ops.global_scale(ops.fp8_weight_gemm(xw, codes, scales).reshape(1, -1))
+    x = workloads.batch(wl)["x"].to(dev, torch.bfloat16)
+    T, H, D, R = wl.T, wl.H, wl.n_qb, wl.o_lora
+    ms, p10, p90 = time_scrubbed(lambda: pipeline.attention_output(x, codes, scales, w_ob, gs_o), steps, warmup)
+    flops = 2.0 * T * (D * R + R * H)
+    bytes_ = T * D * 2 + R * D * (1 + 4.0 / (128 * 128)) + H * R * NVFP4_BYTES_PER_ELEM + T * R * 2 + T * H * 2
+    line = side_line("attention output: T=%d, %d -(FP8 wo_a)-> %d -(NVFP4 wo_b)-> %d" % (T, D, R, H), ms, p10, p90,
+                     flops, bytes_)
+    ams, ap10, ap90 = time_scrubbed(lambda: ops.fp8_weight_gemm(x, codes, scales), steps, warmup)
+    line["wo_a_alone"] = side_line("wo_a: %d x %d x %d, bf16 x E4M3 (128x128 block scales)" % (T, R, D), ams, ap10,
+                                   ap90, 2.0 * T * D * R, T * D * 2 + R * D + T * R * 2)
+    del x, codes, scales, w_ob
+    torch.cuda.empty_cache()
+    return line
+
+
 def fused_line(res):
     f = res.get("fused")
     if f is None:
@@ -472,6 +501,8 @@ def main():
         line["shared_expert"] = run_shared(args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["mla_projections"] = run_mla(args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        line["attention_output"] = run_attn_out(args.steps, args.warmup)
     print(json.dumps(line), flush=True)
 
 

@@ -286,6 +286,39 @@ int32_t silu_mul_requant(const void* gate_up, int32_t in_dtype, int64_t M, int64
                 s);
 }
 
+int32_t fp8_quantize_weight(const float* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* codes, float* scales,
+                            void* stream) {
+  const char* who = "fp8_quantize_weight";
+  if (N < 0 || K < 128 || K % 128) return fail(NVFP4_ESHAPE, "%s: need N >= 0, K >= 128 with K %% 128 == 0", who);
+  if (ld_w < K) return fail(NVFP4_ESHAPE, "%s: ld_w < K", who);
+  if (N == 0) return NVFP4_OK;
+  if (!w || !codes || !scales) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(w, 16) || ld_w % 4 || !aligned(codes, 4) || !aligned(scales, 4))
+    return fail(NVFP4_EALIGN, "%s: w and its pitch must be 16-byte aligned, codes and scales 4-byte", who);
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_fp8_quantize(w, N, K, ld_w, codes, scales, s), s);
+}
+
+int32_t fp8_weight_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* w_codes,
+                        const float* w_scales, int64_t N, void* out, int32_t out_dtype, int64_t ld_out,
+                        void* stream) {
+  const char* who = "fp8_weight_gemm";
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_EINVAL, "%s: unknown out dtype %d", who, out_dtype);
+  if (M < 0 || N < 1 || K < 128 || K % 128)
+    return fail(NVFP4_ESHAPE, "%s: need M >= 0, N >= 1, K >= 128 with K %% 128 == 0", who);
+  if (ld_x < K || ld_out < N) return fail(NVFP4_ESHAPE, "%s: ld_x < K or ld_out < N", who);
+  if (M == 0) return NVFP4_OK;
+  if (!x || !w_codes || !w_scales || !out) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(x, 16) || (ld_x * 2) % 16 || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(out, 4))
+    return fail(NVFP4_EALIGN, "%s: x, its pitch and w_codes must be 16-byte aligned", who);
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who,
+                nvfp4::launch_fp8_gemm(x, M, K, ld_x, w_codes, w_scales, N, out, out_dtype == NVFP4_DTYPE_BF16,
+                                       ld_out, s),
+                s);
+}
+
 size_t silu_mul_global_scale_workspace_size(int64_t M, int64_t I) {
   if (M < 0 || I < 0) return 0;
   return (size_t)nvfp4::silu_amax_chunks(M, I) * sizeof(float);

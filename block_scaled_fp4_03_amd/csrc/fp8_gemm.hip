@@ -1,0 +1,213 @@
+// FP8 (E4M3) weight-only projection of the attention output path: bf16
+// activations times E4M3 weights with one float32 scale per 128 x 128 block
+// (the projection the pages run through an FP8 weight-only einsum: page
+// "Current Bug: vLLM produces empty/garbage output", revision e8b289e,
+// "Phase 2: CuTeDSL Attention Kernel").
+//
+//  * fp8_quantize_kernel: one workgroup per 128 x 128 weight block; scale =
+//    amax / 448 (1 for an all-zero block), code = sign bit of w plus the E4M3
+//    magnitude nearest to |w / scale| (ties to even, saturating).
+//  * fp8_gemm_kernel: 128 x 128 output tiles, 4 waves, wave w owns output
+//    columns 32 w .. 32 w + 31 and all 128 rows (4 blocks of 32 x 32).  E4M3
+//    values convert exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale
+//    1), so every bf16 x E4M3 product of the 32x32x16 bf16 MFMA is exact.  A
+//    128-wide k-block has one weight scale per tile (128 output columns are
+//    one n-block), so each k-block's sum is formed in its own accumulator and
+//    added into the running result as acc += scale * block_sum (one fused
+//    multiply-add per value).  The activations of a k-block go from global
+//    memory straight into a swizzled, double-buffered local tile with
+//    direct-to-LDS loads, as in the NVFP4 256-row kernel; the weights of the
+//    next k-block are loaded into registers while the current one computes.
+#include "nvfp4_device.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t w32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int FB = 128;                 // block edge (scales) = tile edge
+constexpr int kFTile = FB * FB * 2;     // bytes of one bf16 activation k-block tile
+
+__device__ __forceinline__ int acc_row(int i, int kh) { return 8 * (i >> 2) + 4 * kh + (i & 3); }
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const float* __restrict__ w, int64_t N, int64_t K,
+                                                           int64_t ld_w, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  const int64_t nb = blockIdx.y, kb = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int col = 4 * (tid & 31);          // 4 consecutive k of the block
+  const int64_t k = kb * FB + col;
+  float v[16][4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t n = nb * FB + (tid >> 5) + 8 * i;
+    if (n < N) {
+      const float4 q = *(const float4*)(w + n * ld_w + k);
+      v[i][0] = q.x;
+      v[i][1] = q.y;
+      v[i][2] = q.z;
+      v[i][3] = q.w;
+    } else {
+      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][e]));
+  }
+  amax = block_max(amax);
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (tid == 0) scales[nb * (K / FB) + kb] = s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t n = nb * FB + (tid >> 5) + 8 * i;
+    if (n >= N) continue;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float q = v[i][e] / s;
+      const uint32_t c = e4m3_encode(__builtin_fabsf(q)) | ((__float_as_uint(v[i][e]) >> 24) & 0x80u);
+      word |= c << (8 * e);
+    }
+    *(uint32_t*)(codes + n * K + k) = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       int64_t ld_x, const uint8_t* __restrict__ wc,
+                                                       const float* __restrict__ ws, int64_t N, void* out,
+                                                       int32_t out_bf16, int64_t ld_out, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t mt = blockIdx.x / n_tiles;
+  const int64_t nt = blockIdx.x - mt * n_tiles;
+  const int64_t m0 = mt * FB, n0 = nt * FB;
+  const int64_t nkb = K / FB;
+
+  // activation copies: copy i of wave w fills tile rows 32 w + 4 i .. +3,
+  // lane l the physical chunk l % 16 of row 32 w + 4 i + l / 16, which holds
+  // logical chunk (l % 16) ^ (row % 16) (k 8 chunk .. 8 chunk + 7 of the
+  // k-block); rows past M read row M - 1 (their results are not stored)
+  const uint8_t* a_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * wave + 4 * i + (lane >> 4);
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    a_src[i] = (const uint8_t*)(x + m * ld_x) + 16 * ((lane & 15) ^ (r & 15));
+  }
+  auto a_copy = [&](int64_t kb, int buf, int i) {
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(a_src[i] + kb * 256),
+        (__attribute__((address_space(3))) void*)(lds + buf * kFTile + (32 * wave + 4 * i) * 256), 16, 0, 0);
+  };
+  // weights: lane (c, kh) reads bytes [128 kb + 64 kh, +64) of weight row n
+  const int64_t n = n0 + 32 * wave + c < N ? n0 + 32 * wave + c : N - 1;
+  const uint8_t* w_row = wc + n * K + 64 * kh;
+  auto w_load = [&](int64_t kb, w32x4 (&d)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = *(const w32x4*)(w_row + kb * FB + 16 * q);
+  };
+  const float* s_row = ws + (n0 / FB) * nkb;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
+  w32x4 wcur[4], wnxt[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a_copy(0, 0, i);
+  w_load(0, wcur);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int x15 = c & 15;
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int buf = (int)(kb & 1);
+    // this k-block's weight fragments, converted before any new load is
+    // issued (a use of loaded words while copies into local memory are in
+    // flight makes the compiler wait for every outstanding load)
+    bf16x8 bfr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w0 = wcur[j >> 1][2 * (j & 1)], w1 = wcur[j >> 1][2 * (j & 1) + 1];
+      const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+      const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+      const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+      const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+      bfr[j] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+    }
+    const float s = s_row[kb];
+    __builtin_amdgcn_sched_barrier(0);
+    // the last k-block reloads itself into the unused buffer and registers
+    const int64_t kn = kb + 1 < nkb ? kb + 1 : kb;
+    w_load(kn, wnxt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a_copy(kn, buf ^ 1, i);
+    const uint8_t* abuf = lds + buf * kFTile + c * 256;
+    f32x16 tmp[4];
+    // A fragments are read one substep ahead, right after their last use
+    bf16x8 af[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) af[rb] = *(const bf16x8*)(abuf + rb * 32 * 256 + (((8 * kh) ^ x15) << 4));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 bf = bfr[j];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        tmp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bf, j == 0 ? f32x16{} : tmp[rb], 0, 0, 0);
+        if (j < 7) af[rb] = *(const bf16x8*)(abuf + rb * 32 * 256 + (((8 * kh + j + 1) ^ x15) << 4));
+      }
+      // keep each substep's reads among its own MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][i] = __builtin_fmaf(s, tmp[rb][i], acc[rb][i]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wcur[q] = wnxt[q];
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next k-block have landed
+    __syncthreads();
+  }
+
+  const int64_t nn = n0 + 32 * wave + c;
+  if (nn >= N) return;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + 32 * rb + acc_row(i, kh);
+      if (m >= M) continue;
+      if (out_bf16)
+        ((uint16_t*)out)[m * ld_out + nn] = bf16_from_float(acc[rb][i]);
+      else
+        ((float*)out)[m * ld_out + nn] = acc[rb][i];
+    }
+}
+
+hipError_t launch_fp8_quantize(const float* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* codes, float* scales,
+                               hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_quantize_kernel, dim3((unsigned)(K / FB), (unsigned)((N + FB - 1) / FB)), dim3(256), 0, s,
+                     w, N, K, ld_w, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* wc, const float* ws,
+                           int64_t N, void* out, bool out_bf16, int64_t ld_out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t n_tiles = (N + FB - 1) / FB;
+  const int64_t m_tiles = (M + FB - 1) / FB;
+  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s, x, M, K, ld_x, wc, ws, N,
+                     out, out_bf16 ? 1 : 0, ld_out, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -98,6 +98,11 @@ size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled)
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 
+hipError_t launch_fp8_quantize(const float* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* codes, float* scales,
+                               hipStream_t s);
+hipError_t launch_fp8_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* wc, const float* ws,
+                           int64_t N, void* out, bool out_bf16, int64_t ld_out, hipStream_t s);
+
 hipError_t launch_silu_mul_requant(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
                                    const float* gs_h, uint8_t* codes, uint8_t* scales, uint16_t* dq,
                                    hipStream_t s);

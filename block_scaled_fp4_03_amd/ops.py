@@ -226,3 +226,30 @@ def combine(y, inv, w, out=None):
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     _lib.call("moe_combine", _p(y), _dtype(y), _p(inv), _p(w), T, k, H, _p(out), _stream())
     return out
+
+
+def fp8_quantize_weight(w):
+    """w [N, K] float32 -> (codes uint8 [N, K] E4M3, scales float32
+    [ceil(N/128), K/128]): one scale per 128 x 128 block."""
+    _check_dev(w)
+    if w.dtype != torch.float32 or w.stride(1) != 1:
+        raise ValueError("w must be float32 with unit column stride")
+    N, K = w.shape
+    codes = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N + 127) // 128, K // 128, dtype=torch.float32, device=w.device)
+    _lib.call("fp8_quantize_weight", _p(w), N, K, w.stride(0), _p(codes), _p(scales), _stream())
+    return codes, scales
+
+
+def fp8_weight_gemm(x, codes, scales, out_dtype=torch.bfloat16, out=None):
+    """x [M, K] bf16 . (E4M3 weights [N, K] with 128x128 block scales)^T -> [M, N]."""
+    _check_dev(x, codes, scales)
+    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be bfloat16 with unit column stride")
+    M, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    _lib.call("fp8_weight_gemm", _p(x), M, K, x.stride(0), _p(codes), _p(scales), N, _p(out), _dtype(out),
+              out.stride(0), _stream())
+    return out

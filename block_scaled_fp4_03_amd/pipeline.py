@@ -204,3 +204,16 @@ def mla_projections(x1, x2, w_qakv, w_qb, gs_x1, gs_x2):
     c2, s2, *d2 = ops.quantize(x2, gs_x2, dq=True if w_qb.reads_dq(T, T) else None)
     o2 = w_qb.gemm(c2, s2, gs_x2, off, T, out_dtype=torch.bfloat16, a_dq=d2[0] if d2 else None)
     return o1, o2
+
+
+def attention_output(x, wo_a_codes, wo_a_scales, w_ob, gs_o):
+    """Attention output path: x [T, 128*512] bf16 through wo_a (FP8
+    weight-only, bf16 out), then wo_b (NVFP4: the bf16 intermediate quantised
+    with the static global scale gs_o).  Returns (o [T, o_lora], y [T, H]),
+    both bf16."""
+    T = x.shape[0]
+    off = one_group_offsets(T, x.device)
+    o = ops.fp8_weight_gemm(x, wo_a_codes, wo_a_scales, out_dtype=torch.bfloat16)
+    oc, os_, *od = ops.quantize(o, gs_o, dq=True if w_ob.reads_dq(T, T) else None)
+    y = w_ob.gemm(oc, os_, gs_o, off, T, out_dtype=torch.bfloat16, a_dq=od[0] if od else None)
+    return o, y

@@ -19,14 +19,19 @@ prefill    routed layer, T=8192, E=384, top-6; logits N(0,1) plus a
            1..384, so expert popularity follows Zipf(1.1).
 mla        MLA projections, T=4096: x1 [T,7168] through the fused q_a+kv
            weight [1536+512, 7168]; x2 [T,1536] through q_b [65536, 1536].
+attn_out   attention output path, T=4096: all heads' outputs x [T, 128*512]
+           N(0,1) -> bf16 through wo_a [1024, 65536] (FP8 weights), then
+           wo_b [7168, 1024] (NVFP4 weights).
 =========  ==================================================================
 
 Draw order.  Every tensor has its own torch generator seeded from the batch
 seed and a tag, so tensors can be drawn independently and in any order:
 x -> seed*10+1, logits -> seed*10+2, expert-rank permutation -> seed*10+3,
-outlier positions -> seed*10+4, mla x2 -> seed*10+5.  Weights: one generator
+outlier positions -> seed*10+4, mla x2 -> seed*10+5, attention outputs ->
+seed*10+6.  Weights: one generator
 per (expert, projection), seed*1_000_003 + 3*e + p with p = 0 (gate_up),
-1 (down), 2 (extra projections); weights of the full-size routed workloads are
+1 (down), 2 (extra projections), 3 (wo_a), 4 (wo_b; the attention output
+workload has no experts); weights of the full-size routed workloads are
 drawn on the GPU (torch's Philox generator) because 384 experts are 25e9
 values; the rows the oracle needs are copied back to the host.
 The measured batch uses seed 0, the warmup batch that sets the activation
@@ -57,6 +62,7 @@ class Workload:
     n_kv: int = 512
     q_lora: int = 1536
     n_qb: int = 128 * 512
+    o_lora: int = 1024
     weights_on_device: bool = False
     warmup_tokens: int = 0    # tokens in the warmup batch (0: same T as the workload)
 
@@ -66,6 +72,8 @@ class Workload:
             return 6.0 * self.T * self.k * self.H * self.I
         if self.kind == "shared":
             return 6.0 * self.T * self.H * self.I
+        if self.kind == "attn_out":
+            return 2.0 * self.T * (self.n_qb * self.o_lora + self.o_lora * self.H)
         return 2.0 * self.T * (self.H * (self.n_qa + self.n_kv) + self.q_lora * self.n_qb)
 
 
@@ -76,6 +84,7 @@ WORKLOADS = {
     "prefill": Workload("prefill", "moe", T=8192, E=384, k=6, zipf=1.1, weights_on_device=True,
                         warmup_tokens=2),
     "mla": Workload("mla", "mla", T=4096),
+    "attn_out": Workload("attn_out", "attn_out", T=4096, warmup_tokens=64),
 }
 
 
@@ -132,9 +141,17 @@ def mla_weights(wl, seed=0, device="cpu"):
     return w1, w2
 
 
+def attn_out_weights(wl, seed=0, device="cpu"):
+    """(wo_a [o_lora, 128*512], wo_b [H, o_lora]) float32."""
+    return (weight(wl.o_lora, wl.n_qb, expert_seed(seed, 0, 3), device),
+            weight(wl.H, wl.o_lora, expert_seed(seed, 0, 4), device))
+
+
 def batch(wl, seed=0, tokens=None):
     """The activations (and logits) of one batch: dict of float32 CPU tensors."""
     T = wl.T if tokens is None else tokens
+    if wl.kind == "attn_out":
+        return {"x": activations(T, wl.n_qb, seed, tag=6)}
     out = {"x": activations(T, wl.H, seed, wl.outlier_frac, wl.outlier_mult)}
     if wl.kind == "moe":
         out["logits"] = router_logits(T, wl.E, seed, wl.zipf)

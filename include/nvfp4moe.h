@@ -339,6 +339,40 @@ int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm,
                     const float* topk_w, int64_t T, int32_t k, int64_t H, uint16_t* out,
                     void* stream);
 
+/*
+ * fp8_quantize_weight - block-scaled FP8 (E4M3) weights for the attention
+ * output projection wo_a, which the pages run as an FP8 weight-only einsum
+ * without an input scale (page e8b289e, "Phase 2: CuTeDSL Attention Kernel";
+ * "CURRENT_BUG.md - DeepSeek-V4 Blackwell NVFP4", "Architecture Notes").
+ *   w       [N, ld_w] float32 (16-byte aligned, ld_w % 4 == 0), columns [0, K).
+ *   codes   out [N, K] E4M3 (FN) codes.
+ *   scales  out [ceil(N/128), K/128] float32: one dequantisation scale per
+ *           128 x 128 block, s = amax / 448 (1.0 for an all-zero block).
+ * Per weight: q = w / s (float32 division), code = sign bit of w plus the
+ * E4M3 magnitude nearest to |q| (ties to even, saturating at 448, never NaN).
+ * Errors: EINVAL for null pointers; ESHAPE unless N >= 0, K >= 128 with
+ * K % 128 == 0, ld_w >= K; EALIGN as stated.
+ */
+int32_t fp8_quantize_weight(const float* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* codes,
+                            float* scales, void* stream);
+
+/*
+ * fp8_weight_gemm - out = x . value(W)^T with bf16 activations x [M, ld_x]
+ * (uint16 storage, columns [0, K)) and the FP8 weights of
+ * fp8_quantize_weight: value(n, k) = e4m3(codes[n, k]) * scales[n/128, k/128].
+ *   Every bf16 x E4M3 product is exact (bf16 matrix-core products); each
+ *   128-wide k-block is summed in float32 and added to the result as
+ *   result += scale * block_sum, in k order, so the result agrees with the
+ *   exact sum to float32 summation error, not bitwise.
+ *   out  [M, ld_out] of out_dtype (F32 or BF16, rounded to nearest-even).
+ * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless
+ * M >= 0, N >= 1, K >= 128 with K % 128 == 0, ld_x >= K, ld_out >= N;
+ * EALIGN unless x, its row pitch and the codes are 16-byte aligned.
+ */
+int32_t fp8_weight_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* w_codes,
+                        const float* w_scales, int64_t N, void* out, int32_t out_dtype, int64_t ld_out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,6 +136,20 @@ def test_workspace_size_query(L):
     assert q(0, 128, 6144, 7168, lib.LAYOUT_TILED) == 0
 
 
+def test_fp8_validation(L):
+    q, g = L.fp8_quantize_weight, L.fp8_weight_gemm
+    assert q(FAKE, 4, 200, 200, FAKE, FAKE, NULL) == lib.ESHAPE          # K % 128
+    assert q(FAKE, 4, 256, 128, FAKE, FAKE, NULL) == lib.ESHAPE          # ld_w < K
+    assert q(NULL, 4, 256, 256, FAKE, FAKE, NULL) == lib.EINVAL
+    assert q(ctypes.c_void_p(0x1004), 4, 256, 256, FAKE, FAKE, NULL) == lib.EALIGN
+    assert q(NULL, 0, 256, 256, NULL, NULL, NULL) == lib.OK
+    assert g(FAKE, 8, 200, 200, FAKE, FAKE, 64, FAKE, lib.DTYPE_BF16, 64, NULL) == lib.ESHAPE
+    assert g(FAKE, 8, 256, 256, FAKE, FAKE, 64, FAKE, 9, 64, NULL) == lib.EINVAL
+    assert g(FAKE, 8, 256, 256, FAKE, FAKE, 64, FAKE, lib.DTYPE_BF16, 32, NULL) == lib.ESHAPE
+    assert g(FAKE, 8, 256, 260, FAKE, FAKE, 64, FAKE, lib.DTYPE_BF16, 64, NULL) == lib.EALIGN   # pitch
+    assert g(NULL, 0, 256, 256, NULL, NULL, 64, NULL, lib.DTYPE_BF16, 64, NULL) == lib.OK
+
+
 def test_reads_dq_query(L):
     q = L.nvfp4_grouped_gemm_reads_dq
     assert q(1, 8192, 7168, 8192, lib.LAYOUT_TILED) == 1

@@ -8,7 +8,7 @@ import torch
 
 from _helpers import (F32, bf16_tensor, check_gemm, dev, exact_gemm_rows, log, oracle_nvfp4, to_np)
 from block_scaled_fp4_03_amd import ops
-from oracle import formats, moe, quant
+from oracle import formats, fp8, moe, quant
 
 pytestmark = pytest.mark.gpu
 
@@ -409,3 +409,40 @@ def test_combine_bit_exact(T, k, H, dtype):
         yt = yt.to(torch.bfloat16)
     out = ops.combine(yt, torch.from_numpy(inv).to(dev()), torch.from_numpy(w).to(dev()))
     assert np.array_equal(to_np(out).view(np.uint32), ref.view(np.uint32))
+
+
+# --- FP8 weight-only projection (wo_a) ------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(128, 128), (200, 384), (300, 1024)])
+def test_fp8_quantize_weight_bit_exact(N, K):
+    log("fp8 quantize", N, K)
+    rng = np.random.default_rng(N + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[:, :128][:min(N, 128)] *= 300.0          # one block with another range
+    if N > 128 and K > 128:
+        w[128:, 128:256] = 0.0                 # an all-zero block
+    w[1, 2] = -0.0
+    c_ref, s_ref = fp8.quantize_weight(w)
+    c, s = ops.fp8_quantize_weight(torch.from_numpy(w).to(dev()))
+    assert np.array_equal(to_np(c), c_ref)
+    assert np.array_equal(to_np(s), s_ref)
+
+
+@pytest.mark.parametrize("M,N,K,out_bf16", [(1, 128, 128, False), (200, 300, 512, False), (64, 128, 1024, True),
+                                             (257, 140, 384, True)])
+def test_fp8_weight_gemm_within_bound(M, N, K, out_bf16):
+    log("fp8 gemm", M, N, K, out_bf16)
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = formats.bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[:, K // 2:] *= 50.0                      # blocks with different scales
+    codes, scales = fp8.quantize_weight(w)
+    d = dev()
+    out = ops.fp8_weight_gemm(bf16_tensor(x, d), torch.from_numpy(codes).to(d), torch.from_numpy(scales).to(d),
+                              out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    W = fp8.dequantize_weight(codes, scales)
+    exact = x.astype(np.float64) @ W.T
+    absum = np.abs(x.astype(np.float64)) @ np.abs(W).T
+    check_gemm(to_np(out), exact, absum, 1.0, K, out_bf16, "fp8")
+    ref = fp8.weight_gemm(x, codes, scales, "bf16" if out_bf16 else "f32")
+    assert np.allclose(to_np(out), ref, rtol=2 ** -7 if out_bf16 else 1e-4, atol=np.abs(ref).max() * 1e-4)

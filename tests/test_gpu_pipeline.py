@@ -22,7 +22,7 @@ import torch
 from _helpers import (F32, audit_code_flips, bf16_tensor, check_gemm, cosine, dev, exact_gemm_rows, log,
                       to_np)
 from block_scaled_fp4_03_amd import ops, pipeline, workloads
-from oracle import moe, quant
+from oracle import fp8, moe, quant
 
 pytestmark = pytest.mark.gpu
 
@@ -341,3 +341,47 @@ def test_decode_layer_full_size_sampled():
 
 def test_prefill_layer_full_size_sampled():
     _routed_full("prefill", max_rows_per_expert=24)
+
+
+# --- attention output path (wo_a FP8, wo_b NVFP4): full size, sampled ----------
+
+def test_attention_output_full_size_sampled():
+    log("pipeline attention output T=4096: 65536 -(FP8)-> 1024 -(NVFP4)-> 7168")
+    wl = workloads.WORKLOADS["attn_out"]
+    d = dev()
+    fa, fb = workloads.attn_out_weights(wl, device=d)
+    codes, scales = ops.fp8_quantize_weight(fa)
+    # the FP8 weights of two sampled 128-row blocks, bit-exact with the oracle
+    blocks = [0, wl.o_lora // 128 - 1]
+    cols = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in blocks])
+    fa_s = fa[torch.from_numpy(cols).to(d)].cpu().numpy()
+    c_ref = np.empty((cols.size, wl.n_qb), np.uint8)
+    s_ref = np.empty((len(blocks), wl.n_qb // 128), np.float32)
+    for i in range(len(blocks)):
+        c_ref[i * 128:(i + 1) * 128], s_ref[i] = fp8.quantize_weight(fa_s[i * 128:(i + 1) * 128])
+    assert np.array_equal(to_np(codes)[cols], c_ref)
+    assert np.array_equal(to_np(scales)[blocks], s_ref)
+    w_ob = pipeline.quantize_stack([fb], (0, wl.H), d)
+    cb, sb, gb = moe.quantize_weight(fb.cpu().numpy())
+    assert np.array_equal(to_np(w_ob.codes[0]), cb) and np.array_equal(to_np(w_ob.scales[0]), sb)
+    del fa
+    xw = workloads.warmup_batch(wl)["x"].to(d, torch.bfloat16)
+    gs_o = ops.global_scale(ops.fp8_weight_gemm(xw, codes, scales).reshape(1, -1))
+    x = workloads.batch(wl)["x"]
+    o, y = pipeline.attention_output(x.to(d, torch.bfloat16), codes, scales, w_ob, gs_o)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(wl.T, 32, replace=False))
+    xs = x[torch.from_numpy(rows)].numpy()
+    # wo_a on the sampled rows and blocks: the float32 summation bound
+    W = fp8.dequantize_weight(c_ref, s_ref)        # the two sampled 128-row blocks
+    exact = xs.astype(np.float64) @ W.T
+    absum = np.abs(xs.astype(np.float64)) @ np.abs(W).T
+    check_gemm(to_np(o)[rows][:, cols], exact, absum, 1.0, wl.n_qb, True, "wo_a")
+    # wo_b from the GPU's own intermediate (teacher-forced): quantised with
+    # gs_o by the oracle, then the NVFP4 GEMM bound
+    g = to_np(gs_o)[0]
+    o_rows = to_np(o)[rows]
+    oq = quant.quantize(o_rows, g)
+    ex2, ab2 = exact_gemm_rows(oq[0], oq[1], cb, sb)
+    check_gemm(to_np(y)[rows], ex2, ab2, float(F32(F32(g) * gb)), wl.o_lora, True, "wo_b")
+    log("  attention output: sampled rows within bound")
