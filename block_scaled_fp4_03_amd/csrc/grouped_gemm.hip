@@ -1306,7 +1306,11 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     const int skip_min = dq ? kBigMinLast : BIG;
     constexpr int NBW = 2, RB = 1;
     const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-    const int64_t work_s = ((a.M + 32 * RB - 1) / (32 * RB) + a.G) * n_tiles_s;
+    // a group leaves fewer than skip_min rows over: at most that many 32-row
+    // tiles per group, and at most M / 32 + G in all
+    const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
+    const int64_t work_s =
+        std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
     hipLaunchKernelGGL((gemm_stream32<NBW, RB, true, FUSE>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s,
                        BIG, skip_min);
     hipError_t e = hipGetLastError();
