@@ -102,6 +102,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 // instead of one per 64 groups), for kernels with registers to spare at the
 // start of a tile.
 constexpr int kMaxChunks = 16;   // groups in chunks of 64, up to 1024 groups
+constexpr int kMaxGroups = 64 * kMaxChunks;
 
 __device__ __forceinline__ bool find_tile_batched(const int32_t* __restrict__ offsets, int G, int64_t M, int64_t slot, int bm,
                                           int last_min, int skip_bm, int skip_min, int& g_out, int64_t& r0,
@@ -700,28 +701,51 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
 }
 
 // One tile per workgroup, slot-major (the grid is an upper bound; workgroups
-// without a tile exit after one pass over the group offsets).
-template <int NBW, int RB, bool BATCHED, bool FUSE, bool SPLIT = false>
-__global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm, int skip_min) {
+// without a tile exit after one pass over the group offsets), or with PERSIST
+// a grid of a few workgroups per compute unit, each taking every grid-th
+// tile, so that a bound far above the tiles that exist costs no launches.
+template <int NBW, int RB, bool FUSE, bool SPLIT = false, bool PERSIST = false>
+__global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles, int skip_bm, int skip_min,
+                                                    int64_t total) {
+  // the group offsets, staged once per workgroup (all loads in flight
+  // together) so that the tile search costs no further global round trips
+  __shared__ int32_t s_off[kMaxGroups + 1];
+  for (int i = threadIdx.x; i <= p.G; i += blockDim.x) s_off[i] = p.group_offsets[i];
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // split-K: the grid is splits x (slots x column tiles), split-major
   const int64_t work = SPLIT ? gridDim.x / p.splits : gridDim.x;
   const int split = SPLIT ? (int)(blockIdx.x / work) : 0;
-  const int64_t t = SPLIT ? (int64_t)blockIdx.x - split * work : (int64_t)blockIdx.x;
-  const int64_t slot = t / n_tiles;
-  const int64_t nt = t - slot * n_tiles;
-  int g;
-  int64_t row0, row1;
-  const bool found =
-      BATCHED ? find_tile_batched(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)
-              : find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1);
-  if (!found) return;
-  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t t0 = SPLIT ? (int64_t)blockIdx.x - split * work : (int64_t)blockIdx.x;
   const int64_t nks = p.K / 256;
   const int64_t ks0 = SPLIT ? nks * split / p.splits : 0;
   const int64_t ks1 = SPLIT ? nks * (split + 1) / p.splits : nks;
-  stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+  if constexpr (!PERSIST) {
+    const int64_t slot = t0 / n_tiles;
+    const int64_t nt = t0 - slot * n_tiles;
+    int g;
+    int64_t row0, row1;
+    if (!find_tile(s_off, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)) return;
+    g = __builtin_amdgcn_readfirstlane(g);
+    stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+  } else {
+    // tiles t0, t0 + grid, ... below `total`; slots grow with t, and the
+    // tiles that exist come first, so the first missing one ends the loop
+    for (int64_t t = t0; t < total; t += work) {
+      const int64_t slot = t / n_tiles;
+      const int64_t nt = t - slot * n_tiles;
+      int g;
+      int64_t row0, row1;
+      if (!find_tile(s_off, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)) return;
+      g = __builtin_amdgcn_readfirstlane(g);
+      // the lane index made opaque per tile, so that per-lane values are not
+      // hoisted out of the loop and kept live across tiles
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
+    }
+  }
 }
 
 // Split-K tile for ranges of at most two 256-k steps (32 rows, 4 waves x
@@ -1104,6 +1128,60 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t
 //    (The compiler waits for all outstanding vector memory operations once
 //    copies into local memory and register loads are both in flight, so no
 //    load is issued after substep 0 that substeps 1-6 would wait for.)
+// Output of one wave's block of the 256-row tile (RB row blocks of 32, two
+// column blocks of 32) staged through LDS, 32 rows at a time, so that every
+// lane stores 16 contiguous bytes of one row: a quarter (f32) or an eighth
+// (bf16) of the store instructions of one element per lane, and no address
+// arithmetic per element.  Values and rounding are those of store_out.  The
+// caller guarantees that the tile's LDS is free (every wave is past the main
+// loop's last barrier), that out is 16-byte aligned and that ld_out and N are
+// multiples of 8.
+constexpr int kEpiStride = 68;   // floats per staged row: 64, plus 4 to shift the next row's banks
+template <int RB>
+__device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds, const floatx16_t (&acc)[RB][2],
+                                                const float (&alpha)[2], int64_t row0, int64_t row1, int64_t nw,
+                                                int wave, int lane) {
+  const int c = lane & 31, kh = lane >> 5;
+  float* st = (float*)lds + wave * 32 * kEpiStride;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[acc32_row(i, kh) * kEpiStride + 32 * cb + c] = alpha[cb] * acc[rb][cb][i];
+    // one wave's LDS operations complete in issue order: the reads below see
+    // the writes above, and the next row block's writes follow these reads
+    const int64_t mb = row0 + 32 * rb;
+    if (p.out_bf16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;     // 32 rows x 8 chunks of 8 columns
+        const int r = e >> 3, ch = e & 7;
+        const floatx4_t lo = *(const floatx4_t*)(st + r * kEpiStride + 8 * ch);
+        const floatx4_t hi = *(const floatx4_t*)(st + r * kEpiStride + 8 * ch + 4);
+        const int64_t m = mb + r, n = nw + 8 * ch;
+        if (m < row1 && n < p.N) {
+          u32x4 w;
+          w[0] = (uint32_t)bf16_from_float(lo[0]) | ((uint32_t)bf16_from_float(lo[1]) << 16);
+          w[1] = (uint32_t)bf16_from_float(lo[2]) | ((uint32_t)bf16_from_float(lo[3]) << 16);
+          w[2] = (uint32_t)bf16_from_float(hi[0]) | ((uint32_t)bf16_from_float(hi[1]) << 16);
+          w[3] = (uint32_t)bf16_from_float(hi[2]) | ((uint32_t)bf16_from_float(hi[3]) << 16);
+          *(u32x4*)((uint16_t*)p.out + m * p.ld_out + n) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = lane + 64 * q;     // 32 rows x 16 chunks of 4 columns
+        const int r = e >> 4, ch = e & 15;
+        const floatx4_t v = *(const floatx4_t*)(st + r * kEpiStride + 4 * ch);
+        const int64_t m = mb + r, n = nw + 4 * ch;
+        if (m < row1 && n < p.N) *(floatx4_t*)((float*)p.out + m * p.ld_out + n) = v;
+      }
+    }
+  }
+}
+
 template <int RB, bool FUSE>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
                                             int64_t n0, int wave, int lane) {
@@ -1132,37 +1210,41 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     const uint32_t ar = (uint32_t)__shfl(ar_l, r, 64);
     a_off[i] = ar * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (tr & 15));
   }
-  const uint8_t* a_base = (const uint8_t*)p.a_dq;
+  // A through a buffer resource: the lane's 32-bit offset in a VGPR, the
+  // half-step's k offset in an SGPR
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_dq, (short)0, (int)(uint32_t)(p.a_rows * K * 2), 0x00020000);
   auto a_copy = [&](int64_t hs, int buf, int i) {
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(a_base + hs * 256 + a_off[i]),
-        (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (8 * RB * wave + 4 * i) * 256), 16,
-        0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        a_rsrc, (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (8 * RB * wave + 4 * i) * 256),
+        16, (int)a_off[i], (int)(hs * 256), 0, 0);
   };
 
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
   // fused: the wave's h column block j, from gate block j and up block I/32 + j
   const int64_t j = n0 / 64 + wave;
-  const uint8_t* w_t[CB];
+  __amdgpu_buffer_rsrc_t w_rsrc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     int64_t nb = FUSE ? j + cb * (p.N / 64) : n0 / 32 + wave * CB + cb;
     nb = nb < nb_per_g ? nb : nb_per_g - 1;
-    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+    w_rsrc[cb] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes),
+                                                   (short)0, (int)(nks * kTileBytes), 0x00020000);
   }
+  const int w_lo = 16 * lane, w_hi = 16 * lane + 1024, w_sc = 4 * lane + 4096;
   // W words of a half-step: w0 (substeps 0-3), w1 (4-7), scale word ws
   struct WWords {
     u32x4 w0[CB], w1[CB];
     uint32_t ws[CB];
   };
   auto w_load = [&](int64_t hs, WWords& d) {
-    const int64_t ks = hs >> 1, h = hs & 1;
+    const int ks = (int)(hs >> 1), h = (int)(hs & 1);
+    const int so = ks * kTileBytes + 2048 * h, ss = ks * kTileBytes + 256 * h;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const uint8_t* t = w_t[cb] + ks * kTileBytes;
-      d.w0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
-      d.w1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
-      d.ws[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+      d.w0[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_lo, so, 0);
+      d.w1[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_hi, so, 0);
+      d.ws[cb] = __builtin_amdgcn_raw_buffer_load_b32(w_rsrc[cb], w_sc, ss, 0);
     }
   };
 
@@ -1177,8 +1259,15 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   for (int i = 0; i < NC; ++i) a_copy(0, 0, i);
   w_load(0, cur);
   half8_t bf[CB];
+  // the half-step's four scale bytes per column block as two f16 pairs
+  half2_t sc_lo[CB], sc_hi[CB], sc_n[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) bf[cb] = dequant8(cur.w0[cb][0], scale_pair(byte_of(cur.ws[cb], 0)));
+  for (int cb = 0; cb < CB; ++cb) {
+    sc_lo[cb] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.ws[cb], 1.0f, false);
+    sc_hi[cb] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.ws[cb], 1.0f, true);
+    sc_n[cb] = sc_lo[cb];
+    bf[cb] = dequant8(cur.w0[cb][0], half2_t{sc_lo[cb][0], sc_lo[cb][0]});
+  }
   const int x = c & 15;
   int chunk_ofs[8];
 #pragma unroll
@@ -1221,7 +1310,10 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
 #pragma unroll
       for (int wc = 0; wc < CB; ++wc) {
         const uint32_t word = j < 7 ? (j + 1 < 4 ? cur.w0[wc][j + 1] : cur.w1[wc][j + 1 - 4]) : nxt.w0[wc][0];
-        sfn[wc] = scale_pair(j < 7 ? byte_of(cur.ws[wc], (j + 1) >> 1) : byte_of(nxt.ws[wc], 0));
+        if (j == 6) sc_n[wc] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nxt.ws[wc], 1.0f, false);
+        const half2_t sp = j < 7 ? (((j + 1) >> 1) < 2 ? sc_lo[wc] : sc_hi[wc]) : sc_n[wc];
+        const _Float16 sv = j < 7 ? sp[((j + 1) >> 1) & 1] : sp[0];
+        sfn[wc] = half2_t{sv, sv};
 #pragma unroll
         for (int part = 0; part < 4; ++part) {
           const half2_t v = dequant_pair(word, part, sfn[wc]);
@@ -1236,6 +1328,11 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = nxt;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      sc_lo[cb] = sc_n[cb];
+      sc_hi[cb] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.ws[cb], 1.0f, true);
+    }
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next half-tile have landed
     __syncthreads();
   }
@@ -1245,6 +1342,16 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     return;
   }
   const float a_gs = *p.a_gs;
+  if (((uintptr_t)p.out & 15) == 0 && (p.ld_out & 7) == 0 && (p.N & 7) == 0) {
+    float alpha[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t n = n0 + (wave * CB + cb) * 32 + c;
+      alpha[cb] = n < p.N ? alpha_for(p, g, n, a_gs) : 0.0f;
+    }
+    store_block_vec<RB>(p, lds, acc, alpha, row0, row1, n0 + wave * CB * 32, wave, lane);
+    return;
+  }
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int64_t n = n0 + (wave * CB + cb) * 32 + c;
@@ -1311,8 +1418,11 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
     const int64_t work_s =
         std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
-    hipLaunchKernelGGL((gemm_stream32<NBW, RB, true, FUSE>), dim3((unsigned)work_s), dim3(256), 0, s, a, n_tiles_s,
-                       BIG, skip_min);
+    // persistent: three workgroups per compute unit (the looping kernel
+    // holds more registers than four fit)
+    const int64_t grid_s = std::min<int64_t>(work_s, 768);
+    hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a, n_tiles_s,
+                       BIG, skip_min, work_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_tiles = (a.N + BIG - 1) / BIG;
@@ -1334,15 +1444,15 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
       if ((nks + a.splits - 1) / a.splits <= 2)
         hipLaunchKernelGGL(gemm_splitk_short<NBW>, dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a, n_tiles);
       else
-        hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, false, true>), dim3((unsigned)(work * a.splits)),
-                           dim3(256), 0, s, a, n_tiles, 0, 0);
+        hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, true>), dim3((unsigned)(work * a.splits)),
+                           dim3(256), 0, s, a, n_tiles, 0, 0, work);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0);
+  hipLaunchKernelGGL((gemm_stream32<NBW, 1, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0, work);
   return hipGetLastError();
 }
 
@@ -1366,6 +1476,7 @@ size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled)
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.G < 1 || a.G > kMaxGroups) return hipErrorInvalidValue;  // the kernels stage at most kMaxGroups offsets
   if (a.w_tiled) return a.fuse ? launch_tiled<true>(a, s) : launch_tiled<false>(a, s);
   if (a.fuse) return hipErrorInvalidValue;  // the fused epilogue runs on the tiled kernels only
   if (a.M >= (int64_t)64 * a.G && a.K % TBK == 0) {
