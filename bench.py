@@ -45,16 +45,23 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+# untimed layer steps run once after the weights are prepared (see run_gpu)
+SETTLE_STEPS = 40
+# the two ways of running SiLU-requant, as the bench line names them
+SILU_PATHS = {True: "fused into the first GEMM's epilogue", False: "separate kernel"}
+
+
+def measured_traffic(workload, silu_path):
     """HBM bytes per L1 launch from committed rocprofv3 counter runs (FETCH_SIZE
     and WRITE_SIZE, scaled by the same counters on a copy of known size), or
-    None when no summary exists or the kernel source changed since."""
+    None when no summary exists, the kernel source changed since or the
+    summary covers the other SiLU-requant path's launch."""
     path = os.path.join(PROFILE_DIR, "grouped_gemm_l1_%s_traffic.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("silu_requant") != silu_path:
         return None
     return d.get("bytes_per_launch")
 
@@ -186,20 +193,30 @@ def run_gpu(workload, steps, warmup):
     layer = Layer(wl, dev)
     print("[bench] %s: weights ready in %.1fs, timing %d+%d steps" % (workload, layer.weight_setup_s, warmup, steps),
           file=sys.stderr, flush=True)
-    ms, per_op, pct = time_layer(layer, steps, warmup)
+    # the pipeline's default path: SiLU-requant as its own kernel (measured
+    # ahead of the fused epilogue at both shapes in steady state)
+    fused = False
+    # untimed steps before the first timed block: right after the weight
+    # preparation the first blocks of steps measure about 2% slow
+    for _ in range(SETTLE_STEPS):
+        layer.step()
+    torch.cuda.synchronize()
+    ms, per_op, pct = time_layer(layer, steps, warmup, fused=fused)
     n_touched = layer.touched_experts()
-    flops, l1_bytes, l1_flops = algorithmic(wl, n_touched, False)
+    flops, l1_bytes, l1_flops = algorithmic(wl, n_touched, fused)
     res = dict(ms=ms, per_op_ms=per_op, step_pct=pct, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
-               tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl)
+               tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl,
+               fused=fused)
     # the same layer with per-batch activation global scales computed on the
-    # device (two extra amax passes), timed the same way
+    # device (two extra amax passes; gs_h comes from the float32 gate_up, so
+    # SiLU-requant runs as its own kernel), timed the same way
     dms, dper_op, _ = time_layer(layer, steps, warmup, dynamic=True)
     res["dynamic"] = dict(ms=dms, per_op_ms=dper_op, tokens_per_s=wl.T / (dms * 1e-3))
-    # and with SiLU-requant in the first GEMM's epilogue (one launch fewer,
-    # no float32 gate_up in memory)
+    # and with the other SiLU-requant path (fused into the first GEMM's
+    # epilogue, or as its own kernel)
     if layer.w1.can_fuse_silu():
-        fms, fper_op, _ = time_layer(layer, steps, warmup, fused=True)
-        res["fused"] = dict(ms=fms, l1_ms=fper_op["gemm_l1"], tokens_per_s=wl.T / (fms * 1e-3))
+        oms, oper_op, _ = time_layer(layer, steps, warmup, fused=not fused)
+        res["other"] = dict(fused=not fused, ms=oms, l1_ms=oper_op["gemm_l1"], tokens_per_s=wl.T / (oms * 1e-3))
     return res
 
 
@@ -214,7 +231,9 @@ def roofline(res, bound):
         peak = F16_MFMA_PEAK_TFLOPS
         unit = "TFLOP/s"
     return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-            "traffic": measured_traffic(res["wl"].name), "kernel": "nvfp4_grouped_gemm L1 (gate_up)",
+            "traffic": measured_traffic(res["wl"].name, SILU_PATHS[res["fused"]]),
+            "kernel": "nvfp4_grouped_gemm_silu_requant L1 (gate_up, SiLU-requant epilogue)" if res["fused"]
+            else "nvfp4_grouped_gemm L1 (gate_up)",
             "kernel_ms": round(l1_ms, 4)}
 
 
@@ -412,12 +431,12 @@ def run_attn_out(steps, warmup):
     return line
 
 
-def fused_line(res):
-    f = res.get("fused")
+def other_path_line(res):
+    f = res.get("other")
     if f is None:
         return None
-    return {"value": round(f["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(f["ms"], 4),
-            "gemm_l1_ms": round(f["l1_ms"], 4)}
+    return {"silu_requant": SILU_PATHS[f["fused"]], "value": round(f["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(f["ms"], 4), "gemm_l1_ms": round(f["l1_ms"], 4)}
 
 
 def main():
@@ -475,7 +494,8 @@ def main():
         "per_op_ms": {k: round(v, 4) for k, v in main_res["per_op_ms"].items()},
         "dynamic_activation_scales": {"value": round(main_res["dynamic"]["tokens_per_s"], 1), "unit": "tokens/s",
                                       "ms_per_step": round(main_res["dynamic"]["ms"], 4)},
-        "fused_silu_epilogue": fused_line(main_res),
+        "silu_requant": SILU_PATHS[main_res["fused"]],
+        "other_silu_requant_path": other_path_line(main_res),
         "roofline": roofline(main_res, bound),
     }
     if not args.no_cpu_baseline:
@@ -491,7 +511,8 @@ def main():
                            "dynamic_activation_scales": {"value": round(pre["dynamic"]["tokens_per_s"], 1),
                                                          "unit": "tokens/s",
                                                          "ms_per_step": round(pre["dynamic"]["ms"], 4)},
-                           "fused_silu_epilogue": fused_line(pre),
+                           "silu_requant": SILU_PATHS[pre["fused"]],
+                           "other_silu_requant_path": other_path_line(pre),
                            "experts_touched": pre["n_touched"],
                            "per_op_ms": {k: round(v, 4) for k, v in pre["per_op_ms"].items()},
                            "roofline": roofline(pre, "mfma")}
