@@ -555,8 +555,11 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
 }
 
 // gemm_stream32: 32*RB rows x (4 waves x NBW x 32) columns per workgroup; each
-// wave streams its NBW 32-column blocks of W over the whole K, one half-step
-// prefetched ahead, with no shared memory and no barriers.  With skip_bm > 0
+// wave streams its NBW 32-column blocks of W over the whole K with two
+// half-steps of loads in flight (three register sets; at 148 VGPRs three
+// workgroups fit a compute unit, which keeps more bytes in flight per compute
+// unit than four workgroups with one half-step each), with no shared memory
+// and no barriers.  With skip_bm > 0
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
 template <int NBW, int RB, bool FUSE, bool SPLIT>
@@ -601,67 +604,68 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = floatx16_t{};
 
-  u32x4 a0[RB], a1[RB], w0[NBW], w1[NBW];
-  uint32_t as[RB], ws[NBW];
-  auto load = [&](int64_t hs, u32x4 (&c0)[RB], u32x4 (&c1)[RB], uint32_t (&sc)[RB], u32x4 (&d0)[NBW],
-                  u32x4 (&d1)[NBW], uint32_t (&sw)[NBW]) {
+  // operands of one half-step: A codes and scales, W codes and scales
+  struct Ops {
+    u32x4 a0[RB], a1[RB], w0[NBW], w1[NBW];
+    uint32_t as[RB], ws[NBW];
+  };
+  auto load = [&](int64_t hs, Ops& d) {
     const int64_t ks = hs >> 1, h = hs & 1;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (a_valid[rb]) {
-        c0[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h);
-        c1[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h + 16);
-        sc[rb] = *(const uint32_t*)(a_s[rb] + ks * 16 + 8 * h);
+        d.a0[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h);
+        d.a1[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h + 16);
+        d.as[rb] = *(const uint32_t*)(a_s[rb] + ks * 16 + 8 * h);
       } else {
-        c0[rb] = u32x4{0u, 0u, 0u, 0u};
-        c1[rb] = c0[rb];
-        sc[rb] = 0u;
+        d.a0[rb] = u32x4{0u, 0u, 0u, 0u};
+        d.a1[rb] = d.a0[rb];
+        d.as[rb] = 0u;
       }
     }
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
       const uint8_t* t = w_t[cb] + ks * kTileBytes;
-      d0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
-      d1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
-      sw[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+      d.w0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
+      d.w1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
+      d.ws[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
     }
   };
-  // half-steps 2 ks0 .. 2 ks1 - 1 (all of K unless split)
-  const int64_t nhs = 2 * ks1;
-  load(2 * ks0, a0, a1, as, w0, w1, ws);
-  for (int64_t hs = 2 * ks0; hs < nhs; ++hs) {
-    u32x4 na0[RB], na1[RB], nw0[NBW], nw1[NBW];
-    uint32_t nas[RB], nws[NBW];
-    const bool more = hs + 1 < nhs;
-    if (more) load(hs + 1, na0, na1, nas, nw0, nw1, nws);
+  auto compute = [&](const Ops& o) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       half8_t bf[NBW];
 #pragma unroll
       for (int cb = 0; cb < NBW; ++cb)
-        bf[cb] = dequant8(j < 4 ? w0[cb][j] : w1[cb][j - 4], scale_pair(byte_of(ws[cb], j >> 1)));
+        bf[cb] = dequant8(j < 4 ? o.w0[cb][j] : o.w1[cb][j - 4], scale_pair(byte_of(o.ws[cb], j >> 1)));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const half8_t af = dequant8(j < 4 ? a0[rb][j] : a1[rb][j - 4], scale_pair(byte_of(as[rb], j >> 1)));
+        const half8_t af = dequant8(j < 4 ? o.a0[rb][j] : o.a1[rb][j - 4], scale_pair(byte_of(o.as[rb], j >> 1)));
 #pragma unroll
         for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = mfma32(af, bf[cb], acc[rb][cb]);
       }
     }
-    if (more) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        a0[rb] = na0[rb];
-        a1[rb] = na1[rb];
-        as[rb] = nas[rb];
-      }
-#pragma unroll
-      for (int cb = 0; cb < NBW; ++cb) {
-        w0[cb] = nw0[cb];
-        w1[cb] = nw1[cb];
-        ws[cb] = nws[cb];
-      }
-    }
+  };
+  // half-steps 2 ks0 .. 2 ks1 - 1 (all of K unless split), two half-steps of
+  // loads in flight; the three operand sets rotate (no copy of registers
+  // with loads pending)
+  const int64_t h0 = 2 * ks0, nhs = 2 * ks1;
+  Ops s0, s1, s2;
+  load(h0, s0);
+  load(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+  // (the last two half-steps reload the last one: no branch around a load)
+  auto step = [&](int64_t hs, const Ops& cur, Ops& ld) {
+    load(hs + 2 < nhs ? hs + 2 : nhs - 1, ld);
+    compute(cur);
+  };
+  int64_t hs = h0;
+  for (; hs + 3 <= nhs; hs += 3) {
+    step(hs, s0, s2);
+    step(hs + 1, s1, s0);
+    step(hs + 2, s2, s1);
   }
+  if (hs < nhs) step(hs, s0, s2);
+  if (hs + 1 < nhs) step(hs + 1, s1, s0);
 
   if constexpr (FUSE) {
     silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
