@@ -95,6 +95,9 @@ class Layer:
         R = self.x.shape[0] * wl.k
         self.dq1 = True if self.w1.reads_dq(R, self.x.shape[0]) else None
         self.dq2 = True if self.w2.reads_dq(R, R) else None
+        # the pipeline's default SiLU-requant path for this shape (in the first
+        # GEMM's epilogue where that GEMM streams its weights)
+        self.fused_default = self.w1.fuse_by_default(R, self.x.shape[0])
         torch.cuda.synchronize()
 
     def step(self, ev=None, dynamic=False, fused=False):
@@ -193,9 +196,8 @@ def run_gpu(workload, steps, warmup):
     layer = Layer(wl, dev)
     print("[bench] %s: weights ready in %.1fs, timing %d+%d steps" % (workload, layer.weight_setup_s, warmup, steps),
           file=sys.stderr, flush=True)
-    # the pipeline's default path: SiLU-requant as its own kernel (measured
-    # ahead of the fused epilogue at both shapes in steady state)
-    fused = False
+    # the pipeline's default path (see pipeline._expert_mlp)
+    fused = layer.fused_default
     # untimed steps before the first timed block: right after the weight
     # preparation the first blocks of steps measure about 2% slow
     for _ in range(SETTLE_STEPS):

@@ -62,6 +62,17 @@ class NVFP4Weights:
         return self.tiled is not None and len(self.n_seg) == 3 and N == 2 * self.n_seg[1] and \
             self.n_seg[1] % 32 == 0 and (2 * K2) % 256 == 0
 
+    def fuse_by_default(self, M, a_rows):
+        """Whether a first GEMM of M rows runs SiLU-requant in its epilogue by
+        default: where it streams its weights in one pass (few rows per
+        expert: the fused launch measures faster and keeps no float32
+        gate_up), not where it uses the 256-row tiles (their epilogue would
+        idle the matrix cores) or splits K (the fused epilogue needs whole
+        sums)."""
+        G, N, K2 = self.codes.shape
+        return self.can_fuse_silu() and not self.reads_dq(M, a_rows) and \
+            ops.gemm_workspace_size(G, M, N, 2 * K2, True) == 0
+
     def gemm_silu_requant(self, a_codes, a_scales, a_gs, group_offsets, M, gs_h, **kw):
         G, N, K2 = self.codes.shape
         return ops.grouped_gemm_silu_requant(a_codes, a_scales, a_gs, self.tiled, self.gs, group_offsets, M,
@@ -117,12 +128,12 @@ def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False):
 def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xdq=None, fused=None):
     """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` (static
     gs_h and a fusable W1) the re-quantisation runs in the L1 epilogue, with
-    identical results and no float32 gate_up in memory; by default it runs as
-    its own kernel, which measures faster on MI355X (the epilogue's vector
-    work stalls the matrix cores of the 256-row tiles).  gs_h None computes
-    it from this batch's gate_up.  Returns (y bf16, stages)."""
+    identical results and no float32 gate_up in memory; None picks
+    w1.fuse_by_default (fused where L1 streams its weights, a separate kernel
+    where it runs 256-row tiles or splits K).  gs_h None computes it from
+    this batch's gate_up.  Returns (y bf16, stages)."""
     if fused is None:
-        fused = False
+        fused = gs_h is not None and w1.fuse_by_default(R, a_rows)
     if fused and (gs_h is None or not w1.can_fuse_silu()):
         raise ValueError("the fused epilogue needs a static gs_h and tiled W1 with I % 32 == 0")
     dq2 = True if w2.reads_dq(R, R) else None
@@ -147,9 +158,9 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None):
     batch), or None for dynamic ones computed on the device from this batch
     (gs_x = amax(x)/2688 before quantising x, gs_h = amax(SiLU(g)*u)/2688
     between the two GEMMs; the host never waits for them).  `fused` runs
-    SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant);
-    the results are identical either way.  Returns out [T, H] bf16 (and the
-    stages)."""
+    SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant),
+    None chooses by the first GEMM's kernel (see _expert_mlp); the results
+    are identical either way.  Returns out [T, H] bf16 (and the stages)."""
     T, H = x.shape
     R = T * k
     if gs_x is None:
