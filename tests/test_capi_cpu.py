@@ -187,3 +187,21 @@ def test_global_scale_validation_and_workspace(L):
     assert L.nvfp4_global_scale(FAKE, lib.DTYPE_F32, 2, 12, 16, FAKE, FAKE, 64, NULL) == lib.ESHAPE
     assert L.nvfp4_global_scale(FAKE, lib.DTYPE_F32, 2, 16, 16, FAKE, FAKE, 0, NULL) == lib.ESHAPE
     assert L.silu_mul_global_scale(FAKE, lib.DTYPE_F32, 4, 20, 40, FAKE, FAKE, 64, NULL) == lib.ESHAPE
+
+
+def test_fused_silu_default_choice(L):
+    # the pipeline fuses SiLU-requant into the first GEMM where that GEMM
+    # streams its weights in one pass, and not on 256-row tiles or split K
+    import torch
+    from block_scaled_fp4_03_amd.pipeline import NVFP4Weights
+
+    def w1(G, I=3072, H=7168, tiled=True):
+        m = lambda *s: torch.empty(*s, dtype=torch.uint8, device="meta")
+        return NVFP4Weights(m(G, 2 * I, H // 2), m(G, 2 * I, H // 16), m(G, 2), (0, I, 2 * I),
+                            tiled=m(1) if tiled else None)
+
+    assert w1(384).fuse_by_default(1536, 256)                 # decode: 384 experts, 6 x 256 rows
+    assert not w1(384).fuse_by_default(49152, 8192)           # prefill: 256-row tiles
+    assert not w1(1).fuse_by_default(128, 128)                # shared expert: K split
+    assert not w1(384, tiled=False).fuse_by_default(1536, 256)  # row-major weights: no fused kernel
+    assert not w1(8, I=48).fuse_by_default(64, 32)            # I % 32 != 0
