@@ -14,10 +14,14 @@
 //    128-wide k-block has one weight scale per tile (128 output columns are
 //    one n-block), so each k-block's sum is formed in its own accumulator and
 //    added into the running result as acc += scale * block_sum (one fused
-//    multiply-add per value).  The activations of a k-block go from global
-//    memory straight into a swizzled, double-buffered local tile with
-//    direct-to-LDS loads, as in the NVFP4 256-row kernel; the weights of the
-//    next k-block are loaded into registers while the current one computes.
+//    multiply-add per value), software-pipelined: the previous block's
+//    scaled accumulation and the next weight fragment's conversion run
+//    between the current block's MFMAs.  The activations of a k-block go
+//    from global memory straight into a swizzled, double-buffered local tile
+//    with direct-to-LDS loads, as in the NVFP4 256-row kernel; the weights of
+//    the next k-block are loaded into registers while the current one
+//    computes.  Row tiles are dealt to the XCDs so that all column tiles of a
+//    row tile share one XCD's L2.
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -88,8 +92,14 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31;
   const int kh = lane >> 5;
-  const int64_t mt = blockIdx.x / n_tiles;
-  const int64_t nt = blockIdx.x - mt * n_tiles;
+  // workgroups go to the 8 XCDs round-robin; row tiles are dealt out so
+  // that every column tile of a row tile runs on the same XCD (its
+  // activation rows then come from that XCD's L2 after the first read,
+  // instead of from memory once per column tile)
+  const int64_t xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+  const int64_t mt = idx / n_tiles * 8 + xcd;
+  const int64_t nt = idx % n_tiles;
+  if (mt * FB >= M) return;
   const int64_t m0 = mt * FB, n0 = nt * FB;
   const int64_t nkb = K / FB;
 
@@ -118,9 +128,17 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
   };
   const float* s_row = ws + (n0 / FB) * nkb;
 
-  f32x16 acc[4];
+  // the k-blocks are software-pipelined: while a block's 32 MFMAs run into
+  // one set of block accumulators, the previous block's sums (the other
+  // set) are scaled into the result 8 values per substep, and the next
+  // substep's weight fragment is converted, so that the vector work of a
+  // block hides under the matrix work of the next instead of following it
+  f32x16 acc[4], tmp_a[4], tmp_b[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x16{};
+  for (int rb = 0; rb < 4; ++rb) {
+    acc[rb] = f32x16{};
+    tmp_b[rb] = f32x16{};     // "previous block" of block 0: zeros, scaled by 0
+  }
   w32x4 wcur[4], wnxt[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) a_copy(0, 0, i);
@@ -128,53 +146,70 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int x15 = c & 15;
-  for (int64_t kb = 0; kb < nkb; ++kb) {
+  // weight fragment of substep j (k 16 j .. 16 j + 15 of the block) from the
+  // block's loaded words
+  auto convert = [&](const w32x4 (&w)[4], int j) {
+    const uint32_t w0 = w[j >> 1][2 * (j & 1)], w1 = w[j >> 1][2 * (j & 1) + 1];
+    const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+  };
+  bf16x8 bcur = convert(wcur, 0);
+  float s_prev = 0.0f;
+  // one k-block: MFMAs into tc, the previous block's tp scaled by s_prev
+  auto block = [&](int64_t kb, f32x16 (&tc)[4], const f32x16 (&tp)[4]) {
     const int buf = (int)(kb & 1);
-    // this k-block's weight fragments, converted before any new load is
-    // issued (a use of loaded words while copies into local memory are in
-    // flight makes the compiler wait for every outstanding load)
-    bf16x8 bfr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w0 = wcur[j >> 1][2 * (j & 1)], w1 = wcur[j >> 1][2 * (j & 1) + 1];
-      const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-      const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-      const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-      const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-      bfr[j] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-    }
-    const float s = s_row[kb];
-    __builtin_amdgcn_sched_barrier(0);
     // the last k-block reloads itself into the unused buffer and registers
     const int64_t kn = kb + 1 < nkb ? kb + 1 : kb;
     w_load(kn, wnxt);
 #pragma unroll
     for (int i = 0; i < 8; ++i) a_copy(kn, buf ^ 1, i);
     const uint8_t* abuf = lds + buf * kFTile + c * 256;
-    f32x16 tmp[4];
-    // A fragments are read one substep ahead, right after their last use
     bf16x8 af[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) af[rb] = *(const bf16x8*)(abuf + rb * 32 * 256 + (((8 * kh) ^ x15) << 4));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bf16x8 bf = bfr[j];
+      const bf16x8 bf = bcur;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        tmp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bf, j == 0 ? f32x16{} : tmp[rb], 0, 0, 0);
+        tc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bf, j == 0 ? f32x16{} : tc[rb], 0, 0, 0);
         if (j < 7) af[rb] = *(const bf16x8*)(abuf + rb * 32 * 256 + (((8 * kh + j + 1) ^ x15) << 4));
       }
-      // keep each substep's reads among its own MFMAs
+      if (j < 7) bcur = convert(wcur, j + 1);
+      // the previous block: row block j / 2, values 8 (j % 2) .. + 7
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[j >> 1][8 * (j & 1) + i] = __builtin_fmaf(s_prev, tp[j >> 1][8 * (j & 1) + i], acc[j >> 1][8 * (j & 1) + i]);
+      // keep each substep's reads, conversions and updates among its own MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][i] = __builtin_fmaf(s, tmp[rb][i], acc[rb][i]);
+    s_prev = s_row[kb];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wcur[q] = wnxt[q];
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next k-block have landed
     __syncthreads();
+    bcur = convert(wcur, 0);
+  };
+  // two blocks per iteration so that the accumulator sets alternate by name
+  int64_t kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    block(kb, tmp_a, tmp_b);
+    block(kb + 1, tmp_b, tmp_a);
+  }
+  if (kb < nkb) {
+    block(kb, tmp_a, tmp_b);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][i] = __builtin_fmaf(s_prev, tmp_a[rb][i], acc[rb][i]);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][i] = __builtin_fmaf(s_prev, tmp_b[rb][i], acc[rb][i]);
   }
 
   const int64_t nn = n0 + 32 * wave + c;
@@ -204,8 +239,8 @@ hipError_t launch_fp8_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
                            int64_t N, void* out, bool out_bf16, int64_t ld_out, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int64_t n_tiles = (N + FB - 1) / FB;
-  const int64_t m_tiles = (M + FB - 1) / FB;
-  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s, x, M, K, ld_x, wc, ws, N,
+  const int64_t m_slots = ((M + FB - 1) / FB + 7) / 8 * 8;   // row tiles, padded to the 8 XCDs
+  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)(m_slots * n_tiles)), dim3(256), 0, s, x, M, K, ld_x, wc, ws, N,
                      out, out_bf16 ? 1 : 0, ld_out, n_tiles);
   return hipGetLastError();
 }
