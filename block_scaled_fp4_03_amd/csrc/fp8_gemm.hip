@@ -18,10 +18,11 @@
 //    scaled accumulation and the next weight fragment's conversion run
 //    between the current block's MFMAs.  The activations of a k-block go
 //    from global memory straight into a swizzled, double-buffered local tile
-//    with direct-to-LDS loads, as in the NVFP4 256-row kernel; the weights of
-//    the next k-block are loaded into registers while the current one
-//    computes.  Row tiles are dealt to the XCDs so that all column tiles of a
-//    row tile share one XCD's L2.
+//    with direct-to-LDS loads, as in the NVFP4 256-row kernel; so do the
+//    weights of a k-block (whole 128-byte rows per load, swizzled so that
+//    each lane's 64 bytes read back without bank conflicts), each wave
+//    copying and reading its own 32 rows.  Row tiles are dealt to the XCDs so
+//    that all column tiles of a row tile share one XCD's L2.
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -36,6 +37,7 @@ typedef uint32_t w32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FB = 128;                 // block edge (scales) = tile edge
 constexpr int kFTile = FB * FB * 2;     // bytes of one bf16 activation k-block tile
+constexpr int kWTile = FB * FB;         // bytes of one E4M3 weight k-block tile (128 rows x 128 k)
 
 __device__ __forceinline__ int acc_row(int i, int kh) { return 8 * (i >> 2) + 4 * kh + (i & 3); }
 
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
                                                        int64_t ld_x, const uint8_t* __restrict__ wc,
                                                        const float* __restrict__ ws, int64_t N, void* out,
                                                        int32_t out_bf16, int64_t ld_out, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFTile];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFTile + 2 * kWTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31;
@@ -119,12 +121,31 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
         (const void*)(a_src[i] + kb * 256),
         (__attribute__((address_space(3))) void*)(lds + buf * kFTile + (32 * wave + 4 * i) * 256), 16, 0, 0);
   };
-  // weights: lane (c, kh) reads bytes [128 kb + 64 kh, +64) of weight row n
-  const int64_t n = n0 + 32 * wave + c < N ? n0 + 32 * wave + c : N - 1;
-  const uint8_t* w_row = wc + n * K + 64 * kh;
-  auto w_load = [&](int64_t kb, w32x4 (&d)[4]) {
+  // weights go through LDS too, so that the loads from memory are whole
+  // 128-byte rows: copy i of wave w fills the wave's rows 8 i .. 8 i + 7 of
+  // the k-block (lane l: row 8 i + l / 8, physical chunk l % 8 holding
+  // logical chunk (l % 8) ^ (row % 8), 16 k each); a wave copies and reads
+  // only its own 32 rows.  Lane (c, kh) then reads the 64 bytes
+  // [64 kh, 64 kh + 64) of its row c (k-half kh of the block).
+  uint8_t* const wlds = lds + 2 * kFTile;
+  const uint8_t* w_src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = *(const w32x4*)(w_row + kb * FB + 16 * q);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int64_t nr = n0 + 32 * wave + r < N ? n0 + 32 * wave + r : N - 1;
+    w_src[i] = wc + nr * K + 16 * ((lane & 7) ^ (r & 7));
+  }
+  auto w_copy = [&](int64_t kb, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(w_src[i] + kb * FB),
+          (__attribute__((address_space(3))) void*)(wlds + buf * kWTile + (32 * wave + 8 * i) * FB), 16, 0, 0);
+  };
+  auto w_load = [&](int buf, w32x4 (&d)[4]) {
+    const uint8_t* row = wlds + buf * kWTile + (32 * wave + c) * FB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = *(const w32x4*)(row + 16 * ((4 * kh + q) ^ (c & 7)));
   };
   const float* s_row = ws + (n0 / FB) * nkb;
 
@@ -139,12 +160,13 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
     acc[rb] = f32x16{};
     tmp_b[rb] = f32x16{};     // "previous block" of block 0: zeros, scaled by 0
   }
-  w32x4 wcur[4], wnxt[4];
+  w32x4 wcur[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) a_copy(0, 0, i);
-  w_load(0, wcur);
+  w_copy(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  w_load(0, wcur);
   const int x15 = c & 15;
   // weight fragment of substep j (k 16 j .. 16 j + 15 of the block) from the
   // block's loaded words
@@ -163,7 +185,7 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
     const int buf = (int)(kb & 1);
     // the last k-block reloads itself into the unused buffer and registers
     const int64_t kn = kb + 1 < nkb ? kb + 1 : kb;
-    w_load(kn, wnxt);
+    w_copy(kn, buf ^ 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) a_copy(kn, buf ^ 1, i);
     const uint8_t* abuf = lds + buf * kFTile + c * 256;
@@ -187,10 +209,9 @@ __global__ __launch_bounds__(256) void fp8_gemm_kernel(const uint16_t* __restric
       __builtin_amdgcn_sched_barrier(0);
     }
     s_prev = s_row[kb];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wcur[q] = wnxt[q];
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next k-block have landed
     __syncthreads();
+    w_load(buf ^ 1, wcur);             // (the wave's own rows: written by its own copies)
     bcur = convert(wcur, 0);
   };
   // two blocks per iteration so that the accumulator sets alternate by name
