@@ -1422,8 +1422,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
     const int64_t work_s =
         std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
-    // persistent: three workgroups per compute unit (the looping kernel
-    // holds more registers than four fit)
+    // persistent: three workgroups per compute unit (164 VGPRs with two
+    // half-steps of loads in flight)
     const int64_t grid_s = std::min<int64_t>(work_s, 768);
     hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a, n_tiles_s,
                        BIG, skip_min, work_s);
