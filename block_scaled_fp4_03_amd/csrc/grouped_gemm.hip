@@ -850,7 +850,10 @@ __global__ __launch_bounds__(256) void gemm_splitk_short(GemmArgs p, int64_t n_t
 // Split-K reduction: out[m, n] = alpha(g, n) * (part_0 + part_1 + ...) in
 // split order, for the rows m of every group (rows outside all groups are
 // left untouched).  Block (x, y): row y, columns 256 x .. 256 x + 255.
-__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
+// tile_bm > 0: only rows that tiles of tile_bm rows cover (a group's full
+// tiles and its last tile when that has at least tile_last_min rows); the
+// other rows belong to another kernel's launch.
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, int tile_bm, int tile_last_min) {
   const int64_t m = blockIdx.y;
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (n >= p.N) return;
@@ -866,6 +869,10 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   const int64_t g0 = clampv<int64_t>(p.group_offsets[lo], 0, p.M);
   const int64_t g1 = clampv<int64_t>(p.group_offsets[lo + 1], 0, p.M);
   if (m < g0 || m >= g1) return;
+  if (tile_bm > 0) {
+    const int64_t rows = g1 - g0, rest = rows % tile_bm;
+    if (m - g0 >= rows - rest + (rest >= tile_last_min ? rest : 0)) return;
+  }
   float sum = p.ws[m * p.N + n];
   for (int sp = 1; sp < p.splits; ++sp) sum += p.ws[((int64_t)sp * p.M + m) * p.N + n];
   store_out(p, m, n, alpha_for(p, lo, n, *p.a_gs) * sum);
@@ -1186,9 +1193,10 @@ __device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds,
   }
 }
 
-template <int RB, bool FUSE>
+template <int RB, bool FUSE, bool SPLIT = false>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
-                                            int64_t n0, int wave, int lane) {
+                                            int64_t n0, int wave, int lane, int64_t hs0 = 0, int64_t hs1 = -1,
+                                            int split = 0) {
   constexpr int CB = 2;            // 64 columns per wave
   constexpr int NC = 2 * RB;       // copies per wave and half-step
   const int c = lane & 31;
@@ -1258,10 +1266,12 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = floatx16_t{};
 
+  // half-steps hs0 .. hs1 - 1 (all of K unless split); hs0 is in buffer 0
+  if (hs1 < 0) hs1 = 2 * nks;
   WWords cur, nxt;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) a_copy(0, 0, i);
-  w_load(0, cur);
+  for (int i = 0; i < NC; ++i) a_copy(hs0, 0, i);
+  w_load(hs0, cur);
   half8_t bf[CB];
   // the half-step's four scale bytes per column block as two f16 pairs
   half2_t sc_lo[CB], sc_hi[CB], sc_n[CB];
@@ -1278,11 +1288,10 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   for (int j = 0; j < 8; ++j) chunk_ofs[j] = ((8 * kh + j) ^ x) << 4;
   __builtin_amdgcn_s_waitcnt(0);       // this wave's copies of the first half-tile have landed
   __syncthreads();
-  const int64_t nhs = 2 * nks;
-  for (int64_t hs = 0; hs < nhs; ++hs) {
-    const int h = (int)(hs & 1);
+  for (int64_t hs = hs0; hs < hs1; ++hs) {
+    const int h = (int)((hs - hs0) & 1);
     // the last half-step reloads itself (into the unused buffer and registers)
-    const int64_t hn = hs + 1 < nhs ? hs + 1 : hs;
+    const int64_t hn = hs + 1 < hs1 ? hs + 1 : hs;
     w_load(hn, nxt);
     const uint8_t* abuf = lds + h * kAHalfBytes + c * 256;
     half8_t af[RB];
@@ -1345,6 +1354,31 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
     return;
   }
+  if constexpr (SPLIT) {
+    // raw partial sums of this split's k range, float32 [M, N] per split
+    GemmArgs q = p;
+    q.out = p.ws + (int64_t)split * p.M * p.N;
+    q.out_bf16 = false;
+    q.ld_out = p.N;
+    const float one[CB] = {1.0f, 1.0f};
+    if ((p.N & 7) == 0) {
+      store_block_vec<RB>(q, lds, acc, one, row0, row1, n0 + wave * CB * 32, wave, lane);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t n = n0 + (wave * CB + cb) * 32 + c;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int64_t m = row0 + rb * 32 + acc32_row(i, kh);
+            if (m < row1) store_out(q, m, n, acc[rb][cb][i]);
+          }
+      }
+    }
+    return;
+  }
   const float a_gs = *p.a_gs;
   if (((uintptr_t)p.out & 15) == 0 && (p.ld_out & 7) == 0 && (p.N & 7) == 0) {
     float alpha[CB];
@@ -1371,13 +1405,17 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   }
 }
 
-template <bool FUSE>
+// SPLIT: the grid is splits x tiles (split-major); each split sums its k
+// range into the float32 workspace (splitk_reduce adds the ranges in order).
+template <bool FUSE, bool SPLIT = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tiles = SPLIT ? gridDim.x / p.splits : gridDim.x;
+  const int split = SPLIT ? (int)(blockIdx.x / tiles) : 0;
   int64_t slot, nt;
-  xcd_tile(blockIdx.x, n_tiles, slot, nt);
+  xcd_tile((int64_t)blockIdx.x - split * tiles, n_tiles, slot, nt);
   int g;
   int64_t row0, row1;
   if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG, kBigMinLast, 0, 0, g, row0, row1)) return;
@@ -1386,7 +1424,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
   row1 = __builtin_amdgcn_readfirstlane((int)row1);
   const int64_t n0 = nt * BIG;
   const int64_t rows = row1 - row0;
-  if constexpr (kBigMinLast > 128) {
+  if constexpr (SPLIT) {
+    const int64_t nks = p.K / 256;
+    big_dq_tile<8, false, true>(p, lds, g, row0, row1, n0, wave, lane, 2 * (nks * split / p.splits),
+                                2 * (nks * (split + 1) / p.splits), split);
+  } else if constexpr (kBigMinLast > 128) {
     big_dq_tile<8, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
   } else {
     if (rows > 128)
@@ -1431,6 +1473,20 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int64_t n_tiles = (a.N + BIG - 1) / BIG;
     const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
+    if constexpr (!FUSE) {
+      if (dq && a.splits > 1 && a.ws) {
+        // one group with fewer tiles than compute units: K split, the
+        // partial sums reduced in order (only the rows of these tiles: the
+        // left-over rows are already in out)
+        hipLaunchKernelGGL((gemm_big32_dq<false, true>), dim3((unsigned)(slots * n_tiles * a.splits)),
+                           dim3(kBigThreads), 0, s, a, n_tiles);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a,
+                           BIG, kBigMinLast);
+        return hipGetLastError();
+      }
+    }
     if (dq)
       hipLaunchKernelGGL(gemm_big32_dq<FUSE>, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a,
                          n_tiles);
@@ -1452,7 +1508,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
                            dim3(256), 0, s, a, n_tiles, 0, 0, work);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a, 0, 0);
       return hipGetLastError();
     }
   }
@@ -1463,7 +1519,17 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled) {
   // the streaming path with fewer than 512 workgroups (two per compute unit)
   // splits K; the reduction's grid has one row per block
-  if (!tiled || M < 1 || M > 65535 || K % 256 || gemm_uses_big_tiles(G, M, tiled)) return 1;
+  if (!tiled || M < 1 || M > 65535 || K % 256) return 1;
+  if (gemm_uses_big_tiles(G, M, tiled)) {
+    // one group whose 256-row tiles would leave half the compute units idle
+    // or more: about 256 workgroups over k ranges of at least one 256-k
+    // step (used with the f16 form of A only)
+    if (G != 1) return 1;
+    const int64_t tiles = ((M + BIG - 1) / BIG) * ((N + BIG - 1) / BIG);
+    if (tiles > 128) return 1;
+    const int64_t sp = std::min<int64_t>(std::min<int64_t>(256 / tiles, K / 256), 8);
+    return sp > 1 ? (int32_t)sp : 1;
+  }
   const int64_t base = ((M + 31) / 32 + G) * ((N + 255) / 256);
   if (base >= 512) return 1;
   // ranges of at most two 256-k steps where 16 of them cover K (the
