@@ -27,7 +27,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       float v[8];
       const char* p = (const char*)y + (row * H + c) * kElem;
       if constexpr (kBf16) {
-        const uint4 q = *(const uint4*)p;
+        // each row of y is read once: non-temporal load
+        typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+        const u32x4n q = __builtin_nontemporal_load((const u32x4n*)p);
         const uint32_t q4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -562,7 +562,12 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
 // and no barriers.  With skip_bm > 0
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
-template <int NBW, int RB, bool FUSE, bool SPLIT>
+// NT: the tile holds every row of its group, so each weight byte it streams
+// is read once in the launch; those loads carry the non-temporal hint, which
+// reaches a higher share of the HBM bandwidth than ordinary loads on this chip
+// (where several tiles of a group read the same weights, ordinary loads keep
+// the repeats in the caches)
+template <int NBW, int RB, bool FUSE, bool SPLIT, bool NT>
 __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
                                               int wave, int lane, int64_t ks0, int64_t ks1, int split) {
   static_assert(!FUSE || NBW == 2, "the fused epilogue pairs one gate and one up column block");
@@ -626,9 +631,18 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
       const uint8_t* t = w_t[cb] + ks * kTileBytes;
-      d.w0[cb] = *(const u32x4*)(t + 2048 * h + 16 * lane);
-      d.w1[cb] = *(const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
-      d.ws[cb] = *(const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+      const u32x4* t0 = (const u32x4*)(t + 2048 * h + 16 * lane);
+      const u32x4* t1 = (const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
+      const uint32_t* ts = (const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
+      if constexpr (NT) {
+        d.w0[cb] = __builtin_nontemporal_load(t0);
+        d.w1[cb] = __builtin_nontemporal_load(t1);
+        d.ws[cb] = __builtin_nontemporal_load(ts);
+      } else {
+        d.w0[cb] = *t0;
+        d.w1[cb] = *t1;
+        d.ws[cb] = *ts;
+      }
     }
   };
   auto compute = [&](const Ops& o) {
@@ -732,7 +746,10 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
     int64_t row0, row1;
     if (!find_tile(s_off, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)) return;
     g = __builtin_amdgcn_readfirstlane(g);
-    stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+    if (row0 == s_off[g] && row1 == s_off[g + 1])
+      stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+    else
+      stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
   } else {
     // tiles t0, t0 + grid, ... below `total`; slots grow with t, and the
     // tiles that exist come first, so the first missing one ends the loop
@@ -747,7 +764,10 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
       // hoisted out of the loop and kept live across tiles
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      stream32_tile<NBW, RB, FUSE, SPLIT>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
+      if (row0 == s_off[g] && row1 == s_off[g + 1])
+        stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
+      else
+        stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
     }
   }
 }
