@@ -45,6 +45,21 @@ __device__ __forceinline__ T clampv(T v, T lo, T hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP adds: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside the
+// row add 0), then the last lane of row 0 (of row 2) is added to row 1 (row 3),
+// and lane 31 to rows 2 and 3.  No local-memory round trips, unlike a
+// shuffle-based scan.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // The `slot`-th row tile of a launch.  Every group g (rows [lo, hi) from the
 // device offsets) contributes the rows [start, hi): start = lo, or, when
 // skip_bm > 0, the rows another launch leaves over, which tiles skip_bm rows
@@ -73,25 +88,21 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       }
       tiles = (int32_t)((hi - lo) / bm + ((hi - lo) % bm >= last_min ? 1 : 0));
     }
-    int32_t incl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const int32_t incl = wave_incl_scan(tiles);
     const int32_t excl = incl - tiles;
-    const int32_t total = __shfl(incl, 63, 64);
+    const int32_t total = __builtin_amdgcn_readlane(incl, 63);
     if (slot < base + total) {
       const bool mine = g < G && slot >= base + excl && slot < base + incl;
       const uint64_t mask = __ballot(mine);
-      const int src = __ffsll((unsigned long long)mask) - 1;
-      g_out = __shfl(g, src, 64);
-      const int32_t lo_s = __shfl((int32_t)lo, src, 64);
-      const int32_t hi_s = __shfl((int32_t)hi, src, 64);
-      const int32_t ex_s = __shfl(excl, src, 64);
+      if (mask == 0) return false;   // (cannot happen: some lane's range holds the slot)
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)mask) - 1);
+      g_out = __builtin_amdgcn_readlane(g, src);
+      const int32_t lo_s = __builtin_amdgcn_readlane((int32_t)lo, src);
+      const int32_t hi_s = __builtin_amdgcn_readlane((int32_t)hi, src);
+      const int32_t ex_s = __builtin_amdgcn_readlane(excl, src);
       r0 = lo_s + (slot - base - ex_s) * bm;
       r1 = r0 + bm < hi_s ? r0 + bm : hi_s;
-      return true;
+      return r0 < r1;
     }
     base += total;
   }
@@ -137,25 +148,21 @@ __device__ __forceinline__ bool find_tile_batched(const int32_t* __restrict__ of
       }
       tiles = (int32_t)((hi - lo) / bm + ((hi - lo) % bm >= last_min ? 1 : 0));
     }
-    int32_t incl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const int32_t incl = wave_incl_scan(tiles);
     const int32_t excl = incl - tiles;
-    const int32_t total = __shfl(incl, 63, 64);
+    const int32_t total = __builtin_amdgcn_readlane(incl, 63);
     if (slot < base + total) {
       const bool mine = g < G && slot >= base + excl && slot < base + incl;
       const uint64_t mask = __ballot(mine);
-      const int src = __ffsll((unsigned long long)mask) - 1;
-      g_out = __shfl(g, src, 64);
-      const int32_t lo_s = __shfl((int32_t)lo, src, 64);
-      const int32_t hi_s = __shfl((int32_t)hi, src, 64);
-      const int32_t ex_s = __shfl(excl, src, 64);
+      if (mask == 0) return false;   // (cannot happen: some lane's range holds the slot)
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)mask) - 1);
+      g_out = __builtin_amdgcn_readlane(g, src);
+      const int32_t lo_s = __builtin_amdgcn_readlane((int32_t)lo, src);
+      const int32_t hi_s = __builtin_amdgcn_readlane((int32_t)hi, src);
+      const int32_t ex_s = __builtin_amdgcn_readlane(excl, src);
       r0 = lo_s + (slot - base - ex_s) * bm;
       r1 = r0 + bm < hi_s ? r0 + bm : hi_s;
-      return true;
+      return r0 < r1;
     }
     base += total;
   }
