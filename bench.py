@@ -379,6 +379,75 @@ def run_shared(steps, warmup):
     return side_line("shared expert: T=%d, %d -> 2x%d -> %d, one group" % (T, H, I, H), ms, p10, p90, flops, bytes_)
 
 
+def time_eager(step, steps, warmup):
+    """ms per step of `steps` back-to-back eager steps (HIP events around
+    the whole run), after `warmup` untimed ones."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_decode_shared(steps, warmup):
+    """The decode layer with one shared expert (7168 -> 2x3072 -> 7168):
+    folded in as group 384 of both grouped GEMMs (every token visits it with
+    weight 1, added after the routed slots in the combine), against the
+    routed layer followed by the shared expert on its own (one-group GEMMs
+    with split K), on the same weights (group-range views of one stack) and
+    the same activation global scales."""
+    import torch
+    from block_scaled_fp4_03_amd import ops, pipeline, workloads
+    wl = workloads.WORKLOADS["decode"]
+    dev = torch.device("cuda:0")
+    E, k = wl.E, wl.k
+    w1, w2 = pipeline.moe_weights(wl, dev, drop_rows=True, n_shared=1)
+    b = workloads.batch(wl)
+    x = b["x"].to(dev, torch.bfloat16)
+    logits = b["logits"].to(dev)
+    warm = workloads.warmup_batch(wl)
+    xw = warm["x"].to(dev, torch.bfloat16)
+    gs_x = ops.global_scale(xw.reshape(1, -1))
+    xc, xs = ops.quantize(xw, gs_x)
+    _, _, off, srt, _ = ops.route_permute(warm["logits"].to(dev), k, n_shared=1)
+    gs_h = ops.silu_mul_global_scale(w1.gemm(xc, xs, gs_x, off, xw.shape[0] * (k + 1), a_row_index=srt))
+    w1r, w2r, w1s, w2s = w1.groups(0, E), w2.groups(0, E), w1.groups(E, E + 1), w2.groups(E, E + 1)
+
+    def folded():
+        return pipeline.moe_layer(x, logits, k, w1, w2, gs_x, gs_h, n_shared=1)
+
+    def separate():
+        pipeline.moe_layer(x, logits, k, w1r, w2r, gs_x, gs_h)
+        return pipeline.shared_expert(x, w1s, w2s, gs_x, gs_h)
+
+    tf, ts = [], []
+    for _ in range(2):                   # alternated, against drift of the clock
+        tf.append(time_eager(folded, steps, warmup))
+        ts.append(time_eager(separate, steps, warmup))
+    out, st = pipeline.moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=True, n_shared=1)
+    n_touched = int((np.diff(st["offsets"].cpu().numpy()[:E + 1]) > 0).sum())
+    ms_f, ms_s = float(np.median(tf)), float(np.median(ts))
+    T, H, I = wl.T, wl.H, wl.I
+    flops = 6.0 * T * (k + 1) * H * I
+    bytes_ = (n_touched + 1) * 3 * H * I * NVFP4_BYTES_PER_ELEM + T * H * 2 * 2 + T * E * 4
+    del w1, w2, w1r, w2r, w1s, w2s
+    return {"workload": "decode MoE layer + 1 shared expert: T=%d, %d routed experts top-%d, shared expert "
+                        "folded in as group %d" % (T, E, k, E),
+            "ms_per_step": round(ms_f, 4), "tokens_per_s": round(T / (ms_f * 1e-3), 1),
+            "tflops": round(flops / (ms_f * 1e-3) / 1e12, 2),
+            "gbs": round(bytes_ / (ms_f * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(bytes_ / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "separate_ms_per_step": round(ms_s, 4),
+            "separate": "routed layer, then the shared expert's own one-group GEMMs (split K)",
+            "experts_touched": n_touched, "algorithmic_bytes": int(bytes_)}
+
+
 def run_mla(steps, warmup):
     """MLA projections, T=4096: fused q_a+kv (dual gs), then q_b."""
     import torch
@@ -526,6 +595,9 @@ def main():
         line["mla_projections"] = run_mla(args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["attention_output"] = run_attn_out(args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        print("[bench] decode layer with the shared expert folded in", file=sys.stderr, flush=True)
+        line["decode_with_shared_expert"] = run_decode_shared(args.steps, args.warmup)
     print(json.dumps(line), flush=True)
 
 

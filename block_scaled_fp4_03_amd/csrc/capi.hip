@@ -100,26 +100,42 @@ int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_
                 s);
 }
 
+static int32_t route_permute(const char* who, const float* logits, int64_t T, int32_t E, int32_t k,
+                             int32_t ns, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                             int32_t* sorted_token_ids, int32_t* inv_perm, void* stream) {
+  if (T < 0) return fail(NVFP4_ESHAPE, "%s: T < 0", who);
+  if (E < 1 || E > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: E=%d outside [1, %d]", who, E, NVFP4_MAX_EXPERTS);
+  if (k < 1 || k > E || k > NVFP4_MAX_TOPK)
+    return fail(NVFP4_ESHAPE, "%s: k=%d outside [1, min(E, %d)]", who, k, NVFP4_MAX_TOPK);
+  if (ns < 0 || k + ns > NVFP4_MAX_TOPK || E + ns > NVFP4_MAX_EXPERTS)
+    return fail(NVFP4_ESHAPE, "%s: n_shared=%d: need n_shared >= 0, k + n_shared <= %d and E + n_shared <= %d", who,
+                ns, NVFP4_MAX_TOPK, NVFP4_MAX_EXPERTS);
+  if (T * (int64_t)(k + ns) >= ((int64_t)1 << 31)) return fail(NVFP4_ESHAPE, "%s: T*(k+n_shared) >= 2^31", who);
+  if (!expert_offsets) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_token_ids || !inv_perm))
+    return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_token_ids, 4) || !aligned(inv_perm, 4))
+    return fail(NVFP4_EALIGN, "%s: arrays must be 4-byte aligned", who);
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who,
+                nvfp4::launch_route_permute(logits, T, E, k, ns, topk_ids, topk_w, expert_offsets,
+                                            sorted_token_ids, inv_perm, s),
+                s);
+}
+
 int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
                           float* topk_w, int32_t* expert_offsets, int32_t* sorted_token_ids,
                           int32_t* inv_perm, void* stream) {
-  if (T < 0) return fail(NVFP4_ESHAPE, "moe_route_permute: T < 0");
-  if (E < 1 || E > NVFP4_MAX_EXPERTS)
-    return fail(NVFP4_ESHAPE, "moe_route_permute: E=%d outside [1, %d]", E, NVFP4_MAX_EXPERTS);
-  if (k < 1 || k > E || k > NVFP4_MAX_TOPK)
-    return fail(NVFP4_ESHAPE, "moe_route_permute: k=%d outside [1, min(E, %d)]", k, NVFP4_MAX_TOPK);
-  if (T * (int64_t)k >= ((int64_t)1 << 31)) return fail(NVFP4_ESHAPE, "moe_route_permute: T*k >= 2^31");
-  if (!expert_offsets) return fail(NVFP4_EINVAL, "moe_route_permute: null pointer");
-  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_token_ids || !inv_perm))
-    return fail(NVFP4_EINVAL, "moe_route_permute: null pointer");
-  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_offsets, 4) ||
-      !aligned(sorted_token_ids, 4) || !aligned(inv_perm, 4))
-    return fail(NVFP4_EALIGN, "moe_route_permute: arrays must be 4-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  return finish("moe_route_permute",
-                nvfp4::launch_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets,
-                                            sorted_token_ids, inv_perm, s),
-                s);
+  return route_permute("moe_route_permute", logits, T, E, k, 0, topk_ids, topk_w, expert_offsets,
+                       sorted_token_ids, inv_perm, stream);
+}
+
+int32_t moe_route_permute_shared(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_shared,
+                                 int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                 int32_t* sorted_token_ids, int32_t* inv_perm, void* stream) {
+  return route_permute("moe_route_permute_shared", logits, T, E, k, n_shared, topk_ids, topk_w, expert_offsets,
+                       sorted_token_ids, inv_perm, stream);
 }
 
 int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,

@@ -50,9 +50,8 @@ int64_t amax_chunks(int64_t n);
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride,
                                float* gs_out, float* partial, hipStream_t s);
 
-hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int32_t* ids,
-                                float* w, int32_t* offsets, int32_t* sorted_ids, int32_t* inv,
-                                hipStream_t s);
+hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int ns, int32_t* ids,
+                                float* w, int32_t* offsets, int32_t* sorted_ids, int32_t* inv, hipStream_t s);
 
 int64_t prepared_bytes(int64_t G, int64_t N, int64_t K);
 hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int64_t G, int64_t N, int64_t K,

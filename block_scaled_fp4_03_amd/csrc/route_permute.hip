@@ -11,8 +11,10 @@ constexpr int kMaxPerLane = 16;   // 64 lanes x 16 = NVFP4_MAX_EXPERTS logits pe
 // logit, or an equal logit with a lower expert id, so the selection does not
 // depend on evaluation order.  Lane 0 then forms the softmax over the k
 // selected logits in slot order.
+// ns > 0: each token's row of ids/w has k + ns slots; slots k .. k+ns-1 are
+// the always-on shared experts E .. E+ns-1 with weight 1.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
-                                                   int k, int32_t* __restrict__ ids,
+                                                   int k, int ns, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -60,9 +62,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       e[j] = exp_f32(sel_val[j] - sel_val[0]);
       total = j == 0 ? e[0] : total + e[j];
     }
+    const int kk = k + ns;
     for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = sel_id[j];
-      w[t * k + j] = e[j] / total;
+      ids[t * kk + j] = sel_id[j];
+      w[t * kk + j] = e[j] / total;
+    }
+    for (int j = 0; j < ns; ++j) {
+      ids[t * kk + k + j] = E + j;
+      w[t * kk + k + j] = 1.0f;
     }
   }
 }
@@ -134,17 +141,20 @@ __global__ void zero_offsets_kernel(int32_t* offsets, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) offsets[i] = 0;
 }
 
-hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, int ns, int32_t* ids, float* w,
                                 int32_t* offsets, int32_t* sorted_ids, int32_t* inv, hipStream_t s) {
+  // the shared experts are groups E .. E+ns-1 of the permutation, each
+  // token's slots k .. k+ns-1
+  const int G = E + ns, kk = k + ns;
   if (T == 0) {
-    hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, E + 1);
+    hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, G + 1);
     return hipGetLastError();
   }
   const int64_t blocks = (T + 3) / 4;      // 4 tokens (waves) per block
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(256), 0, s, logits, T, E, k, ids, w);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(256), 0, s, logits, T, E, k, ns, ids, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)E), dim3(kPermThreads), 0, s, ids, T * k, k, E,
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)G), dim3(kPermThreads), 0, s, ids, T * kk, kk, G,
                      offsets, sorted_ids, inv);
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ SIGNATURES = {
     "nvfp4_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "moe_route_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "moe_route_permute_shared": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,
                                   _P, _I32, _I64, _I64, _I64, _P, _I32, _I64, _P, _SZ, _P]),
     "nvfp4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),

@@ -81,21 +81,28 @@ def global_scale(x, out=None):
     return out
 
 
-def route_permute(logits, k):
-    """logits [T, E] f32 -> (ids [T,k] i32, w [T,k] f32, offsets [E+1] i32,
-    sorted_token_ids [T*k] i32, inv [T,k] i32)."""
+def route_permute(logits, k, n_shared=0):
+    """logits [T, E] f32 -> (ids [T,kk] i32, w [T,kk] f32, offsets [E+n_shared+1] i32,
+    sorted_token_ids [T*kk] i32, inv [T,kk] i32) with kk = k + n_shared: the
+    k routed slots, then n_shared always-on shared experts E, E+1, ... with
+    weight 1 (moe_route_permute_shared; n_shared = 0 is moe_route_permute)."""
     _check_dev(logits)
     if logits.dtype != torch.float32 or not logits.is_contiguous():
         raise ValueError("logits must be contiguous float32")
     T, E = logits.shape
+    kk = k + n_shared
     dev = logits.device
-    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
-    w = torch.empty(T, k, dtype=torch.float32, device=dev)
-    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sorted_ids = torch.empty(T * k, dtype=torch.int32, device=dev)
-    inv = torch.empty(T, k, dtype=torch.int32, device=dev)
-    _lib.call("moe_route_permute", _p(logits), T, E, k, _p(ids), _p(w), _p(off), _p(sorted_ids),
-              _p(inv), _stream())
+    ids = torch.empty(T, kk, dtype=torch.int32, device=dev)
+    w = torch.empty(T, kk, dtype=torch.float32, device=dev)
+    off = torch.empty(E + n_shared + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(T * kk, dtype=torch.int32, device=dev)
+    inv = torch.empty(T, kk, dtype=torch.int32, device=dev)
+    if n_shared:
+        _lib.call("moe_route_permute_shared", _p(logits), T, E, k, n_shared, _p(ids), _p(w), _p(off),
+                  _p(sorted_ids), _p(inv), _stream())
+    else:
+        _lib.call("moe_route_permute", _p(logits), T, E, k, _p(ids), _p(w), _p(off), _p(sorted_ids),
+                  _p(inv), _stream())
     return ids, w, off, sorted_ids, inv
 
 

@@ -4,7 +4,8 @@
   stacked gate_up weights (gate and up with their own global scales) ->
   SiLU(gate)*up re-quantised -> L2 grouped GEMM over the down weights (bf16
   out) -> weighted combine (bf16);
-* shared expert: the same with one group and no routing or combine;
+* shared expert: the same with one group and no routing or combine, or
+  folded into the routed layer as an always-on extra group;
 * MLA projections: one-group GEMMs, the fused q_a+kv weight with two global
   scales, then q_b.
 Every step is one call into libnvfp4moe.so; torch only provides the buffers
@@ -45,6 +46,18 @@ class NVFP4Weights:
                 self.codes = torch.empty(self.codes.shape, dtype=torch.uint8, device="meta")
                 self.scales = torch.empty(self.scales.shape, dtype=torch.uint8, device="meta")
         return self
+
+    def groups(self, g0, g1):
+        """Groups [g0, g1) as a view (no copy): the tiled layout stores the
+        groups one after another, so a range of groups is one slice of it."""
+        G, N, K2 = self.codes.shape
+        if not 0 <= g0 < g1 <= G:
+            raise ValueError("groups [%d, %d) outside [0, %d)" % (g0, g1, G))
+        tiled = None
+        if self.tiled is not None:
+            per = ops.prepared_weight_bytes(1, N, 2 * K2)
+            tiled = self.tiled[g0 * per:g1 * per]
+        return NVFP4Weights(self.codes[g0:g1], self.scales[g0:g1], self.gs[g0:g1], self.n_seg, tiled)
 
     def reads_dq(self, M, a_rows):
         """Whether a GEMM of M rows (A stored in a_rows rows) reads A's f16 form."""
@@ -97,12 +110,14 @@ def quantize_stack(mats, n_seg, device):
     return NVFP4Weights(codes, scales, gs, tuple(n_seg)).prepare()
 
 
-def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False):
+def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False, n_shared=0):
     """(W1, W2) of a routed workload: W1 stacked gate_up [E, 2I, H] with
     segments (gate, up), W2 down [E, H, I].  Drawn expert by expert on
     `device` and quantised there; with `tiled`, also rearranged for the GEMM
-    (and with `drop_rows` the row-major copies are released)."""
-    E = wl.E if experts is None else experts
+    (and with `drop_rows` the row-major copies are released).  With
+    n_shared, the stacks hold E + n_shared groups: the shared experts are
+    groups E, E+1, ... (drawn as experts E, E+1, ... of the same seed)."""
+    E = (wl.E if experts is None else experts) + n_shared
     I, H = wl.I, wl.H
     gen_dev = device if wl.weights_on_device else "cpu"
     w1 = NVFP4Weights(torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=device),
@@ -152,7 +167,7 @@ def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xd
     return y, st
 
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None):
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared=0):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
     1-element f32 tensors: static activation global scales (from a warmup
     batch), or None for dynamic ones computed on the device from this batch
@@ -160,15 +175,23 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None):
     between the two GEMMs; the host never waits for them).  `fused` runs
     SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant),
     None chooses by the first GEMM's kernel (see _expert_mlp); the results
-    are identical either way.  Returns out [T, H] bf16 (and the stages)."""
+    are identical either way.  With n_shared, w1/w2 also hold that many
+    shared experts as their last groups: every token visits them with weight
+    1 (moe_route_permute_shared), so one grouped GEMM per projection covers
+    the routed and the shared experts, and the combine adds the shared
+    outputs after the routed slots.  Returns out [T, H] bf16 (and the
+    stages)."""
     T, H = x.shape
-    R = T * k
+    if w1.codes.shape[0] != logits.shape[1] + n_shared:
+        raise ValueError("w1 holds %d groups; expected %d routed + %d shared" %
+                         (w1.codes.shape[0], logits.shape[1], n_shared))
+    R = T * (k + n_shared)
     if gs_x is None:
         gs_x = ops.global_scale(x.reshape(1, -1))
     # the many-row GEMM tiles read A in exactly dequantised f16 form, which the
     # producers write alongside the codes when it will be read
     xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) else None)
-    ids, w, off, sorted_ids, inv = ops.route_permute(logits, k)
+    ids, w, off, sorted_ids, inv = ops.route_permute(logits, k, n_shared)
     y, st = _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, T, a_row_index=sorted_ids,
                         xdq=xdq[0] if xdq else None, fused=fused)
     out = ops.combine(y, inv, w)

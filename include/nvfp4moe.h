@@ -156,6 +156,33 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                           int32_t* sorted_token_ids, int32_t* inv_perm, void* stream);
 
 /*
+ * moe_route_permute_shared - moe_route_permute with n_shared always-on
+ * shared experts folded in as extra groups, so that one grouped GEMM per
+ * projection covers the routed and the shared experts of a layer.  The page
+ * "Current Bug: vLLM produces empty/garbage output" (e8b289e, section
+ * "Phase 1: CuTeDSL Shared Expert Kernel") describes a shared expert as an
+ * MoE of one expert without routing, run by the same grouped kernel; here it
+ * is one more expert that every token visits with weight 1.
+ *   Each token has kk = k + n_shared slots: slots 0 .. k-1 exactly as
+ *   moe_route_permute (ids, softmax weights over the k selected logits);
+ *   slot k + s holds expert id E + s with weight 1.0f.
+ *   topk_ids, topk_w, inv_perm   out [T, kk].
+ *   expert_offsets               out [E + n_shared + 1]: groups 0 .. E-1 are
+ *                                the routed experts, group E + s the shared
+ *                                expert s (T rows, tokens in order).
+ *   sorted_token_ids             out [T*kk], expert-major, flat index t*kk + j
+ *                                within a group.
+ * moe_combine over kk slots then adds each shared expert's output with weight
+ * 1 after the routed slots, in slot order.  n_shared = 0 is moe_route_permute.
+ * Errors: those of moe_route_permute, and ESHAPE unless n_shared >= 0,
+ * k + n_shared <= NVFP4_MAX_TOPK, E + n_shared <= NVFP4_MAX_EXPERTS,
+ * T*kk < 2^31.
+ */
+int32_t moe_route_permute_shared(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_shared,
+                                 int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                 int32_t* sorted_token_ids, int32_t* inv_perm, void* stream);
+
+/*
  * nvfp4_grouped_gemm - grouped GEMM of two NVFP4 operands.
  *   For every group g and every row m in [group_offsets[g], group_offsets[g+1]):
  *     out[m, n] = alpha(g, n) * sum_k A[m, k] * W[g, n, k]

@@ -36,6 +36,12 @@ Readings where the pages are silent (each listed in the design notes):
   rounding happens before the re-quantisation.
 * combine: acc = w_0*y_0, then acc = acc + w_j*y_j for j = 1..k-1, each a
   separate float32 operation, then one rounding to bf16.
+* shared experts folded into the routed layer: a shared expert is an MoE of
+  one expert without routing ("Current Bug: vLLM produces empty/garbage
+  output" @e8b289e, section "Phase 1: CuTeDSL Shared Expert Kernel"); folded
+  in, it is one more expert (id E, E+1, ...) that every token visits, in the
+  slots after its k routed ones, with weight 1, so the combine adds its
+  output after the routed ones.
 """
 import numpy as np
 
@@ -69,6 +75,15 @@ def route_topk(logits, k):
         total = (total + e[:, j]).astype(F32)
     w = (e / total[:, None]).astype(F32)
     return ids, w
+
+
+def append_shared(ids, w, E, n_shared):
+    """Routed (ids, w) [T, k] -> [T, k + n_shared]: slot k + s holds the
+    always-on shared expert E + s with weight 1."""
+    T = ids.shape[0]
+    sid = np.broadcast_to(np.arange(E, E + n_shared, dtype=np.int32), (T, n_shared))
+    return (np.concatenate([ids, sid], axis=1).astype(np.int32),
+            np.concatenate([w, np.ones((T, n_shared), dtype=F32)], axis=1).astype(F32))
 
 
 def permute(ids, E):
@@ -174,21 +189,27 @@ def combine(y, inv, w):
 
 # --- compositions --------------------------------------------------------------
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=False):
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=False, n_shared=0):
     """The routed MoE layer.
 
     x float32 [T, H] (bf16 values); logits float32 [T, E];
     w1 = (codes [E, 2I, H/2], scales [E, 2I, H/16], gs [E, 2]) gate rows first;
     w2 = (codes [E, H, I/2], scales [E, H, I/16], gs [E, 1]).
+    With n_shared, w1 and w2 hold E + n_shared experts, the last n_shared
+    being shared experts folded in (see append_shared).
     Returns out float32 [T, H] holding bf16 values (and the stages if asked).
     """
     T, H = x.shape
     E = logits.shape[1]
     I2 = w1[0].shape[1]
     I = I2 // 2
+    if w1[0].shape[0] != E + n_shared or w2[0].shape[0] != E + n_shared:
+        raise ValueError("weights must hold E + n_shared experts")
     xq = quantize(x, gs_x)
     ids, wts = route_topk(logits, k)
-    offsets, sorted_ids, inv = permute(ids, E)
+    if n_shared:
+        ids, wts = append_shared(ids, wts, E, n_shared)
+    offsets, sorted_ids, inv = permute(ids, E + n_shared)
     gu = grouped_gemm(xq[0], xq[1], gs_x, w1[0], w1[1], w1[2], [0, I, I2],
                       offsets, a_row_index=sorted_ids, out_dtype="f32")
     h = silu_mul(gu)

@@ -71,6 +71,17 @@ def test_route_validation(L):
     assert f(FAKE, 4, 8, 2, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == lib.EINVAL
 
 
+def test_route_shared_validation(L):
+    f = L.moe_route_permute_shared
+    assert f(FAKE, 4, 8, 2, -1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE
+    assert "n_shared" in _err(L)
+    assert f(FAKE, 4, 8, 2, 15, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE      # k + n_shared > 16
+    assert f(FAKE, 4, 1020, 6, 5, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE    # E + n_shared > 1024
+    assert f(FAKE, 4, 8, 9, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.ESHAPE       # the routed k > E
+    assert f(FAKE, 4, 8, 2, 1, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == lib.EINVAL
+    assert f(ctypes.c_void_p(0x1002), 4, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == lib.EALIGN
+
+
 def _gemm(L, **kw):
     a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, a_dq=NULL, w_codes=FAKE,
              w_scales=FAKE, w_layout=lib.LAYOUT_ROWS, w_gs=FAKE, n_seg=[0, 64], group_offsets=FAKE, G=1,

@@ -117,6 +117,25 @@ def test_route_permute_bit_exact(T, E, k, zipf, ties):
     assert np.array_equal(to_np(inv), inv_r)
 
 
+@pytest.mark.parametrize("T,E,k,ns,ties", [(16, 8, 2, 1, False), (256, 384, 6, 1, False), (100, 384, 6, 2, True),
+                                           (5, 1, 1, 1, False), (3, 16, 15, 1, True), (1, 1022, 6, 2, False)])
+def test_route_permute_shared_bit_exact(T, E, k, ns, ties):
+    # the shared experts folded in: routed slots as without them, then slots
+    # k.. with ids E.. and weight 1; the permutation over E + ns groups
+    log("route shared", T, E, k, ns, ties)
+    lg = _route_case(T, E, k, T * 11 + E, 0.0, ties)
+    ids_r, w_r = moe.append_shared(*moe.route_topk(lg, k), E, ns)
+    off_r, srt_r, inv_r = moe.permute(ids_r, E + ns)
+    ids, w, off, srt, inv = ops.route_permute(torch.from_numpy(lg).to(dev()), k, n_shared=ns)
+    assert np.array_equal(to_np(ids), ids_r)
+    assert np.array_equal(to_np(w).view(np.uint32), w_r.view(np.uint32))
+    assert np.array_equal(to_np(off), off_r)
+    assert np.array_equal(to_np(srt), srt_r)
+    assert np.array_equal(to_np(inv), inv_r)
+    _, _, off0, _, _ = ops.route_permute(torch.empty(0, E, device=dev()), k, n_shared=ns)
+    assert off0.shape == (E + ns + 1,) and (to_np(off0) == 0).all()
+
+
 def test_route_permute_empty_batch():
     ids, w, off, srt, inv = ops.route_permute(torch.empty(0, 8, device=dev()), 2)
     assert (to_np(off) == 0).all()

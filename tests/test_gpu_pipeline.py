@@ -91,12 +91,12 @@ def _fused_same(unfused, fused):
                           o1.view(torch.int16).cpu().numpy())
 
 
-def _tiny_setup():
+def _tiny_setup(n_shared=0):
     wl = workloads.WORKLOADS["tiny"]
     d = dev()
-    w1, w2 = pipeline.moe_weights(wl, d)
-    ow = [_oracle_moe_expert(wl, e, "cpu") for e in range(wl.E)]
-    for e in range(wl.E):
+    w1, w2 = pipeline.moe_weights(wl, d, n_shared=n_shared)
+    ow = [_oracle_moe_expert(wl, e, "cpu") for e in range(wl.E + n_shared)]
+    for e in range(wl.E + n_shared):
         _check_weights(w1, e, ow[e][0])
         _check_weights(w2, e, ow[e][1])
     W1 = (np.stack([o[0][0] for o in ow]), np.stack([o[0][1] for o in ow]), np.stack([o[0][2] for o in ow]))
@@ -104,10 +104,11 @@ def _tiny_setup():
     return wl, d, w1, w2, ow, W1, W2
 
 
-def _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g):
+def _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g, n_shared=0):
     """Every stage of the GPU layer (out, stages g) against the oracle layer
     run with the same activation global scales."""
-    ref, st = moe.moe_layer(b["x"].numpy(), b["logits"].numpy(), wl.k, W1, W2, gs_x, gs_h, return_stages=True)
+    ref, st = moe.moe_layer(b["x"].numpy(), b["logits"].numpy(), wl.k, W1, W2, gs_x, gs_h, return_stages=True,
+                            n_shared=n_shared)
     assert np.array_equal(to_np(g["xc"]), st["xq"][0]) and np.array_equal(to_np(g["xs"]), st["xq"][1])
     for k_ in ("ids", "offsets", "sorted_ids", "inv"):
         assert np.array_equal(to_np(g[k_]), st[k_]), k_
@@ -115,7 +116,7 @@ def _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g):
     g_gu, g_hc, g_hs, g_y = to_np(g["gate_up"]), to_np(g["hc"]), to_np(g["hs"]), to_np(g["y"])
     off = st["offsets"]
     flips = 0
-    for e in range(wl.E):
+    for e in range(wl.E + n_shared):
         rows = np.arange(off[e], off[e + 1])
         if rows.size:
             flips += _expert_rows_check(wl, e, rows, st["sorted_ids"][rows], st["xq"], gs_x, gs_h, ow[e][0],
@@ -162,6 +163,35 @@ def test_tiny_layer_dynamic_activation_scales():
     assert gs_h == quant.global_scale(quant.amax(moe.silu_mul(to_np(g["gate_up"]))))
     c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g)
     log("  tiny dynamic: gs_x %.6g, gs_h %.6g, cosine %.7f, audited flips %d" % (gs_x, gs_h, c, flips))
+
+
+def test_tiny_layer_shared_expert_folded():
+    # one shared expert folded into the routed layer as group E (every token,
+    # weight 1, added after the routed slots): every stage against the oracle
+    # layer with the same fold, both SiLU-requant paths identical
+    log("pipeline tiny, shared expert folded in as group E")
+    wl, d, w1, w2, ow, W1, W2 = _tiny_setup(n_shared=1)
+    warm = workloads.warmup_batch(wl)
+    gs_x = quant.global_scale(quant.amax(warm["x"].numpy()))
+    _, wst = moe.moe_layer(warm["x"].numpy(), warm["logits"].numpy(), wl.k, W1, W2, gs_x, F32(1),
+                           return_stages=True, n_shared=1)
+    gs_h = quant.global_scale(quant.amax(wst["h"]))
+    b = workloads.batch(wl)
+    run = lambda fused: pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
+                                           torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
+                                           keep=True, fused=fused, n_shared=1)
+    out, g = run(False)
+    c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g, n_shared=1)
+    _fused_same((out, g), run(True))
+    assert to_np(g["offsets"])[wl.E + 1] - to_np(g["offsets"])[wl.E] == wl.T
+    # a group-range view of the stack is the routed experts' own stack
+    w1r, w2r = pipeline.moe_weights(wl, d)
+    args = (b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k)
+    scales = (torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d))
+    o_view = pipeline.moe_layer(*args, w1.groups(0, wl.E), w2.groups(0, wl.E), *scales)
+    o_own = pipeline.moe_layer(*args, w1r, w2r, *scales)
+    assert torch.equal(o_view, o_own)
+    log("  tiny + shared: cosine %.7f, max-abs/rms %.3g, audited flips %d" % (c, rel, flips))
 
 
 # --- shared expert: full size -----------------------------------------------------
@@ -269,11 +299,12 @@ def test_mla_projections_full_size():
 
 # --- routed layers at full size: sampled token, its experts, their rows ------------
 
-def _routed_full(name, max_rows_per_expert):
+def _routed_full(name, max_rows_per_expert, n_shared=0):
     wl = workloads.WORKLOADS[name]
     d = dev()
-    log("pipeline %s: T=%d, %d experts, top-%d; drawing and quantising weights" % (name, wl.T, wl.E, wl.k))
-    w1, w2 = pipeline.moe_weights(wl, d)
+    log("pipeline %s: T=%d, %d experts + %d shared, top-%d; drawing and quantising weights" % (
+        name, wl.T, wl.E, n_shared, wl.k))
+    w1, w2 = pipeline.moe_weights(wl, d, n_shared=n_shared)
     b = workloads.batch(wl)
     x, logits = b["x"].numpy(), b["logits"].numpy()
     warm = workloads.warmup_batch(wl)
@@ -281,7 +312,9 @@ def _routed_full(name, max_rows_per_expert):
     # routing and permutation: whole batch, bit-exact
     xq = quant.quantize(x, gs_x)
     ids, wts = moe.route_topk(logits, wl.k)
-    off, srt, inv = moe.permute(ids, wl.E)
+    if n_shared:
+        ids, wts = moe.append_shared(ids, wts, wl.E, n_shared)
+    off, srt, inv = moe.permute(ids, wl.E + n_shared)
     # the sampled token and its experts, quantised by the oracle
     t0 = 0
     experts = [int(e) for e in ids[t0]]
@@ -298,7 +331,7 @@ def _routed_full(name, max_rows_per_expert):
     gs_h = quant.global_scale(max(quant.amax(h) for h in hs_all))
     run = lambda fused: pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
                                            torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
-                                           keep=True, fused=fused)
+                                           keep=True, fused=fused, n_shared=n_shared)
     out, g = run(False)
     _fused_same((out, g), run(True))
     torch.cuda.synchronize()
@@ -322,9 +355,11 @@ def _routed_full(name, max_rows_per_expert):
     # the token's whole layer output from the oracle
     W1 = tuple(np.stack([ow[e][0][i] for e in experts]) for i in range(3))
     W2 = tuple(np.stack([ow[e][1][i] for e in experts]) for i in range(3))
-    # the token's logits restricted to its own experts, in slot order: routing
-    # over them reproduces the same slots and weights
-    ref = moe.moe_layer(x[t0:t0 + 1], logits[t0:t0 + 1, experts], wl.k, W1, W2, gs_x, gs_h)
+    # the token's logits restricted to its own routed experts, in slot order:
+    # routing over them reproduces the same slots and weights (the shared
+    # experts follow as the last groups)
+    ref = moe.moe_layer(x[t0:t0 + 1], logits[t0:t0 + 1, experts[:wl.k]], wl.k, W1, W2, gs_x, gs_h,
+                        n_shared=n_shared)
     o = to_np(out)[t0]
     c = cosine(o, ref[0])
     log("  %s: token %d cosine %.7f, audited flips %d, experts touched %d" % (
@@ -341,6 +376,12 @@ def test_decode_layer_full_size_sampled():
 
 def test_prefill_layer_full_size_sampled():
     _routed_full("prefill", max_rows_per_expert=24)
+
+
+def test_decode_layer_shared_expert_folded_full_size_sampled():
+    # the decode layer with one shared expert (7168 -> 2x3072 -> 7168) folded
+    # in as group 384: 385 groups per GEMM, 7 slots per token
+    _routed_full("decode", max_rows_per_expert=64, n_shared=1)
 
 
 # --- attention output path (wo_a FP8, wo_b NVFP4): full size, sampled ----------

@@ -1,5 +1,6 @@
 """End-to-end pins of the oracle pipeline on the tiny workload: a direct
-per-token loop with no permutation, the shared expert as the one-expert MoE,
+per-token loop with no permutation, the shared expert as the one-expert MoE
+and folded into the routed layer as an always-on group,
 the dual-scale fused projection as two separate projections, and the size of
 the quantisation error against an unquantised float64 layer."""
 import numpy as np
@@ -39,12 +40,14 @@ def _tiny():
     return wl, x, logits, w1, w2, w1f, w2f, gs_x, gs_h
 
 
-def test_tiny_layer_equals_per_token_loop():
-    wl, x, logits, w1, w2, _, _, gs_x, gs_h = _tiny()
-    out, st = moe.moe_layer(x, logits, wl.k, w1, w2, gs_x, gs_h, return_stages=True)
+def _per_token_acc(wl, x, logits, w1, w2, gs_x, gs_h):
+    """The routed layer's float32 accumulator per token (before the bf16
+    rounding of the combine), by a direct loop over each token's experts:
+    no permutation, no grouped GEMM."""
     T, H, I, k = wl.T, wl.H, wl.I, wl.k
     xq = quant.quantize(x, gs_x)
     xd = quant.dequantize_blocks(*xq)
+    accs = np.empty((T, H), dtype=np.float32)
     for t in range(T):
         order = sorted(range(wl.E), key=lambda e: (-float(logits[t, e]), e))[:k]
         sel = logits[t, order].astype(np.float32)
@@ -69,8 +72,53 @@ def test_tiny_layer_equals_per_token_loop():
             y = formats.bf16_round(((W2 @ hd) * float(a2)).astype(np.float32))
             p = (wts[j] * y).astype(np.float32)
             acc = p if acc is None else (acc + p).astype(np.float32)
-        ref = formats.bf16_round(acc)
-        assert np.array_equal(out[t], ref), t
+        accs[t] = acc
+    return accs
+
+
+def test_tiny_layer_equals_per_token_loop():
+    wl, x, logits, w1, w2, _, _, gs_x, gs_h = _tiny()
+    out = moe.moe_layer(x, logits, wl.k, w1, w2, gs_x, gs_h)
+    ref = formats.bf16_round(_per_token_acc(wl, x, logits, w1, w2, gs_x, gs_h))
+    for t in range(wl.T):
+        assert np.array_equal(out[t], ref[t]), t
+
+
+def _stack(a, b):
+    return tuple(np.concatenate([a[i], b[i]]) for i in range(3))
+
+
+def test_folded_shared_expert_equals_routed_plus_shared():
+    # the shared expert folded in as group E of the routed layer gives, per
+    # token, the routed accumulator plus the standalone shared expert's
+    # output (one-group GEMMs, no routing), added last, then one bf16
+    # rounding; its rows in the permuted order are the shared expert's own
+    wl, x, logits, w1, w2, _, _, gs_x, gs_h = _tiny()
+    I = wl.I
+    m1 = workloads.moe_gate_up(wl, wl.E).numpy()
+    gg, gu = quant.global_scale(quant.amax(m1[:I])), quant.global_scale(quant.amax(m1[I:]))
+    cg, sg = quant.quantize(m1[:I], gg)
+    cu, su = quant.quantize(m1[I:], gu)
+    w1s = (np.concatenate([cg, cu])[None], np.concatenate([sg, su])[None], np.array([[gg, gu]], np.float32))
+    c2, s2, g2 = moe.quantize_weight(workloads.moe_down(wl, wl.E).numpy())
+    w2s = (c2[None], s2[None], np.array([[g2]], np.float32))
+    y_shared = moe.shared_expert(x, w1s, w2s, gs_x, gs_h)
+    out, st = moe.moe_layer(x, logits, wl.k, _stack(w1, w1s), _stack(w2, w2s), gs_x, gs_h,
+                            return_stages=True, n_shared=1)
+    acc = _per_token_acc(wl, x, logits, w1, w2, gs_x, gs_h)
+    ref = formats.bf16_round((acc + y_shared).astype(np.float32))
+    assert np.array_equal(out, ref)
+    T, k = wl.T, wl.k
+    assert np.array_equal(st["ids"][:, k], np.full(T, wl.E)) and np.all(st["w"][:, k] == 1.0)
+    assert st["offsets"][wl.E + 1] - st["offsets"][wl.E] == T
+    rows = np.arange(st["offsets"][wl.E], st["offsets"][wl.E + 1])
+    assert np.array_equal(st["sorted_ids"][rows], np.arange(T))
+    assert np.array_equal(st["y"][rows], y_shared)
+    assert np.array_equal(st["inv"][:, k], rows)
+    # the routed part is the routed layer's own
+    _, st0 = moe.moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=True)
+    assert np.array_equal(st["ids"][:, :k], st0["ids"]) and np.array_equal(st["w"][:, :k], st0["w"])
+    assert np.array_equal(st["offsets"][:wl.E + 1], st0["offsets"])
 
 
 def test_shared_expert_is_moe_with_one_expert():
