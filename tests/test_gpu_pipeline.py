@@ -194,6 +194,49 @@ def test_tiny_layer_shared_expert_folded():
     log("  tiny + shared: cosine %.7f, max-abs/rms %.3g, audited flips %d" % (c, rel, flips))
 
 
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_tiny_layer_graph_replays_match_eager(n_shared):
+    # the routed layer (routing, permutation, both grouped GEMMs, SiLU-requant
+    # in either place, combine) captured in a HIP graph gives the eager output
+    # bit for bit on every replay, with eager work and synchronisation between
+    # the replays; the inputs are refilled in place before each replay
+    log("pipeline tiny: graph replays vs eager, n_shared=%d" % n_shared)
+    wl = workloads.WORKLOADS["tiny"]
+    d = dev()
+    w1, w2 = pipeline.moe_weights(wl, d, n_shared=n_shared)
+    b0, b1 = workloads.batch(wl, seed=0), workloads.batch(wl, seed=2)
+    x = b0["x"].to(d, torch.bfloat16)
+    logits = b0["logits"].to(d)
+    gs_x = ops.global_scale(x.reshape(1, -1))
+    gs_h = torch.tensor([0.01], dtype=torch.float32, device=d)
+    for fused in (False, True):
+        layer = lambda: pipeline.moe_layer(x, logits, wl.k, w1, w2, gs_x, gs_h, fused=fused, n_shared=n_shared)
+        refs = []
+        for bb in (b0, b1):
+            x.copy_(bb["x"].to(d, torch.bfloat16))
+            logits.copy_(bb["logits"].to(d))
+            refs.append(to_np(layer().view(torch.int16)))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            out = layer()
+        for r in range(4):
+            bb = (b0, b1)[r % 2]
+            x.copy_(bb["x"].to(d, torch.bfloat16))
+            logits.copy_(bb["logits"].to(d))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_np(out.view(torch.int16)), refs[r % 2]), "fused=%s replay %d" % (fused, r)
+            layer()                      # eager work between replays
+            torch.cuda.synchronize()
+        del graph
+
+
 # --- shared expert: full size -----------------------------------------------------
 
 def test_shared_expert_full_size():
