@@ -942,9 +942,10 @@ __device__ __forceinline__ void xcd_tile(int64_t bid, int64_t n_tiles, int64_t& 
 
 constexpr int BIG = 256;
 // with A in f16 form, the last tile of a group goes to the 256-row kernel
-// when it has at least this many rows (fewer: the streaming kernel, for
-// which a short tile's weight stream is not latency-bound)
-constexpr int kBigMinLast = 129;
+// when it has at least this many rows (65..128 rows: a 128-row tile), fewer
+// to the streaming kernel.  Measured on the prefill layer against 129, 97,
+// 81, 49 and 33: 65 was fastest (1.4-2% of the layer against 129)
+constexpr int kBigMinLast = 65;
 constexpr int kAHalfBytes = BIG * 256;           // 64 KiB per f16 half-tile
 constexpr int kBigThreads = 256;
 
