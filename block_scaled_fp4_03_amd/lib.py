@@ -54,6 +54,10 @@ def load():
     other implementation to fall back to."""
     global _lib
     if _lib is None:
+        # torch first: its HIP runtime is then the one the library binds to
+        # (loading the library first would bring a second runtime into the
+        # process, which torch's tensors are not visible to)
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("%s is not built; run __graft_entry__.build() or "
                                "python -m block_scaled_fp4_03_amd.build" % LIB_PATH)

@@ -195,6 +195,30 @@ def test_tiny_layer_shared_expert_folded():
 
 
 @pytest.mark.parametrize("n_shared", [0, 1])
+def test_tiny_layer_one_token_and_empty_batch(n_shared):
+    # one token: every stage against the oracle; no token: an empty output
+    # (the route writes zero offsets, the GEMMs and the combine do nothing)
+    log("pipeline tiny: T=1 and T=0, n_shared=%d" % n_shared)
+    wl, d, w1, w2, ow, W1, W2 = _tiny_setup(n_shared=n_shared)
+    b = workloads.batch(wl, seed=5, tokens=1)
+    gs_x = quant.global_scale(quant.amax(b["x"].numpy()))
+    _, st = moe.moe_layer(b["x"].numpy(), b["logits"].numpy(), wl.k, W1, W2, gs_x, F32(1), return_stages=True,
+                          n_shared=n_shared)
+    gs_h = quant.global_scale(quant.amax(st["h"]))
+    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2,
+                                torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d), keep=True,
+                                fused=False, n_shared=n_shared)
+    _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g, n_shared=n_shared)
+    x0 = torch.empty(0, wl.H, dtype=torch.bfloat16, device=d)
+    l0 = torch.empty(0, wl.E, dtype=torch.float32, device=d)
+    out0, g0 = pipeline.moe_layer(x0, l0, wl.k, w1, w2, torch.tensor([gs_x], device=d),
+                                  torch.tensor([gs_h], device=d), keep=True, n_shared=n_shared)
+    torch.cuda.synchronize()
+    assert out0.shape == (0, wl.H)
+    assert (to_np(g0["offsets"]) == 0).all() and g0["offsets"].shape == (wl.E + n_shared + 1,)
+
+
+@pytest.mark.parametrize("n_shared", [0, 1])
 def test_tiny_layer_graph_replays_match_eager(n_shared):
     # the routed layer (routing, permutation, both grouped GEMMs, SiLU-requant
     # in either place, combine) captured in a HIP graph gives the eager output
