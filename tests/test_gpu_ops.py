@@ -432,7 +432,8 @@ def test_silu_mul_requant_bit_exact(M, I, dtype):
 
 
 @pytest.mark.parametrize("T,k,H,dtype", [(16, 2, 256, "bf16"), (256, 6, 7168, "bf16"), (9, 1, 24, "f32"),
-                                         (33, 16, 64, "f32")])
+                                         (33, 16, 64, "f32"), (40, 7, 512, "bf16"), (12, 8, 64, "f32"),
+                                         (21, 11, 128, "bf16")])
 def test_combine_bit_exact(T, k, H, dtype):
     log("combine", T, k, H, dtype)
     rng = np.random.default_rng(T * k)
