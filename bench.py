@@ -534,7 +534,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
