@@ -187,10 +187,13 @@ def algorithmic(wl, n_touched, fused):
     return flops, l1_bytes, l1_flops
 
 
-def run_gpu(workload, steps, warmup):
+def run_gpu(workload, steps, warmup, tokens=None):
+    import dataclasses
     import torch
     from block_scaled_fp4_03_amd import workloads
     wl = workloads.WORKLOADS[workload]
+    if tokens:
+        wl = dataclasses.replace(wl, T=tokens)
     dev = torch.device("cuda:0")
     print("[bench] %s: preparing weights (%d experts) and inputs" % (workload, wl.E), file=sys.stderr, flush=True)
     layer = Layer(wl, dev)
@@ -208,7 +211,7 @@ def run_gpu(workload, steps, warmup):
     flops, l1_bytes, l1_flops = algorithmic(wl, n_touched, fused)
     res = dict(ms=ms, per_op_ms=per_op, step_pct=pct, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
                tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl,
-               fused=fused)
+               fused=fused, wl_default_T=workloads.WORKLOADS[workload].T)
     # the same layer with per-batch activation global scales computed on the
     # device (two extra amax passes; gs_h comes from the float32 gate_up, so
     # SiLU-requant runs as its own kernel), timed the same way
@@ -233,7 +236,9 @@ def roofline(res, bound):
         peak = F16_MFMA_PEAK_TFLOPS
         unit = "TFLOP/s"
     return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-            "traffic": measured_traffic(res["wl"].name, SILU_PATHS[res["fused"]]),
+            # (the committed counter runs cover the workloads at their own token counts)
+            "traffic": measured_traffic(res["wl"].name, SILU_PATHS[res["fused"]])
+            if res["wl"].T == res["wl_default_T"] else None,
             "kernel": "nvfp4_grouped_gemm_silu_requant L1 (gate_up, SiLU-requant epilogue)" if res["fused"]
             else "nvfp4_grouped_gemm L1 (gate_up)",
             "kernel_ms": round(l1_ms, 4)}
@@ -518,6 +523,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per step of the timed layer instead of the workload's own (the secondary "
+                         "prefill and side measurements are then skipped)")
     ap.add_argument("--cpu-experts", type=int, default=24)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (x3); used to calibrate the "
@@ -540,7 +548,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
-    main_res = run_gpu(args.workload, args.steps, args.warmup)
+    main_res = run_gpu(args.workload, args.steps, args.warmup, args.tokens or None)
+    if args.tokens:
+        args.no_prefill = True
     bound = "hbm" if args.workload == "decode" else "mfma"
     wl = main_res["wl"]
     line = {
