@@ -175,6 +175,9 @@ def _gemm_case(counts, N, K, n_seg, seed, gather=False, out_bf16=False, a_extra=
         # kernel) is checked against the same bound
         tiled = ops.prepare_weights(T(wc), T(ws))
         outs.append(("tiled", to_np(ops.grouped_gemm(*args, w_tiled=tiled, **kw))))
+        if ops.gemm_workspace_size(G, M, N, K, True) > 0:
+            # the same without a split-K workspace: the one-pass kernels
+            outs.append(("tiled, one pass", to_np(ops.grouped_gemm(*args, w_tiled=tiled, workspace=False, **kw))))
         if ops.gemm_reads_dq(G, M, K, a_rows, True):
             # A also in f16 form (from the oracle's dequantisation): the
             # many-row kernel copies it instead of decoding the codes.  Rows in
@@ -250,6 +253,13 @@ def test_gemm_big_tiles_with_remainders():
     # column tiles with a partial last one, two segments
     _gemm_case([456, 3, 256, 0, 611, 70], 520, 512, [0, 260, 520], 12, gather=True)
     _gemm_case([1024, 255, 257], 256, 768, [0, 256], 13, out_bf16=True)
+
+
+def test_gemm_64_row_streaming_slots():
+    # 40..64 rows per group on average (below the 256-row tiles): 64-row
+    # slots, with an empty group, a group of two slots, partial column tiles
+    _gemm_case([40, 55, 0, 47, 63, 41, 90], 320, 512, [0, 160, 320], 31, gather=True)
+    _gemm_case([65, 44, 50, 64, 1], 200, 768, [0, 200], 32, gather=True, out_bf16=True)
 
 
 def test_gemm_big_tiles_every_last_tile_height():
@@ -398,6 +408,10 @@ def test_fused_silu_requant_big_tiles():
     counts = [456, 3, 256, 0, 611, 70, 385]
     _fused_case(counts, 256, 512, 22, use_dq=True)
     _fused_case(counts, 256, 512, 23, use_dq=False)
+
+
+def test_fused_silu_requant_64_row_slots():
+    _fused_case([40, 55, 0, 47, 63, 41, 90], 160, 512, 26)
 
 
 def test_fused_silu_requant_one_group_no_gather():
