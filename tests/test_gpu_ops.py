@@ -266,6 +266,7 @@ def test_gemm_big_tiles_every_last_tile_height():
     # group sizes whose last tile takes each of the 256/128/64/32-row forms
     # (1, 31, 32, 33, 64, 65, 128, 129, 255 left-over rows)
     _gemm_case([257, 287, 288, 289, 320, 321, 384, 385, 511, 256], 96, 256, [0, 40, 96], 14, gather=True)
+    _gemm_case([257, 288, 289, 320, 321, 384, 385], 64, 4608, [0, 64], 17, gather=True)
 
 
 def test_gemm_big_tiles_split_k_one_group():
