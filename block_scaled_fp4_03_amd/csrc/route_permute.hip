@@ -79,9 +79,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // entry of e its rank among e's entries in flat order: every wave owns one
 // contiguous range of flat indices, ranks inside the wave come from a ballot,
 // and the ranges are offset by the counts of the waves before.  No atomics, so
-// the permutation is the same on every run.
+// the permutation is the same on every run.  Both passes read a wave's range
+// kPermBatch x 64 ids at a time, all loads issued before the first is used,
+// so that a pass costs one memory round trip per batch instead of one per 64
+// ids; pass 2 still takes the batch's 64-id chunks in flat order.
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermBatch = 8;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int64_t R,
                                                                int k, int E, int32_t* __restrict__ offsets,
@@ -96,10 +100,18 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   const int64_t lo = wv * per_wave;
   const int64_t hi = lo + per_wave < R ? lo + per_wave : R;
   int32_t n_lt = 0, n_eq = 0;
-  for (int64_t f = lo + lane; f < hi; f += 64) {
-    const int32_t id = ids[f];
-    n_lt += id < e;
-    n_eq += id == e;
+  for (int64_t b = lo; b < hi; b += 64 * kPermBatch) {
+    int32_t v[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int64_t f = b + 64 * u + lane;
+      v[u] = f < hi ? ids[f] : INT32_MAX;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      n_lt += v[u] < e;
+      n_eq += v[u] == e;
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -123,17 +135,26 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   }
   if (total_eq == 0) return;
   int32_t pos = total_lt + base;
-  for (int64_t f0 = lo; f0 < hi; f0 += 64) {
-    const int64_t f = f0 + lane;
-    const bool mine = f < hi && ids[f] == e;
-    const uint64_t mask = __ballot(mine);
-    const uint64_t below = lane ? (mask & ((~0ull) >> (64 - lane))) : 0ull;
-    if (mine) {
-      const int32_t p = pos + (int32_t)__popcll(below);
-      sorted_ids[p] = (int32_t)(f / k);
-      inv[f] = p;
+  for (int64_t b = lo; b < hi; b += 64 * kPermBatch) {
+    int32_t v[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int64_t f = b + 64 * u + lane;
+      v[u] = f < hi ? ids[f] : INT32_MAX;
     }
-    pos += (int32_t)__popcll(mask);
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int64_t f = b + 64 * u + lane;
+      const bool mine = v[u] == e;     // INT32_MAX (past the range) is never an expert id
+      const uint64_t mask = __ballot(mine);
+      const uint64_t below = lane ? (mask & ((~0ull) >> (64 - lane))) : 0ull;
+      if (mine) {
+        const int32_t p = pos + (int32_t)__popcll(below);
+        sorted_ids[p] = (int32_t)(f / k);
+        inv[f] = p;
+      }
+      pos += (int32_t)__popcll(mask);
+    }
   }
 }
 

@@ -103,7 +103,8 @@ def _route_case(T, E, k, seed, zipf=0.0, ties=False):
 @pytest.mark.parametrize("T,E,k,zipf,ties", [(16, 8, 2, 0, False), (256, 384, 6, 0, False),
                                              (8192, 384, 6, 1.1, False), (100, 384, 6, 0, True),
                                              (5, 1, 1, 0, False), (3, 16, 16, 0, True),
-                                             (77, 1024, 16, 0, False), (1, 64, 6, 0, True)])
+                                             (77, 1024, 16, 0, False), (1, 64, 6, 0, True),
+                                             (3001, 384, 7, 1.1, False)])
 def test_route_permute_bit_exact(T, E, k, zipf, ties):
     log("route", T, E, k, zipf, ties)
     lg = _route_case(T, E, k, T * 7 + E, zipf, ties)
