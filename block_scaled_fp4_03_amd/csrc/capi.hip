@@ -361,7 +361,7 @@ int32_t silu_mul_global_scale(const void* gate_up, int32_t in_dtype, int64_t M, 
 }
 
 int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm, const float* topk_w, int64_t T,
-                    int32_t k, int64_t H, uint16_t* out, void* stream) {
+                    int32_t k, int64_t H, const uint16_t* residual, uint16_t* out, void* stream) {
   const int es = elem_size(y_dtype);
   if (!es) return fail(NVFP4_EINVAL, "moe_combine: unknown dtype %d", y_dtype);
   if (T < 0 || H < 0) return fail(NVFP4_ESHAPE, "moe_combine: negative size");
@@ -369,11 +369,13 @@ int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm, con
   if (H % 8) return fail(NVFP4_ESHAPE, "moe_combine: H must be a multiple of 8");
   if (T == 0 || H == 0) return NVFP4_OK;
   if (!y || !inv_perm || !topk_w || !out) return fail(NVFP4_EINVAL, "moe_combine: null pointer");
-  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(inv_perm, 4) || !aligned(topk_w, 4))
-    return fail(NVFP4_EALIGN, "moe_combine: y and out must be 16-byte aligned");
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(residual, 16) || !aligned(inv_perm, 4) ||
+      !aligned(topk_w, 4))
+    return fail(NVFP4_EALIGN, "moe_combine: y, residual and out must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   return finish("moe_combine",
-                nvfp4::launch_combine(y, y_dtype == NVFP4_DTYPE_BF16, inv_perm, topk_w, T, k, H, out, s), s);
+                nvfp4::launch_combine(y, y_dtype == NVFP4_DTYPE_BF16, inv_perm, topk_w, T, k, H, residual, out, s),
+                s);
 }
 
 }  // extern "C"

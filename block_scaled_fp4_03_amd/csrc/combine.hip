@@ -1,4 +1,5 @@
-// Weighted combine of each token's k expert outputs back in token order.
+// Weighted combine of each token's k expert outputs back in token order,
+// with an optional residual added before the one rounding to bf16.
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -9,12 +10,16 @@ namespace nvfp4 {
 // order with separate float32 multiplies and adds, and writes 16 B of bf16.
 // The slot indices, weights and row slices are all requested before the
 // first product (KMAX slots unrolled, those past k skipped), so a thread
-// waits for two memory round trips, not two per slot.
+// waits for two memory round trips, not two per slot.  With a residual (bf16
+// [T, H]), its 8 values are loaded with the slices and added to the slot sum
+// as one more float32 addition.
 template <bool kBf16, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t T, int k,
-                                                      int64_t H, int64_t R, uint16_t* __restrict__ out) {
+                                                      int64_t H, int64_t R,
+                                                      const uint16_t* __restrict__ residual,
+                                                      uint16_t* __restrict__ out) {
   const int64_t per_row = H / 8;
   const int64_t n = T * per_row;
   constexpr int64_t kElem = kBf16 ? 2 : 4;
@@ -49,6 +54,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         q[j][1] = *(const u32x4n*)(p + 16);
       }
     }
+    u32x4n rq = {0u, 0u, 0u, 0u};
+    if (residual) rq = __builtin_nontemporal_load((const u32x4n*)(residual + t * H + c));
     float acc[8];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
@@ -73,6 +80,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         acc[e] = j == 0 ? prod : acc[e] + prod;
       }
     }
+    if (residual) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = acc[2 * e] + __uint_as_float(rq[e] << 16);
+        acc[2 * e + 1] = acc[2 * e + 1] + __uint_as_float(rq[e] & 0xFFFF0000u);
+      }
+    }
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -82,7 +96,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 }
 
 hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const float* w, int64_t T, int k,
-                          int64_t H, uint16_t* out, hipStream_t s) {
+                          int64_t H, const uint16_t* residual, uint16_t* out, hipStream_t s) {
   const int64_t n = T * (H / 8);
   if (n == 0) return hipSuccess;
   int64_t g = (n + 255) / 256;
@@ -91,14 +105,18 @@ hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const fl
   // slots unrolled up to 8 (top-6 with up to two shared experts) or 16
   if (bf16) {
     if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<true, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R, out);
+      hipLaunchKernelGGL((combine_kernel<true, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
+                         residual, out);
     else
-      hipLaunchKernelGGL((combine_kernel<true, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R, out);
+      hipLaunchKernelGGL((combine_kernel<true, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
+                         residual, out);
   } else {
     if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<false, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R, out);
+      hipLaunchKernelGGL((combine_kernel<false, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
+                         residual, out);
     else
-      hipLaunchKernelGGL((combine_kernel<false, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R, out);
+      hipLaunchKernelGGL((combine_kernel<false, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
+                         residual, out);
   }
   return hipGetLastError();
 }

@@ -110,6 +110,6 @@ hipError_t launch_silu_mul_global_scale(const void* gu, bool bf16, int64_t M, in
                                         float* gs_out, float* partial, hipStream_t s);
 
 hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const float* w, int64_t T,
-                          int k, int64_t H, uint16_t* out, hipStream_t s);
+                          int k, int64_t H, const uint16_t* residual, uint16_t* out, hipStream_t s);
 
 }  // namespace nvfp4

@@ -37,7 +37,7 @@ SIGNATURES = {
     "silu_mul_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "fp8_quantize_weight": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "fp8_weight_gemm": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _I32, _I64, _P]),
-    "moe_combine": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I64, _P, _P]),
+    "moe_combine": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I64, _P, _P, _P]),
 }
 
 _lib = None

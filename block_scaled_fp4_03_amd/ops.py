@@ -224,14 +224,18 @@ def silu_mul_global_scale(gate_up, out=None):
     return out
 
 
-def combine(y, inv, w, out=None):
-    """y [T*k, H] f32/bf16, inv [T, k], w [T, k] -> out [T, H] bf16."""
-    _check_dev(y, inv, w)
+def combine(y, inv, w, out=None, residual=None):
+    """y [T*k, H] f32/bf16, inv [T, k], w [T, k] -> out [T, H] bf16; with
+    residual (bf16 [T, H], contiguous) it is added before the rounding."""
+    _check_dev(y, inv, w, residual)
     T, k = inv.shape
     H = y.shape[1]
+    if residual is not None and (residual.dtype != torch.bfloat16 or tuple(residual.shape) != (T, H)
+                                 or not residual.is_contiguous()):
+        raise ValueError("residual must be a contiguous bfloat16 [%d, %d] tensor" % (T, H))
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
-    _lib.call("moe_combine", _p(y), _dtype(y), _p(inv), _p(w), T, k, H, _p(out), _stream())
+    _lib.call("moe_combine", _p(y), _dtype(y), _p(inv), _p(w), T, k, H, _p(residual), _p(out), _stream())
     return out
 
 

@@ -167,7 +167,7 @@ def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xd
     return y, st
 
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared=0):
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared=0, residual=None):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
     1-element f32 tensors: static activation global scales (from a warmup
     batch), or None for dynamic ones computed on the device from this batch
@@ -179,7 +179,8 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared
     shared experts as their last groups: every token visits them with weight
     1 (moe_route_permute_shared), so one grouped GEMM per projection covers
     the routed and the shared experts, and the combine adds the shared
-    outputs after the routed slots.  Returns out [T, H] bf16 (and the
+    outputs after the routed slots.  residual (bf16 [T, H]) is added by the
+    combine before its one rounding.  Returns out [T, H] bf16 (and the
     stages)."""
     T, H = x.shape
     if w1.codes.shape[0] != logits.shape[1] + n_shared:
@@ -194,7 +195,7 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared
     ids, w, off, sorted_ids, inv = ops.route_permute(logits, k, n_shared)
     y, st = _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, T, a_row_index=sorted_ids,
                         xdq=xdq[0] if xdq else None, fused=fused)
-    out = ops.combine(y, inv, w)
+    out = ops.combine(y, inv, w, residual=residual)
     if keep:
         st.update(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv, gs_x=gs_x)
         return out, st

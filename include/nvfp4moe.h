@@ -103,6 +103,13 @@ int32_t nvfp4_version(void);
  * code of the block is 0x0.  Otherwise r = 1/(sf*gs) and code_i = sign bit of
  * x_i, plus the E2M1 magnitude nearest to |x_i*r| (ties to the even code,
  * saturating at 6).
+ * This is the activation quantiser that feeds each NVFP4 GEMM: page
+ * "CURRENT_BUG.md - DeepSeek-V4 Blackwell NVFP4" (revision dd7af0c, section
+ * "Root Cause Investigation") tests it on its own as one step of the MoE
+ * path, and page "Current Bug: vLLM produces empty/garbage output" (revision
+ * a51edd2, section "What the quant method does") shows why the direction of
+ * its global scale must be fixed (a stored inverse read as a multiplier gave
+ * NaN); here the direction is pinned and out-of-range blocks saturate.
  * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless
  * rows >= 0, cols % 16 == 0, ld_x >= cols; EALIGN for misaligned pointers or
  * row pitch.  rows == 0 or cols == 0 is a no-op.
@@ -123,6 +130,14 @@ int32_t nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t col
  *   ws       workspace of at least nvfp4_global_scale_workspace_size(batch, n)
  *            bytes (16-byte aligned; may be NULL if that size is 0).
  * The maximum is order-independent, so the result is exact and deterministic.
+ * The pages compute activation global scales from a warmup pass (page
+ * "Current Bug: vLLM produces empty/garbage output", revision e8b289e,
+ * section "Phase 1: CuTeDSL Shared Expert Kernel", and the MoE runner "with
+ * warmup gs" in the standalone-chain table of revision a51edd2) and keep one
+ * activation scale per layer input (revision a51edd2, "What the quant method
+ * does": the per-expert input scales are collapsed to their maximum); this
+ * call is that reduction, run over a warmup batch, a weight, or (for
+ * per-batch scales) the batch itself.
  */
 size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n);
 int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_t n,
@@ -332,6 +347,11 @@ int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, i
  * Per element in float32, each step one IEEE operation: e = exp(-g) (the
  * same exponential as moe_route_permute, +Inf above 88), s = g / (1 + e),
  * h = s * u; then the quantisation of nvfp4_quantize with gs_h.
+ * This is the "SiLU -> re-quant" step between the two GEMMs of the expert
+ * MLP on page "Current Bug: vLLM produces empty/garbage output" (revision
+ * e8b289e, section "Phase 1: CuTeDSL Shared Expert Kernel"), applied to the
+ * stacked gate_up output; the page keeps SiLU in BF16, here it stays float32
+ * up to the re-quantisation (no intermediate rounding).
  * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless M >= 0,
  * I % 16 == 0, ld >= 2I; EALIGN unless gate_up is 16-byte aligned and
  * ld*elem_size is a multiple of 16.
@@ -352,21 +372,28 @@ int32_t silu_mul_global_scale(const void* gate_up, int32_t in_dtype, int64_t M, 
                               void* stream);
 
 /*
- * moe_combine - weighted sum of each token's k expert outputs.
- *   y        [T*k, H] of y_dtype (F32 or BF16), permuted rows.
- *   inv_perm [T, k] int32, topk_w [T, k] float32 (from moe_route_permute).
- *   out      [T, H] bf16 (uint16 storage).
+ * moe_combine - weighted sum of each token's k expert outputs, plus an
+ * optional residual, back in token order.
+ *   y         [T*k, H] of y_dtype (F32 or BF16), permuted rows.
+ *   inv_perm  [T, k] int32, topk_w [T, k] float32 (from moe_route_permute).
+ *   residual  [T, H] bf16 (uint16 storage, 16-byte aligned) or NULL.
+ *   out       [T, H] bf16 (uint16 storage).
  * out[t] = bf16(acc) with acc = w_0*y[inv[t,0]], then acc = acc + w_j*y[inv[t,j]]
- * for j = 1..k-1, each product and sum a separate float32 operation, one
- * rounding to bf16 (nearest-even) at the end.  The page keeps the final
- * scatter in BF16 (e8b289e, "Phase 3: Clean up").
+ * for j = 1..k-1, then (with a residual) acc = acc + residual[t], each product
+ * and sum a separate float32 operation, one rounding to bf16 (nearest-even)
+ * at the end.  This is the final scatter of the routed experts' outputs back
+ * to the tokens, which the page keeps in BF16 (page "Current Bug: vLLM
+ * produces empty/garbage output", revision e8b289e, section "Phase 3: Clean
+ * up"); the residual lets a caller add the layer's skip connection (or a
+ * separately computed shared expert) in the same pass without a second
+ * bf16 rounding.
  * Errors: EINVAL for null pointers or an unknown dtype; ESHAPE unless T >= 0,
- * 1 <= k <= NVFP4_MAX_TOPK, H % 8 == 0; EALIGN unless y and out are 16-byte
- * aligned.
+ * 1 <= k <= NVFP4_MAX_TOPK, H % 8 == 0; EALIGN unless y, residual and out are
+ * 16-byte aligned.
  */
 int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm,
-                    const float* topk_w, int64_t T, int32_t k, int64_t H, uint16_t* out,
-                    void* stream);
+                    const float* topk_w, int64_t T, int32_t k, int64_t H, const uint16_t* residual,
+                    uint16_t* out, void* stream);
 
 /*
  * fp8_quantize_weight - block-scaled FP8 (E4M3) weights for the attention

@@ -109,10 +109,21 @@ def permute(ids, E):
 # --- grouped GEMM -----------------------------------------------------------
 
 def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg,
-                 group_offsets, a_row_index=None, out_dtype="f32"):
+                 group_offsets, a_row_index=None, out_dtype="f32", mode="exact"):
     """out[m, n] = alpha(g, seg(n)) * sum_k A[m, k] * W[g, n, k] for rows m of
     group g, A and W dequantised without their global scales,
     alpha = fp32(a_gs * w_gs[g, seg]).
+
+    mode "exact" (the reference): float64 products of the exactly
+    dequantised values (exact: each is an integer multiple of 2**-20 below
+    2**43 of those units) and float64 sums, which stay exact while partial
+    sums are below 2**53 units and otherwise err by less than
+    K * 2**-53 * sum |a w|, far below float32 resolution; alpha applied in
+    float64, one rounding to float32.
+    mode "f32": dequantise to float32 (exact: at most five significant bits)
+    and multiply with a float32 library matmul, then alpha in float32 (two
+    roundings): the plain dequantise-then-matmul reference, accurate to the
+    float32 summation bound gamma_K * sum |a w| of the exact result.
 
     a_codes/a_scales: NVFP4 [Ma, K]; a_row_index (optional) [M]: logical row m
     reads stored row a_row_index[m]; w_codes/w_scales: [G, N, K/2], [G, N, K/16];
@@ -129,22 +140,32 @@ def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg,
     n_seg = list(n_seg)
     if n_seg[0] != 0 or n_seg[-1] != N or len(n_seg) != w_gs.shape[1] + 1:
         raise ValueError("bad n_seg")
+    if mode not in ("exact", "f32"):
+        raise ValueError("mode must be 'exact' or 'f32'")
     A = dequantize_blocks(a_codes, a_scales)
     if a_row_index is not None:
         A = A[np.asarray(a_row_index, dtype=np.int64)]
     if A.shape != (M, K):
         raise ValueError("A has shape %s, expected %s" % (A.shape, (M, K)))
+    if mode == "f32":
+        A = A.astype(F32)                                       # exact
     out = np.zeros((M, N), dtype=F32)
     for g in range(G):
         r0, r1 = int(off[g]), int(off[g + 1])
         if r1 == r0:
             continue
         W = dequantize_blocks(w_codes[g], w_scales[g])          # [N, K] float64
-        acc = A[r0:r1] @ W.T                                    # float64
+        if mode == "f32":
+            acc = A[r0:r1] @ W.astype(F32).T                    # float32 matmul
+        else:
+            acc = A[r0:r1] @ W.T                                # float64
         for s in range(len(n_seg) - 1):
             c0, c1 = n_seg[s], n_seg[s + 1]
             alpha = F32(F32(a_gs) * w_gs[g, s])
-            out[r0:r1, c0:c1] = (acc[:, c0:c1] * np.float64(alpha)).astype(F32)
+            if mode == "f32":
+                out[r0:r1, c0:c1] = (acc[:, c0:c1] * alpha).astype(F32)
+            else:
+                out[r0:r1, c0:c1] = (acc[:, c0:c1] * np.float64(alpha)).astype(F32)
     if out_dtype == "bf16":
         out = bf16_round(out)
     elif out_dtype != "f32":
@@ -174,9 +195,13 @@ def silu_mul_requant(gate_up, gs_h):
 
 # --- combine -----------------------------------------------------------------
 
-def combine(y, inv, w):
+def combine(y, inv, w, residual=None):
     """y float32 [T*k, H] (bf16 values), inv int32 [T, k], w float32 [T, k]
-    -> out float32 [T, H] holding bf16 values."""
+    -> out float32 [T, H] holding bf16 values.
+
+    With residual (float32 [T, H] holding bf16 values), it is added after
+    the last slot, as one more float32 addition before the single rounding
+    to bf16: out = bf16(((w_0 y_0 + w_1 y_1) + ...) + residual)."""
     y = np.asarray(y, dtype=F32)
     inv = np.asarray(inv, dtype=np.int64)
     w = np.asarray(w, dtype=F32)
@@ -184,19 +209,27 @@ def combine(y, inv, w):
     acc = (w[:, 0:1] * y[inv[:, 0]]).astype(F32)
     for j in range(1, k):
         acc = (acc + (w[:, j:j + 1] * y[inv[:, j]]).astype(F32)).astype(F32)
+    if residual is not None:
+        residual = np.asarray(residual, dtype=F32)
+        if residual.shape != acc.shape:
+            raise ValueError("residual must be [T, H]")
+        acc = (acc + residual).astype(F32)
     return bf16_round(acc)
 
 
 # --- compositions --------------------------------------------------------------
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=False, n_shared=0):
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=False, n_shared=0, gemm_mode="exact",
+              residual=None):
     """The routed MoE layer.
 
     x float32 [T, H] (bf16 values); logits float32 [T, E];
     w1 = (codes [E, 2I, H/2], scales [E, 2I, H/16], gs [E, 2]) gate rows first;
     w2 = (codes [E, H, I/2], scales [E, H, I/16], gs [E, 1]).
     With n_shared, w1 and w2 hold E + n_shared experts, the last n_shared
-    being shared experts folded in (see append_shared).
+    being shared experts folded in (see append_shared).  gemm_mode selects
+    the GEMM arithmetic (see grouped_gemm); residual (optional [T, H] bf16
+    values) is added by the combine.
     Returns out float32 [T, H] holding bf16 values (and the stages if asked).
     """
     T, H = x.shape
@@ -211,12 +244,12 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, return_stages=False, n_shared=0)
         ids, wts = append_shared(ids, wts, E, n_shared)
     offsets, sorted_ids, inv = permute(ids, E + n_shared)
     gu = grouped_gemm(xq[0], xq[1], gs_x, w1[0], w1[1], w1[2], [0, I, I2],
-                      offsets, a_row_index=sorted_ids, out_dtype="f32")
+                      offsets, a_row_index=sorted_ids, out_dtype="f32", mode=gemm_mode)
     h = silu_mul(gu)
     hq = quantize(h, gs_h)
     y = grouped_gemm(hq[0], hq[1], gs_h, w2[0], w2[1], w2[2], [0, H],
-                     offsets, out_dtype="bf16")
-    out = combine(y, inv, wts)
+                     offsets, out_dtype="bf16", mode=gemm_mode)
+    out = combine(y, inv, wts, residual)
     if return_stages:
         return out, dict(xq=xq, ids=ids, w=wts, offsets=offsets,
                          sorted_ids=sorted_ids, inv=inv, gate_up=gu, h=h, hq=hq, y=y)

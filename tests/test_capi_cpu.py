@@ -185,10 +185,14 @@ def test_silu_and_combine_validation(L):
                               NULL) == lib.EALIGN
     assert L.silu_mul_requant(FAKE, lib.DTYPE_F32, 4, 32, 32, FAKE, FAKE, FAKE, NULL, NULL) == lib.ESHAPE
     assert L.silu_mul_requant(FAKE, 3, 4, 32, 64, FAKE, FAKE, FAKE, NULL, NULL) == lib.EINVAL
-    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 0, 64, FAKE, NULL) == lib.ESHAPE
-    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 2, 60, FAKE, NULL) == lib.ESHAPE
-    assert L.moe_combine(FAKE, lib.DTYPE_BF16, NULL, FAKE, 4, 2, 64, FAKE, NULL) == lib.EINVAL
-    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 0, 2, 64, NULL, NULL) == lib.OK
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 0, 64, NULL, FAKE, NULL) == lib.ESHAPE
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 2, 60, NULL, FAKE, NULL) == lib.ESHAPE
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, NULL, FAKE, 4, 2, 64, NULL, FAKE, NULL) == lib.EINVAL
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 0, 2, 64, NULL, NULL, NULL) == lib.OK
+    # the optional residual must be 16-byte aligned like y and out
+    assert L.moe_combine(FAKE, lib.DTYPE_BF16, FAKE, FAKE, 4, 2, 64, ctypes.c_void_p(0x1008), FAKE,
+                         NULL) == lib.EALIGN
+    assert "residual" in _err(L)
 
 
 def test_global_scale_validation_and_workspace(L):
@@ -216,3 +220,4 @@ def test_fused_silu_default_choice(L):
     assert not w1(1).fuse_by_default(128, 128)                # shared expert: K split
     assert not w1(384, tiled=False).fuse_by_default(1536, 256)  # row-major weights: no fused kernel
     assert not w1(8, I=48).fuse_by_default(64, 32)            # I % 32 != 0
+

@@ -464,6 +464,13 @@ def test_combine_bit_exact(T, k, H, dtype):
         yt = yt.to(torch.bfloat16)
     out = ops.combine(yt, torch.from_numpy(inv).to(dev()), torch.from_numpy(w).to(dev()))
     assert np.array_equal(to_np(out).view(np.uint32), ref.view(np.uint32))
+    # with a residual (added after the slots, before the one bf16 rounding)
+    r = formats.bf16_round((rng.standard_normal((T, H)) * 2).astype(np.float32))
+    ref_r = moe.combine(y, inv, w, residual=r)
+    out_r = ops.combine(yt, torch.from_numpy(inv).to(dev()), torch.from_numpy(w).to(dev()),
+                        residual=bf16_tensor(r, dev()))
+    assert np.array_equal(to_np(out_r).view(np.uint32), ref_r.view(np.uint32))
+    assert not np.array_equal(ref_r, ref)
 
 
 # --- FP8 weight-only projection (wo_a) ------------------------------------------

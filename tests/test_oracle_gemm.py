@@ -103,3 +103,81 @@ def test_bf16_output_is_rounded_f32_output():
     f = moe.grouped_gemm(*args)
     b = moe.grouped_gemm(*args, out_dtype="bf16")
     assert np.array_equal(b, formats.bf16_round(f))
+
+
+def test_f32_mode_within_summation_bound_of_exact_mode():
+    """The float32 dequantise-then-matmul mode agrees with the exact mode to
+    the float32 summation bound gamma_K * sum |a w| * alpha (plus the two
+    roundings of the alpha product), and is not bitwise the same (it really
+    sums in float32)."""
+    G, N, K = 3, 96, 2048
+    off = np.array([0, 5, 5, 17], dtype=np.int32)
+    # block magnitudes spread over e^-9 .. 1, so that products of very
+    # different sizes meet in the float32 sums and those sums round
+    rng = np.random.default_rng(31)
+    xa = (rng.standard_normal((17, K)) * np.exp(rng.uniform(-9, 0, (17, K // 16))).repeat(16, 1)).astype(np.float32)
+    gsa = quant.global_scale(quant.amax(xa))
+    a = quant.quantize(xa, gsa) + (gsa,)
+    ws = [_nvfp4(N, K, 40 + g, std=0.02) for g in range(G)]
+    wc = np.stack([w[0] for w in ws]); wsc = np.stack([w[1] for w in ws])
+    wgs = np.array([[w[2], w[2] * np.float32(1.5)] for w in ws], dtype=np.float32)
+    args = (a[0], a[1], a[2], wc, wsc, wgs, [0, 40, N], off)
+    ex = moe.grouped_gemm(*args).astype(np.float64)
+    f = moe.grouped_gemm(*args, mode="f32").astype(np.float64)
+    A = quant.dequantize_blocks(a[0], a[1])
+    gamma = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    for g in range(G):
+        r = slice(off[g], off[g + 1])
+        if off[g + 1] == off[g]:
+            continue
+        W = quant.dequantize_blocks(wc[g], wsc[g])
+        absum = np.abs(A[r]) @ np.abs(W).T
+        alpha = np.concatenate([np.full(40, float(np.float32(a[2] * wgs[g, 0]))),
+                                np.full(N - 40, float(np.float32(a[2] * wgs[g, 1])))])
+        bound = gamma * absum * alpha + 3 * np.spacing(np.abs(ex[r]).astype(np.float32)).astype(np.float64)
+        assert (np.abs(f[r] - ex[r]) <= bound).all()
+    assert not np.array_equal(f, ex)
+
+
+def test_f32_mode_equals_float32_library_matmul_bitwise():
+    """The f32 mode is a float32 matmul of the dequantised operands followed
+    by one float32 multiply by alpha: re-computed with torch's float32 CPU
+    matmul (a second library) it agrees to the last bit only where both
+    libraries sum in the same order, so compare within one float32 ulp of
+    the sum magnitude per K-block instead."""
+    import torch
+    M, N, K = 12, 64, 1024
+    a = _nvfp4(M, K, 51)
+    w = _nvfp4(N, K, 52, std=0.02)
+    f = moe.grouped_gemm(a[0], a[1], a[2], w[0][None], w[1][None], np.array([[w[2]]]), [0, N], [0, M], mode="f32")
+    A = torch.from_numpy(quant.dequantize_blocks(a[0], a[1]).astype(np.float32))
+    W = torch.from_numpy(quant.dequantize_blocks(w[0], w[1]).astype(np.float32))
+    t = (A @ W.T).numpy() * np.float32(a[2] * w[2])
+    absum = (np.abs(A.numpy()).astype(np.float64) @ np.abs(W.numpy()).astype(np.float64).T) * float(
+        np.float32(a[2] * w[2]))
+    gamma = K * 2.0 ** -24 / (1 - K * 2.0 ** -24)
+    assert (np.abs(f.astype(np.float64) - t.astype(np.float64)) <= 2 * gamma * absum + 1e-30).all()
+
+
+def test_layer_in_f32_mode_tracks_exact_mode():
+    """The whole tiny layer with float32 GEMMs: routing, permutation and the
+    layer input codes are the same; the output agrees with the exact-mode
+    layer to cosine 1 - 1e-6 (differences come only from float32 sums and
+    the re-quantisation flips they may cause)."""
+    from oracle import formats
+    rng = np.random.default_rng(60)
+    T, H, I, E, k = 16, 256, 128, 8, 2
+    x = formats.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w1 = [_nvfp4(2 * I, H, 70 + e, std=0.02) for e in range(E)]
+    w2 = [_nvfp4(H, I, 90 + e, std=0.02) for e in range(E)]
+    W1 = (np.stack([w[0] for w in w1]), np.stack([w[1] for w in w1]),
+          np.array([[w[2], w[2]] for w in w1], np.float32))
+    W2 = (np.stack([w[0] for w in w2]), np.stack([w[1] for w in w2]), np.array([[w[2]] for w in w2], np.float32))
+    gs_x = quant.global_scale(quant.amax(x))
+    ex, st = moe.moe_layer(x, logits, k, W1, W2, gs_x, np.float32(0.002), return_stages=True)
+    f, sf = moe.moe_layer(x, logits, k, W1, W2, gs_x, np.float32(0.002), return_stages=True, gemm_mode="f32")
+    for key in ("ids", "offsets", "sorted_ids", "inv"):
+        assert np.array_equal(st[key], sf[key])
+    a, b = ex.astype(np.float64).ravel(), f.astype(np.float64).ravel()
+    assert (a * b).sum() / np.sqrt((a * a).sum() * (b * b).sum()) >= 1 - 1e-6

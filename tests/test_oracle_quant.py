@@ -147,3 +147,79 @@ def test_brute_force_tiny_block_reconstruction_is_nearest_grid_point():
         for xi, di in zip(x[0].astype(np.float64), d):
             best = np.abs(grid - xi).min()
             assert abs(di - xi) <= best * (1 + 1e-6) + 1e-12
+
+
+def _f32_div(a, b):
+    """IEEE float32 a / b of float32 operands, via float64: the float64
+    quotient rounded once to float32 is the correctly rounded float32
+    quotient (53 >= 2 * 24 + 2 bits, so the double rounding is innocuous)."""
+    return (np.asarray(a, np.float32).astype(np.float64) / np.asarray(b, np.float32).astype(np.float64)).astype(
+        np.float32)
+
+
+def _f32_mul(a, b):
+    """IEEE float32 a * b of float32 operands: the float64 product is exact
+    (48 significant bits), so one rounding to float32 is the float32 product."""
+    return (np.asarray(a, np.float32).astype(np.float64) * np.asarray(b, np.float32).astype(np.float64)).astype(
+        np.float32)
+
+
+def _pre_rounding_cases():
+    """Blocks of every kind: normal scales, subnormal scales, saturated
+    scales (block amax far above what 448 * 6 * gs can encode), all-zero."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((16, 256)).astype(np.float32)
+    x[0, :16] = 0.0                                   # all-zero block
+    x[1, :] *= np.float32(3e-5)                       # subnormal block scales
+    x[2, 16:32] *= np.float32(1e-9)                   # scale rounds to zero: flushed
+    x[3, :] *= np.float32(400.0)                      # saturated scales (448)
+    gs = quant.global_scale(np.float32(4.0))          # amax 4 -> most blocks normal
+    return x, gs
+
+
+def test_pre_rounding_values_follow_the_quantisation_steps():
+    """pre_rounding_values re-derived with float64 arithmetic and one rounding
+    per step (a different route to the same IEEE float32 results):
+    s = bamax / (6 gs), r = 1 / (sf gs), v = x r, v = 0 in flushed blocks."""
+    x, gs = _pre_rounding_cases()
+    s, v = quant.pre_rounding_values(x, gs)
+    xb = x.reshape(16, 16, 16)
+    bamax = np.abs(xb).max(axis=2)
+    d = _f32_mul(np.float32(6.0), gs)
+    s_ref = _f32_div(bamax, d)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    sf = formats.e4m3_decode(formats.e4m3_encode_nonneg(s_ref)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        r = np.where(sf > 0, _f32_div(np.float32(1.0), _f32_mul(sf, gs)), np.float32(0.0)).astype(np.float32)
+    v_ref = _f32_mul(xb, r[:, :, None]).reshape(16, 256)
+    assert np.array_equal(np.abs(v), np.abs(v_ref))
+    # the cases really are there: zero, subnormal, flushed, saturated, normal
+    assert (s == 0).any() and (sf == 0).sum() >= 2
+    assert ((sf > 0) & (sf < 2.0 ** -6)).any()
+    assert (s > 448).any()
+    assert ((sf >= 2.0 ** -6) & (sf < 448)).any()
+    # in unsaturated normal blocks the largest element sits within one E4M3
+    # rounding (at most 1/16 relative) of 6
+    normal = (sf >= 2.0 ** -6) & (s <= 448)
+    vmax = np.abs(v.reshape(16, 16, 16)).max(axis=2)
+    assert (np.abs(vmax[normal] - 6.0) <= 6.0 / 15.0).all()
+
+
+def test_quantize_is_the_encoding_of_pre_rounding_values():
+    """quantize(x, gs) equals, bit for bit, the E4M3 encoding of the block
+    values s and the sign plus E2M1 encoding of the element values v that
+    pre_rounding_values reports, on normal, subnormal, saturated and zero
+    blocks: the audit of rounding flips reads the numbers the encoders saw."""
+    x, gs = _pre_rounding_cases()
+    c, sc = quant.quantize(x, gs)
+    s, v = quant.pre_rounding_values(x, gs)
+    assert np.array_equal(sc, formats.e4m3_encode_nonneg(s))
+    sf = np.repeat(formats.e4m3_decode(sc), 16, axis=1)
+    codes = quant.unpack_codes(c)
+    want = formats.e2m1_magnitude_index(np.abs(v)) | (np.signbit(x).astype(np.uint8) << 3)
+    want = np.where(sf > 0, want, 0).astype(np.uint8)
+    assert np.array_equal(codes, want)
+    # saturated blocks: scale code 0x7E (448) and some element at code 6
+    sat = s > 448
+    assert (sc[sat] == 0x7E).all()
+    assert ((codes.reshape(16, 16, 16)[sat] & 7) == 7).any(axis=-1).all()
