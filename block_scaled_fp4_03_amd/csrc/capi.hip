@@ -10,6 +10,9 @@
 #include "../../include/nvfp4moe.h"
 #include "launch.hpp"
 
+static_assert(NVFP4_NOALLOC_SCRATCH_BYTES == nvfp4::kNoAllocScratchFloats * sizeof(float),
+              "the header's scratch limit must match the scratch array");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -97,6 +100,31 @@ int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_
   return finish("nvfp4_global_scale",
                 nvfp4::launch_global_scale(x, x_dtype == NVFP4_DTYPE_BF16, batch, n, stride, gs_out,
                                            (float*)ws, s),
+                s);
+}
+
+int32_t nvfp4_global_scale_noalloc(const void* x, int32_t x_dtype, int64_t batch, int64_t n, int64_t stride,
+                                   float* gs_out, void* stream) {
+  const char* who = "nvfp4_global_scale_noalloc";
+  const int es = elem_size(x_dtype);
+  if (!es) return fail(NVFP4_EINVAL, "%s: unknown dtype %d", who, x_dtype);
+  if (batch < 0 || n < 0) return fail(NVFP4_ESHAPE, "%s: negative size", who);
+  if (batch > 65535) return fail(NVFP4_ESHAPE, "%s: batch > 65535", who);
+  if (n % 8) return fail(NVFP4_ESHAPE, "%s: n must be a multiple of 8", who);
+  if (stride < n) return fail(NVFP4_ESHAPE, "%s: stride < n", who);
+  if (batch == 0) return NVFP4_OK;
+  const size_t need = nvfp4_global_scale_workspace_size(batch, n);
+  if (need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(NVFP4_ESHAPE, "%s: batch=%lld slices of n=%lld need %zu bytes of scratch, above the %d-byte limit",
+                who, (long long)batch, (long long)n, need, NVFP4_NOALLOC_SCRATCH_BYTES);
+  if (!x || !gs_out) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(x, 16) || (stride * es) % 16 || !aligned(gs_out, 4))
+    return fail(NVFP4_EALIGN, "%s: x and its pitch must be 16-byte aligned", who);
+  float* ws = nullptr;
+  const hipError_t e = nvfp4::noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: scratch lookup failed: %s", who, hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_global_scale(x, x_dtype == NVFP4_DTYPE_BF16, batch, n, stride, gs_out, ws, s),
                 s);
 }
 

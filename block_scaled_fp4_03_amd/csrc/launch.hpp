@@ -47,6 +47,10 @@ constexpr int kTileBytes = 4608;
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,
                            const float* gs, uint8_t* codes, uint8_t* scales, uint16_t* dq, hipStream_t s);
 int64_t amax_chunks(int64_t n);
+// The no-allocation entry point's scratch: floats per device, and its device
+// address on the current device (looked up once per device).
+constexpr int64_t kNoAllocScratchFloats = 65536;
+hipError_t noalloc_scratch(float** ptr);
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t batch, int64_t n, int64_t stride,
                                float* gs_out, float* partial, hipStream_t s);
 

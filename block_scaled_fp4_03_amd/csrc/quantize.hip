@@ -1,4 +1,6 @@
 // NVFP4 quantisation of float tensors and global-scale (amax) reductions.
+#include <mutex>
+
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -78,6 +80,37 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict
     m = __builtin_fmaxf(m, partial[b * chunks + i]);
   m = block_max(m);
   if (threadIdx.x == 0) gs_out[b] = global_scale_from_amax(m);
+}
+
+// Scratch memory of the no-allocation global-scale entry point: the partial
+// maxima of launch_global_scale, kNoAllocScratchFloats floats per device,
+// held from the library's load to the end of the process.  In host code
+// `scratch` names a host-side stand-in, never the device copy: the device
+// address is looked up once per device with hipGetSymbolAddress and only
+// that address is passed to kernels.
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current (it is: dev is the current one)
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? (float*)p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return *ptr ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 int64_t amax_chunks(int64_t n) {

@@ -9,6 +9,7 @@ OK, EINVAL, ESHAPE, EALIGN, EHIP = 0, 1, 2, 3, 4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 MAX_EXPERTS, MAX_TOPK, MAX_SEGMENTS = 1024, 16, 4
+NOALLOC_SCRATCH_BYTES = 262144
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -22,6 +23,7 @@ SIGNATURES = {
     "nvfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_global_scale_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_global_scale": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "nvfp4_global_scale_noalloc": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P]),
     "moe_route_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_route_permute_shared": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, ctypes.POINTER(_I32), _I32,

@@ -81,6 +81,21 @@ def global_scale(x, out=None):
     return out
 
 
+def global_scale_noalloc(x, out):
+    """global_scale into a caller-given out [batch] float32, through the entry
+    point that allocates nothing (its partial maxima use the library's
+    per-device scratch); no torch allocation either."""
+    _check_dev(x, out)
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    if x2.stride(1) != 1:
+        raise ValueError("x must have unit inner stride")
+    batch, n = x2.shape
+    if out.dtype != torch.float32 or out.numel() < batch or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of at least %d elements" % batch)
+    _lib.call("nvfp4_global_scale_noalloc", _p(x2), _dtype(x2), batch, n, x2.stride(0), _p(out), _stream())
+    return out
+
+
 def route_permute(logits, k, n_shared=0):
     """logits [T, E] f32 -> (ids [T,kk] i32, w [T,kk] f32, offsets [E+n_shared+1] i32,
     sorted_token_ids [T*kk] i32, inv [T,kk] i32) with kk = k + n_shared: the

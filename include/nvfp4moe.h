@@ -145,6 +145,27 @@ int32_t nvfp4_global_scale(const void* x, int32_t x_dtype, int64_t batch, int64_
                            void* stream);
 
 /*
+ * nvfp4_global_scale_noalloc - nvfp4_global_scale without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * partial maxima go to scratch memory the library holds on each device, so
+ * the call allocates nothing.  Same arguments (minus ws, ws_bytes), results
+ * and errors as nvfp4_global_scale, plus:
+ *   - ESHAPE when nvfp4_global_scale_workspace_size(batch, n) exceeds
+ *     NVFP4_NOALLOC_SCRATCH_BYTES (256 KiB: e.g. up to 64 slices of any
+ *     length, or 65535 slices of up to 16384 elements);
+ *   - EHIP if the scratch of the current device cannot be looked up.
+ * The scratch is per device and shared by every call on it: it is fully
+ * rewritten before it is read, so a call never depends on an earlier one,
+ * but calls that overlap in time on one device (several streams or host
+ * threads) race on it and give unspecified results.  `stream` must belong
+ * to the current device.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES 262144
+int32_t nvfp4_global_scale_noalloc(const void* x, int32_t x_dtype, int64_t batch, int64_t n,
+                                   int64_t stride, float* gs_out, void* stream);
+
+/*
  * moe_route_permute - top-k routing and the group-by-expert permutation.
  *   logits            [T, E] float32 router logits.
  *   topk_ids          out [T, k] int32: slot 0 is the largest logit; equal

@@ -221,3 +221,17 @@ def test_fused_silu_default_choice(L):
     assert not w1(384, tiled=False).fuse_by_default(1536, 256)  # row-major weights: no fused kernel
     assert not w1(8, I=48).fuse_by_default(64, 32)            # I % 32 != 0
 
+
+def test_global_scale_noalloc_validation(L):
+    # the scratch limit is checked on the host, before any HIP call
+    lim = lib.NOALLOC_SCRATCH_BYTES
+    assert L.nvfp4_global_scale_workspace_size(64, 16384 * 1024) == lim
+    assert L.nvfp4_global_scale_noalloc(FAKE, lib.DTYPE_BF16, 65, 16384 * 1024, 16384 * 1024, FAKE,
+                                        NULL) == lib.ESHAPE
+    assert "scratch" in _err(L)
+    assert L.nvfp4_global_scale_noalloc(FAKE, lib.DTYPE_BF16, 2, 12, 16, FAKE, NULL) == lib.ESHAPE
+    assert L.nvfp4_global_scale_noalloc(FAKE, 5, 2, 16, 16, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_global_scale_noalloc(NULL, lib.DTYPE_BF16, 2, 16, 16, FAKE, NULL) == lib.EINVAL
+    assert L.nvfp4_global_scale_noalloc(ctypes.c_void_p(0x1004), lib.DTYPE_BF16, 2, 16, 16, FAKE,
+                                        NULL) == lib.EALIGN
+    assert L.nvfp4_global_scale_noalloc(FAKE, lib.DTYPE_BF16, 0, 16, 16, NULL, NULL) == lib.OK
