@@ -270,6 +270,51 @@ def test_gemm_big_tiles_every_last_tile_height():
     _gemm_case([257, 288, 289, 320, 321, 384, 385], 64, 4608, [0, 64], 17, gather=True)
 
 
+def test_gemm_big_tiles_last_tile_heights_at_model_depths():
+    # the last-tile forms at the depths of the MoE layer's two GEMMs (K = 7168
+    # for gate_up, 3072 for down): 65..128 left-over rows as a 128-row tile,
+    # 129..255 as a 256-row tile, <= 64 on the streaming kernel
+    _gemm_case([257, 300, 320, 321, 384, 385, 511, 64], 64, 7168, [0, 32, 64], 33, gather=True)
+    _gemm_case([260, 289, 330, 400, 449, 600, 33], 96, 3072, [0, 96], 34, gather=True, out_bf16=True)
+
+
+def test_gemm_left_over_rows_beyond_one_round_of_the_persistent_grid():
+    # 400 groups of 257..320 rows at N = 1024: each group's 1..64 rows past
+    # its 256-row tile go to the persistent streaming kernel, about 600
+    # 32-row slots x 4 column tiles = 2400 tiles for its 768 workgroups, so
+    # every workgroup runs several rounds.  Codes and scales are random bytes
+    # (any NVFP4 operand is valid input); A comes with its f16 form.
+    log("gemm left-over rounds")
+    rng = np.random.default_rng(40)
+    G, N, K = 400, 1024, 256
+    counts = rng.integers(257, 321, G)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    as_ = rng.integers(0x28, 0x49, (M, K // 16), dtype=np.uint8)
+    wc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    ws = rng.integers(0x20, 0x41, (G, N, K // 16), dtype=np.uint8)
+    wgs = rng.uniform(0.5, 2.0, (G, 1)).astype(np.float32)
+    ags = F32(1.0 / 64)
+    slots = int(((counts - 256 + 31) // 32).sum())
+    assert slots * (N // 256) > 3 * 768
+    d = dev()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    assert ops.gemm_reads_dq(G, M, K, M, True)
+    tiled = ops.prepare_weights(T(wc), T(ws))
+    a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16))
+    out = to_np(ops.grouped_gemm(T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), [0, N],
+                                 T(off), M, w_tiled=tiled, a_dq=a_dq))
+    worst = 0.0
+    for g in range(G):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        # every left-over row, and 8 rows of the group's 256-row tile
+        rows = np.concatenate([np.arange(r0 + 256, r1), r0 + rng.choice(256, 8, replace=False)])
+        ex, ab = exact_gemm_rows(ac[rows], as_[rows], wc[g], ws[g])
+        worst = max(worst, check_gemm(out[rows], ex, ab, float(F32(ags * wgs[g, 0])), K, False, "group %d" % g))
+    log("  %d left-over slots x %d column tiles; max err / rms = %.3g" % (slots, N // 256, worst))
+
+
 def test_gemm_big_tiles_split_k_one_group():
     # one group with few 256-row tiles: K is split over the tiles (f16 A);
     # the partial sums are reduced only on the tiles' rows, the left-over rows
