@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense bf16/f16 matrix peak, TFLOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense fp4/fp6 matrix peak, TFLOP/s (not an exact path for NVFP4)
 NVFP4_BYTES_PER_ELEM = 0.5 + 1.0 / 16.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 GEMM_SRC = os.path.join(ROOT, "block_scaled_fp4_03_amd", "csrc", "grouped_gemm.hip")
@@ -71,7 +72,7 @@ class Layer:
 
     def __init__(self, wl, device):
         import torch
-        from block_scaled_fp4_03_amd import ops, pipeline, workloads
+        from block_scaled_fp4_03_amd import lib, ops, pipeline, workloads
         self.wl = wl
         self.dev = device
         t0 = time.time()
@@ -98,14 +99,19 @@ class Layer:
         # the pipeline's default SiLU-requant path for this shape (in the first
         # GEMM's epilogue where that GEMM streams its weights)
         self.fused_default = self.w1.fuse_by_default(R, self.x.shape[0])
+        # workspace of the one-launch expert MLP (tile queue, slot counters)
+        self.mlp_ws = torch.empty(max(16, lib.load().nvfp4_moe_expert_mlp_workspace_size(wl.E, R)),
+                                  dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
 
-    def step(self, ev=None, dynamic=False, fused=False):
+    def step(self, ev=None, dynamic=False, fused=False, persistent=False):
         """One layer pass; if ev is given, record events around each op.  With
         `dynamic`, the activation global scales come from this batch on the
         device (amax of x before quantising it, amax of SiLU(g)*u before the
         re-quantisation) instead of the warmup scalars; with `fused`, SiLU-requant
-        runs in the first GEMM's epilogue (static scales only)."""
+        runs in the first GEMM's epilogue (static scales only); with
+        `persistent`, both GEMMs and the fused SiLU-requant run as one
+        persistent launch (nvfp4_moe_expert_mlp)."""
         from block_scaled_fp4_03_amd import ops
         import torch
         wl = self.wl
@@ -119,6 +125,17 @@ class Layer:
         rec("quantize")
         ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
         rec("route_permute")
+        if persistent:
+            G = self.w1.gs.shape[0]
+            hc, hs, y = ops.moe_expert_mlp(xc, xs, gs_x, srt, off, self.w1.tiled, self.w1.gs, self.w2.tiled,
+                                           self.w2.gs, R, wl.H, wl.I, self.gs_h, workspace=self.mlp_ws)
+            rec("gemm_l1")
+            rec("silu_mul_requant")
+            rec("gemm_l2")
+            out = ops.combine(y, inv, w)
+            rec("combine")
+            self._off = off
+            return out
         if not fused:
             gu = self.w1.gemm(xc, xs, gs_x, off, R, a_row_index=srt, a_dq=xdq[0] if xdq else None)
             rec("gemm_l1")
@@ -139,18 +156,39 @@ class Layer:
         self._off = off
         return out
 
+    def saturation(self):
+        """Share of the measured batch's 16-element blocks whose E4M3 scale
+        saturates at 448 with the warmup's activation global scales: of x,
+        and of the intermediate h (counted on one untimed pass)."""
+        import torch
+        from block_scaled_fp4_03_amd import ops
+        wl = self.wl
+        T = self.x.shape[0]
+        R = T * wl.k
+        xc, xs = ops.quantize(self.x, self.gs_x)
+        ids, w, off, srt, inv = ops.route_permute(self.logits, wl.k)
+        gu = self.w1.gemm(xc, xs, self.gs_x, off, R, a_row_index=srt)
+        hc, hs = ops.silu_mul_requant(gu, self.gs_h)
+        sat_x = int((xs == 0x7E).sum().item())
+        sat_h = int((hs == 0x7E).sum().item())
+        out = {"x_blocks": int(xs.numel()), "x_saturated": sat_x, "h_blocks": int(hs.numel()),
+               "h_saturated": sat_h}
+        del gu
+        torch.cuda.empty_cache()
+        return out
+
     def touched_experts(self):
         import torch
         off = self._off.cpu().numpy()
         return int((np.diff(off) > 0).sum())
 
 
-def time_layer(layer, steps, warmup, dynamic=False, fused=False):
+def time_layer(layer, steps, warmup, dynamic=False, fused=False, persistent=False):
     """Mean ms per step over `steps` back-to-back steps (after `warmup`), the
     mean per-op ms, and the p10/p50/p90 of the per-step times."""
     import torch
     for _ in range(warmup):
-        layer.step(dynamic=dynamic, fused=fused)
+        layer.step(dynamic=dynamic, fused=fused, persistent=persistent)
     torch.cuda.synchronize()
     names = ["start", "quantize", "route_permute", "gemm_l1", "silu_mul_requant", "gemm_l2", "combine"]
     ev = {n: [] for n in names}
@@ -159,7 +197,7 @@ def time_layer(layer, steps, warmup, dynamic=False, fused=False):
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(steps):
-        layer.step(ev, dynamic=dynamic, fused=fused)
+        layer.step(ev, dynamic=dynamic, fused=fused, persistent=persistent)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -187,6 +225,49 @@ def algorithmic(wl, n_touched, fused):
     return flops, l1_bytes, l1_flops
 
 
+def layer_bytes(wl, n_touched):
+    """Algorithmic HBM bytes of one layer pass: the touched experts' weights
+    (codes and block scales of W1 and W2), x in bf16, the router logits and
+    the bf16 output."""
+    per_expert = 3 * wl.H * wl.I * NVFP4_BYTES_PER_ELEM
+    return n_touched * per_expert + wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 2
+
+
+def measure_ceilings(steps=10):
+    """What the simplest kernels reach on this chip: a 4 GiB read with the
+    weight stream's non-temporal 16-byte loads (GB/s), and eight independent
+    f16 32x32x16 matrix-core chains per wave on register operands (TFLOP/s),
+    each timed with HIP events on the stream it runs on."""
+    import torch
+    from block_scaled_fp4_03_amd import ops
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev).fill_(3)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e-3
+
+    t_read = timed(lambda: ops.probe_hbm_read(buf, sink))
+    del buf
+    iters, wgs = 20000, 512
+    flops = ops.probe_mfma_f16(iters, wgs, sink)
+    t_mfma = timed(lambda: ops.probe_mfma_f16(iters, wgs, sink))
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round((1 << 32) / t_read / 1e9, 1),
+            "hbm_read_probe": "4 GiB read once, 16-byte non-temporal loads, 8 in flight per lane, 2048 workgroups",
+            "f16_mfma_tflops": round(flops / t_mfma / 1e12, 1),
+            "f16_mfma_probe": "v_mfma_f32_32x32x16_f16, 8 independent chains per wave, 4 waves per "
+                              "workgroup, 512 workgroups, operands alternating between two random sets"}
+
+
 def run_gpu(workload, steps, warmup, tokens=None):
     import dataclasses
     import torch
@@ -211,7 +292,8 @@ def run_gpu(workload, steps, warmup, tokens=None):
     flops, l1_bytes, l1_flops = algorithmic(wl, n_touched, fused)
     res = dict(ms=ms, per_op_ms=per_op, step_pct=pct, n_touched=n_touched, tokens_per_s=wl.T / (ms * 1e-3),
                tflops=flops / (ms * 1e-3) / 1e12, l1_bytes=l1_bytes, l1_flops=l1_flops, layer=layer, wl=wl,
-               fused=fused, wl_default_T=workloads.WORKLOADS[workload].T)
+               fused=fused, wl_default_T=workloads.WORKLOADS[workload].T,
+               layer_bytes=layer_bytes(wl, n_touched), saturation=layer.saturation())
     # the same layer with per-batch activation global scales computed on the
     # device (two extra amax passes; gs_h comes from the float32 gate_up, so
     # SiLU-requant runs as its own kernel), timed the same way
@@ -222,33 +304,77 @@ def run_gpu(workload, steps, warmup, tokens=None):
     if layer.w1.can_fuse_silu():
         oms, oper_op, _ = time_layer(layer, steps, warmup, fused=not fused)
         res["other"] = dict(fused=not fused, ms=oms, l1_ms=oper_op["gemm_l1"], tokens_per_s=wl.T / (oms * 1e-3))
+    # and with the expert MLP as one persistent launch (where the first GEMM
+    # streams its weights: the regime that launch is built for)
+    if fused:
+        pms, pper_op, ppct = time_layer(layer, steps, warmup, persistent=True)
+        res["persistent"] = dict(ms=pms, mlp_ms=pper_op["gemm_l1"] + pper_op["silu_mul_requant"] + pper_op["gemm_l2"],
+                                 tokens_per_s=wl.T / (pms * 1e-3), step_pct=ppct)
     return res
 
 
-def roofline(res, bound):
+def roofline(res, bound, ceilings=None):
     l1_ms = res["per_op_ms"]["gemm_l1"]
     if bound == "hbm":
         ach = res["l1_bytes"] / (l1_ms * 1e-3) / 1e9
         peak = HBM_PEAK_GBS
         unit = "GB/s"
+        ceil = ceilings and ceilings["hbm_read_gbs"]
     else:
         ach = res["l1_flops"] / (l1_ms * 1e-3) / 1e12
         peak = F16_MFMA_PEAK_TFLOPS
         unit = "TFLOP/s"
-    return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-            # (the committed counter runs cover the workloads at their own token counts)
-            "traffic": measured_traffic(res["wl"].name, SILU_PATHS[res["fused"]])
-            if res["wl"].T == res["wl_default_T"] else None,
-            "kernel": "nvfp4_grouped_gemm_silu_requant L1 (gate_up, SiLU-requant epilogue)" if res["fused"]
-            else "nvfp4_grouped_gemm L1 (gate_up)",
-            "kernel_ms": round(l1_ms, 4)}
+        ceil = ceilings and ceilings["f16_mfma_tflops"]
+    # (the committed counter runs cover the workloads at their own token counts)
+    traffic = measured_traffic(res["wl"].name, SILU_PATHS[res["fused"]]) \
+        if res["wl"].T == res["wl_default_T"] else None
+    out = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+           "traffic": traffic,
+           "algorithmic_bytes": int(res["l1_bytes"]),
+           "traffic_over_algorithmic": round(traffic / res["l1_bytes"], 3) if traffic else None,
+           "kernel": "nvfp4_grouped_gemm_silu_requant L1 (gate_up, SiLU-requant epilogue)" if res["fused"]
+           else "nvfp4_grouped_gemm L1 (gate_up)",
+           "kernel_ms": round(l1_ms, 4)}
+    if bound == "mfma":
+        out["frac_of_fp4_peak"] = round(ach / FP4_MFMA_PEAK_TFLOPS, 4)
+    if ceil:
+        out["measured_ceiling"] = ceil
+        out["frac_of_measured_ceiling"] = round(ach / ceil, 4)
+    return out
+
+
+def layer_roofline(res, bound, ceilings):
+    """The whole layer against its bound: at decode the algorithmic bytes of
+    the layer (touched experts' weights, x, logits, out) per step against HBM;
+    at prefill its algorithmic flops per step against the dense f16 and fp4
+    matrix peaks.  Second denominators: the measured ceilings."""
+    ms = res["ms"]
+    if bound == "hbm":
+        gbs = res["layer_bytes"] / (ms * 1e-3) / 1e9
+        out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": int(res["layer_bytes"])}
+        if ceilings:
+            out["measured_ceiling"] = ceilings["hbm_read_gbs"]
+            out["frac_of_measured_ceiling"] = round(gbs / ceilings["hbm_read_gbs"], 4)
+        return out
+    tf = res["tflops"]
+    out = {"bound": "mfma", "achieved": round(tf, 1), "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4),
+           "frac_of_fp4_peak": round(tf / FP4_MFMA_PEAK_TFLOPS, 4),
+           "fp4_peak": FP4_MFMA_PEAK_TFLOPS,
+           "flops_per_step": 6.0 * res["wl"].T * res["wl"].k * res["wl"].H * res["wl"].I}
+    if ceilings:
+        out["measured_ceiling"] = ceilings["f16_mfma_tflops"]
+        out["frac_of_measured_ceiling"] = round(tf / ceilings["f16_mfma_tflops"], 4)
+    return out
 
 
 def cpu_baseline(res, n_experts=24):
-    """The oracle timed on the host on a bounded sample: n_experts of the
-    touched experts with all their routed rows (L1, SiLU-requant, L2), plus
-    the per-token steps (quantise, route, permute, combine) for the whole
-    batch; the expert part is scaled by touched/n_experts."""
+    """The oracle, in its float32 mode (dequantise to float32, float32 BLAS
+    matmul), timed on the host on a bounded sample: n_experts of the touched
+    experts with all their routed rows (L1, SiLU-requant, L2), plus the
+    per-token steps (quantise, route, permute, combine) for the whole batch;
+    the expert part is scaled by touched/n_experts."""
     import torch
     from block_scaled_fp4_03_amd import workloads
     from oracle import moe, quant
@@ -293,9 +419,9 @@ def cpu_baseline(res, n_experts=24):
     soff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     t1 = time.perf_counter()
     gu = moe.grouped_gemm(xq[0], xq[1], gs_x, w1[0], w1[1], w1[2], [0, wl.I, 2 * wl.I], soff,
-                          a_row_index=srt[rows])
+                          a_row_index=srt[rows], mode="f32")
     hq = moe.silu_mul_requant(gu, gs_h)
-    y = moe.grouped_gemm(hq[0], hq[1], gs_h, w2[0], w2[1], w2[2], [0, wl.H], soff, out_dtype="bf16")
+    y = moe.grouped_gemm(hq[0], hq[1], gs_h, w2[0], w2[1], w2[2], [0, wl.H], soff, out_dtype="bf16", mode="f32")
     t_exp = time.perf_counter() - t1
     # combine over the whole batch with stand-in rows (same arithmetic)
     yfull = np.zeros((wl.T * wl.k, wl.H), np.float32)
@@ -311,7 +437,8 @@ def cpu_baseline(res, n_experts=24):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     return {"value": round(wl.T / est, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "%d of %d touched experts with all their %d routed rows (L1, SiLU-requant, L2), "
+            "sample": "oracle in its float32 mode (dequantise to float32, float32 library matmul); "
+                      "%d of %d touched experts with all their %d routed rows (L1, SiLU-requant, L2), "
                       "scaled by %d/%d; quantise, route, permute and combine over all %d tokens; "
                       "timed %.1fs of CPU work; host %d logical CPUs" % (
                           len(experts), n_t, int(sum(counts)), n_t, len(experts), wl.T, t_tok + t_exp,
@@ -507,6 +634,16 @@ def run_attn_out(steps, warmup):
     return line
 
 
+def persistent_line(res):
+    f = res.get("persistent")
+    if f is None:
+        return None
+    return {"expert_mlp": "one persistent launch (nvfp4_moe_expert_mlp)", "value": round(f["tokens_per_s"], 1),
+            "unit": "tokens/s", "ms_per_step": round(f["ms"], 4), "expert_mlp_ms": round(f["mlp_ms"], 4),
+            "layer_frac_hbm": round(res["layer_bytes"] / (f["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step_pct": {k: round(v, 4) for k, v in f["step_pct"].items()}}
+
+
 def other_path_line(res):
     f = res.get("other")
     if f is None:
@@ -548,6 +685,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    print("[bench] measured ceilings (HBM read probe, f16 MFMA loop)", file=sys.stderr, flush=True)
+    ceilings = measure_ceilings()
     main_res = run_gpu(args.workload, args.steps, args.warmup, args.tokens or None)
     if args.tokens:
         args.no_prefill = True
@@ -577,7 +716,11 @@ def main():
                                       "ms_per_step": round(main_res["dynamic"]["ms"], 4)},
         "silu_requant": SILU_PATHS[main_res["fused"]],
         "other_silu_requant_path": other_path_line(main_res),
-        "roofline": roofline(main_res, bound),
+        "persistent_expert_mlp": persistent_line(main_res),
+        "roofline": roofline(main_res, bound, ceilings),
+        "layer_roofline": layer_roofline(main_res, bound, ceilings),
+        "measured_ceilings": ceilings,
+        "block_scale_saturation": main_res["saturation"],
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -596,7 +739,9 @@ def main():
                            "other_silu_requant_path": other_path_line(pre),
                            "experts_touched": pre["n_touched"],
                            "per_op_ms": {k: round(v, 4) for k, v in pre["per_op_ms"].items()},
-                           "roofline": roofline(pre, "mfma")}
+                           "roofline": roofline(pre, "mfma", ceilings),
+                           "layer_roofline": layer_roofline(pre, "mfma", ceilings),
+                           "block_scale_saturation": pre["saturation"]}
     if args.workload == "decode" and not args.no_prefill:
         print("[bench] shared expert and MLA projections", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()

@@ -290,6 +290,98 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
   return finish(who, nvfp4::launch_grouped_gemm(a, s), s);
 }
 
+size_t nvfp4_moe_expert_mlp_workspace_size(int32_t G, int64_t R) {
+  if (G < 1 || R < 1) return 0;
+  return (size_t)nvfp4::moe_persistent_counters(G, R) * sizeof(int32_t);
+}
+
+static int32_t spin_limit_from_env() {
+  const char* v = getenv("NVFP4MOE_SPIN_LIMIT");
+  if (v && v[0]) {
+    const long n = strtol(v, nullptr, 10);
+    if (n >= 1 && n <= (1L << 30)) return (int32_t)n;
+  }
+  return 1 << 22;
+}
+
+int32_t nvfp4_moe_expert_mlp(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t x_rows,
+                             const int32_t* sorted_token_ids, const int32_t* expert_offsets, int32_t G, int64_t R,
+                             const uint8_t* w1_tiled, const float* w1_gs, const uint8_t* w2_tiled,
+                             const float* w2_gs, int64_t H, int64_t I, const float* h_gs, uint8_t* h_codes,
+                             uint8_t* h_scales, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  const char* who = "nvfp4_moe_expert_mlp";
+  if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
+  if (R < 0 || H < 256 || H % 256 || I < 256 || I % 256)
+    return fail(NVFP4_ESHAPE, "%s: need R >= 0, H and I >= 256 and multiples of 256", who);
+  if (R >= ((int64_t)1 << 31) || 2 * I >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 31))
+    return fail(NVFP4_ESHAPE, "%s: R, 2 I and H must be below 2^31", who);
+  if (x_rows < 0 || (!sorted_token_ids && x_rows < R) || (R > 0 && x_rows < 1))
+    return fail(NVFP4_ESHAPE, "%s: x_rows too small", who);
+  if (R == 0) return NVFP4_OK;
+  if (!x_codes || !x_scales || !x_gs || !expert_offsets || !w1_tiled || !w1_gs || !w2_tiled || !w2_gs || !h_gs ||
+      !h_codes || !h_scales || !y || !workspace)
+    return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (ws_bytes < nvfp4_moe_expert_mlp_workspace_size(G, R))
+    return fail(NVFP4_ESHAPE, "%s: workspace too small", who);
+  if (!aligned(x_codes, 16) || !aligned(w1_tiled, 16) || !aligned(w2_tiled, 16) || !aligned(h_codes, 16) ||
+      !aligned(y, 16) || !aligned(x_scales, 4) || !aligned(h_scales, 4) || !aligned(x_gs, 4) || !aligned(h_gs, 4) ||
+      !aligned(w1_gs, 4) || !aligned(w2_gs, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_token_ids, 4) ||
+      !aligned(workspace, 4))
+    return fail(NVFP4_EALIGN, "%s: codes, tiled weights and y must be 16-byte aligned, the rest 4-byte", who);
+  nvfp4::GemmArgs l1{};
+  l1.a_codes = x_codes;
+  l1.a_scales = x_scales;
+  l1.a_gs = x_gs;
+  l1.a_rows = sorted_token_ids ? x_rows : R;
+  l1.a_row_index = sorted_token_ids;
+  l1.w_codes = w1_tiled;
+  l1.w_tiled = 1;
+  l1.w_gs = w1_gs;
+  l1.n_seg[0] = 0;
+  l1.n_seg[1] = (int32_t)I;
+  for (int i = 2; i < 5; ++i) l1.n_seg[i] = (int32_t)(2 * I);
+  l1.n_segs = 2;
+  l1.group_offsets = expert_offsets;
+  l1.G = G;
+  l1.M = R;
+  l1.N = 2 * I;
+  l1.K = H;
+  l1.ld_out = 2 * I;
+  l1.fuse = 1;
+  l1.h_gs = h_gs;
+  l1.h_codes = h_codes;
+  l1.h_scales = h_scales;
+  nvfp4::GemmArgs l2{};
+  l2.a_codes = h_codes;
+  l2.a_scales = h_scales;
+  l2.a_gs = h_gs;
+  l2.a_rows = R;
+  l2.w_codes = w2_tiled;
+  l2.w_tiled = 1;
+  l2.w_gs = w2_gs;
+  l2.n_seg[0] = 0;
+  for (int i = 1; i < 5; ++i) l2.n_seg[i] = (int32_t)H;
+  l2.n_segs = 1;
+  l2.group_offsets = expert_offsets;
+  l2.G = G;
+  l2.M = R;
+  l2.N = H;
+  l2.K = I;
+  l2.out = y;
+  l2.out_bf16 = 1;
+  l2.ld_out = H;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ctr = (int32_t*)workspace;
+  const int32_t st = finish(who, nvfp4::launch_moe_persistent(l1, l2, ctr, spin_limit_from_env(), s), s);
+  if (st == NVFP4_OK && sync_check_enabled()) {
+    int32_t status = 0;
+    const hipError_t e = hipMemcpy(&status, ctr + 1, sizeof(status), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: status read failed: %s", who, hipGetErrorString(e));
+    if (status) return fail(NVFP4_EHIP, "%s: a dependency wait timed out (results unspecified)", who);
+  }
+  return st;
+}
+
 int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout) {
   if (G < 1 || M < 1 || K < 256 || K % 256 || a_rows < 1) return 0;
   if ((uint64_t)a_rows * (uint64_t)K * 2u >= ((uint64_t)1 << 32)) return 0;
@@ -404,6 +496,27 @@ int32_t moe_combine(const void* y, int32_t y_dtype, const int32_t* inv_perm, con
   return finish("moe_combine",
                 nvfp4::launch_combine(y, y_dtype == NVFP4_DTYPE_BF16, inv_perm, topk_w, T, k, H, residual, out, s),
                 s);
+}
+
+int32_t nvfp4_probe_hbm_read(const void* buf, int64_t bytes, void* sink, void* stream) {
+  const char* who = "nvfp4_probe_hbm_read";
+  if (bytes < 0 || bytes % 16) return fail(NVFP4_ESHAPE, "%s: bytes must be a non-negative multiple of 16", who);
+  if (bytes == 0) return NVFP4_OK;
+  if (!buf || !sink) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NVFP4_EALIGN, "%s: buf must be 16-byte aligned", who);
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_read_probe(buf, bytes, sink, s), s);
+}
+
+int32_t nvfp4_probe_mfma_f16(int64_t iters, int64_t workgroups, void* sink, void* stream) {
+  const char* who = "nvfp4_probe_mfma_f16";
+  if (iters < 0 || workgroups < 0 || workgroups > 65535)
+    return fail(NVFP4_ESHAPE, "%s: need iters >= 0 and 0 <= workgroups <= 65535", who);
+  if (iters == 0 || workgroups == 0) return NVFP4_OK;
+  if (!sink) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(sink, 4)) return fail(NVFP4_EALIGN, "%s: sink must be 4-byte aligned", who);
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_mfma_probe(iters, workgroups, sink, s), s);
 }
 
 }  // extern "C"

@@ -574,9 +574,49 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
 // reaches a higher share of the HBM bandwidth than ordinary loads on this chip
 // (where several tiles of a group read the same weights, ordinary loads keep
 // the repeats in the caches)
+// Dependency hooks of the persistent expert kernel (all null elsewhere):
+// `signal` is incremented (agent scope, release) once a tile's output is
+// stored; before its first A load, a wave waits (agent scope, acquire) until
+// `*wait_ctr` reaches `wait_target`, giving up after `spin_limit` polls and
+// then recording the failure in `*status`.  The weight loads of the first
+// two half-steps are issued before the wait: they do not depend on A.
+struct TileSync {
+  int32_t* signal = nullptr;
+  const int32_t* wait_ctr = nullptr;
+  int32_t wait_target = 0;
+  int32_t spin_limit = 0;
+  int32_t* status = nullptr;
+};
+
+// Polls are relaxed; one acquire fence follows the last poll, so the caches
+// are invalidated once per wait, not once per poll.
+__device__ __forceinline__ void tile_wait(const TileSync& sy) {
+  if (!sy.wait_ctr) return;
+  int32_t polls = 0;
+  while (__hip_atomic_load(sy.wait_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < sy.wait_target) {
+    if (++polls >= sy.spin_limit) {
+      // give up: the results are unspecified, the failure is recorded
+      if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(sy.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// One signal per workgroup: every wave's stores are complete before the
+// barrier, then one release (cache write-back) and one atomic add.
+__device__ __forceinline__ void tile_signal(const TileSync& sy) {
+  if (!sy.signal) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sy.signal, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int NBW, int RB, bool FUSE, bool SPLIT, bool NT>
 __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
-                                              int wave, int lane, int64_t ks0, int64_t ks1, int split) {
+                                              int wave, int lane, int64_t ks0, int64_t ks1, int split,
+                                              const TileSync& sy = TileSync()) {
   static_assert(!FUSE || NBW == 2, "the fused epilogue pairs one gate and one up column block");
   constexpr int BN = 4 * NBW * 32;
   const int c = lane & 31;
@@ -621,7 +661,7 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     u32x4 a0[RB], a1[RB], w0[NBW], w1[NBW];
     uint32_t as[RB], ws[NBW];
   };
-  auto load = [&](int64_t hs, Ops& d) {
+  auto load_a = [&](int64_t hs, Ops& d) {
     const int64_t ks = hs >> 1, h = hs & 1;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -635,6 +675,9 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
         d.as[rb] = 0u;
       }
     }
+  };
+  auto load_w = [&](int64_t hs, Ops& d) {
+    const int64_t ks = hs >> 1, h = hs & 1;
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
       const uint8_t* t = w_t[cb] + ks * kTileBytes;
@@ -651,6 +694,10 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
         d.ws[cb] = *ts;
       }
     }
+  };
+  auto load = [&](int64_t hs, Ops& d) {
+    load_a(hs, d);
+    load_w(hs, d);
   };
   auto compute = [&](const Ops& o) {
 #pragma unroll
@@ -672,8 +719,16 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   // with loads pending)
   const int64_t h0 = 2 * ks0, nhs = 2 * ks1;
   Ops s0, s1, s2;
-  load(h0, s0);
-  load(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+  if (sy.wait_ctr) {
+    load_w(h0, s0);
+    load_w(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+    tile_wait(sy);
+    load_a(h0, s0);
+    load_a(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+  } else {
+    load(h0, s0);
+    load(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+  }
   // (the last two half-steps reload the last one: no branch around a load)
   auto step = [&](int64_t hs, const Ops& cur, Ops& ld) {
     load(hs + 2 < nhs ? hs + 2 : nhs - 1, ld);
@@ -777,6 +832,113 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
         stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
     }
   }
+}
+
+// Number of bm-row tiles over all groups (a last partial tile counts), from
+// offsets staged in local memory; every lane gets the result.
+__device__ __forceinline__ int64_t count_tiles(const int32_t* __restrict__ offsets, int G, int64_t M, int bm) {
+  const int lane = threadIdx.x & 63;
+  int64_t total = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int32_t tiles = 0;
+    if (g < G) {
+      const int64_t lo = clampv<int64_t>(offsets[g], 0, M);
+      int64_t hi = clampv<int64_t>(offsets[g + 1], 0, M);
+      if (hi < lo) hi = lo;
+      tiles = (int32_t)((hi - lo + bm - 1) / bm);
+    }
+    total += __builtin_amdgcn_readlane(wave_incl_scan(tiles), 63);
+  }
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// gemm_moe_persistent: the routed experts' MLP in one launch.  A grid of a
+// few workgroups per compute unit takes tiles from a device queue (one
+// atomic counter) in a fixed order: first every tile of the first GEMM
+// (stacked gate_up, SiLU-requant epilogue writing h; slot-major over the
+// 32-row slots of every group, then the column tiles), then every tile of
+// the second GEMM (down, bf16 y; same slots).  A second-GEMM tile of slot s
+// needs the whole h rows of that slot: each first-GEMM workgroup adds 1 to
+// done[s] (agent scope, release) once all its waves have stored their h
+// blocks, and the second-GEMM waves of slot s issue their first weight
+// loads, then wait until done[s] counts all the first GEMM's column tiles
+// (relaxed polls, then one agent-scope acquire) before loading h.  So the second GEMM's weight stream starts while the
+// first GEMM's last tiles still run, and no launch boundary separates them.
+// A tile is taken only by a running workgroup, and every tile of the first
+// GEMM is taken before any of the second and never waits, so a waiting tile
+// always depends on tiles that running workgroups finish: the launch cannot
+// deadlock, whatever the number of resident workgroups.  The waits are
+// bounded (spin_limit polls) and a timeout is recorded in ctr[1].
+// ctr: [0] queue, [1] status, [2 ..] done per slot; zeroed before the launch.
+__global__ __launch_bounds__(256) void gemm_moe_persistent(GemmArgs p1, GemmArgs p2, int32_t* ctr, int64_t n_tiles1,
+                                                          int64_t n_tiles2, int64_t max_slots, int32_t spin_limit) {
+  __shared__ int32_t s_off[kMaxGroups + 1];
+  __shared__ int64_t s_next[2];
+  for (int i = threadIdx.x; i <= p1.G; i += blockDim.x) s_off[i] = p1.group_offsets[i];
+  if (threadIdx.x == 0) s_next[0] = atomicAdd(ctr, 1);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (at most the counters there are: offsets that are not a partition of
+  // [0, M) cannot index past them)
+  const int64_t slots = std::min<int64_t>(count_tiles(s_off, p1.G, p1.M, 32), max_slots);
+  const int64_t tiles1 = slots * n_tiles1;
+  const int64_t total = tiles1 + slots * n_tiles2;
+  const int64_t nks1 = p1.K / 256, nks2 = p2.K / 256;
+  const int32_t h_blocks = (int32_t)n_tiles1;          // column tiles of the first GEMM per slot
+  int buf = 0;
+  int64_t t = s_next[0];
+  while (t < total) {
+    // the next tile's index is fetched while this one runs
+    if (threadIdx.x == 0) s_next[buf ^ 1] = atomicAdd(ctr, 1);
+    // the lane index made opaque per tile, so that per-lane values are not
+    // hoisted out of the loop and kept live across tiles
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const bool first = t < tiles1;
+    const int64_t u = first ? t : t - tiles1;
+    const int64_t nt_count = first ? n_tiles1 : n_tiles2;
+    const int64_t slot = u / nt_count;
+    const int64_t nt = u - slot * nt_count;
+    int g;
+    int64_t row0, row1;
+    if (find_tile(s_off, p1.G, p1.M, slot, 32, 1, 0, 0, g, row0, row1)) {
+      g = __builtin_amdgcn_readfirstlane(g);
+      const bool whole = row0 == s_off[g] && row1 == s_off[g + 1];
+      TileSync sy;
+      sy.status = ctr + 1;
+      sy.spin_limit = spin_limit;
+      if (first) {
+        if (whole)
+          stream32_tile<2, 1, true, false, true>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy);
+        else
+          stream32_tile<2, 1, true, false, false>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy);
+        // every wave's h stores have reached memory, then one signal for
+        // the workgroup's column tile
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        sy.signal = ctr + 2 + slot;
+        tile_signal(sy);
+      } else {
+        sy.wait_ctr = ctr + 2 + slot;
+        sy.wait_target = h_blocks;
+        if (whole)
+          stream32_tile<2, 1, false, false, true>(p2, g, row0, row1, nt, wave, ln, 0, nks2, 0, sy);
+        else
+          stream32_tile<2, 1, false, false, false>(p2, g, row0, row1, nt, wave, ln, 0, nks2, 0, sy);
+      }
+    }
+    __syncthreads();
+    buf ^= 1;
+    t = s_next[buf];
+  }
+}
+
+__global__ void zero_i32(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
 }
 
 // Split-K tile for ranges of at most two 256-k steps (32 rows, 4 waves x
@@ -1552,6 +1714,35 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_stream32<NBW, 1, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0, work);
+  return hipGetLastError();
+}
+
+int64_t moe_persistent_counters(int64_t G, int64_t M) { return 2 + (M + 31) / 32 + G; }
+
+hipError_t launch_moe_persistent(const GemmArgs& l1, const GemmArgs& l2, int32_t* ctr, int32_t spin_limit,
+                                 hipStream_t s) {
+  if (l1.M == 0) return hipSuccess;
+  if (l1.G < 1 || l1.G > kMaxGroups) return hipErrorInvalidValue;
+  const int64_t n_ctr = moe_persistent_counters(l1.G, l1.M);
+  hipLaunchKernelGGL(zero_i32, dim3((unsigned)std::min<int64_t>((n_ctr + 255) / 256, 1024)), dim3(256), 0, s, ctr,
+                     n_ctr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // three workgroups per compute unit (the streaming tiles' register use)
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+        hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  constexpr int NBW = 2;
+  const int64_t n_tiles1 = (l1.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+  const int64_t n_tiles2 = (l2.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+  hipLaunchKernelGGL(gemm_moe_persistent, dim3((unsigned)(3 * cus)), dim3(256), 0, s, l1, l2, ctr, n_tiles1,
+                     n_tiles2, n_ctr - 2, spin_limit);
   return hipGetLastError();
 }
 

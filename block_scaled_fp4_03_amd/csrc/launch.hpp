@@ -100,6 +100,12 @@ size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled)
 // true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+// the expert MLP in one persistent launch: l1 the first GEMM with the fused
+// SiLU-requant epilogue, l2 the second GEMM over the same groups (A = h);
+// ctr holds moe_persistent_counters(G, M) int32 counters
+int64_t moe_persistent_counters(int64_t G, int64_t M);
+hipError_t launch_moe_persistent(const GemmArgs& l1, const GemmArgs& l2, int32_t* ctr, int32_t spin_limit,
+                                 hipStream_t s);
 
 hipError_t launch_fp8_quantize(const float* w, int64_t N, int64_t K, int64_t ld_w, uint8_t* codes, float* scales,
                                hipStream_t s);
@@ -112,6 +118,9 @@ hipError_t launch_silu_mul_requant(const void* gu, bool bf16, int64_t M, int64_t
 int64_t silu_amax_chunks(int64_t M, int64_t I);
 hipError_t launch_silu_mul_global_scale(const void* gu, bool bf16, int64_t M, int64_t I, int64_t ld,
                                         float* gs_out, float* partial, hipStream_t s);
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, void* sink, hipStream_t s);
+hipError_t launch_mfma_probe(int64_t iters, int64_t workgroups, void* sink, hipStream_t s);
 
 hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const float* w, int64_t T,
                           int k, int64_t H, const uint16_t* residual, uint16_t* out, hipStream_t s);

@@ -32,6 +32,9 @@ SIGNATURES = {
     "nvfp4_grouped_gemm_silu_requant": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
                                                _P, _P, _P, _P, _P]),
     "nvfp4_grouped_gemm_reads_dq": (_I32, [_I32, _I64, _I64, _I64, _I32]),
+    "nvfp4_moe_expert_mlp_workspace_size": (_SZ, [_I32, _I64]),
+    "nvfp4_moe_expert_mlp": (_I32, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P,
+                                    _P, _P, _SZ, _P]),
     "nvfp4_prepared_weight_bytes": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_prepare_weights": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "silu_mul_requant": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -40,6 +43,8 @@ SIGNATURES = {
     "fp8_quantize_weight": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "fp8_weight_gemm": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _I32, _I64, _P]),
     "moe_combine": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I64, _P, _P, _P]),
+    "nvfp4_probe_hbm_read": (_I32, [_P, _I64, _P, _P]),
+    "nvfp4_probe_mfma_f16": (_I32, [_I64, _I64, _P, _P]),
 }
 
 _lib = None

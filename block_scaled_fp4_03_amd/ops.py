@@ -207,6 +207,27 @@ def grouped_gemm_silu_requant(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offs
     return (codes, scales, dq) if want_dq else (codes, scales)
 
 
+def moe_expert_mlp(x_codes, x_scales, x_gs, sorted_ids, offsets, w1_tiled, w1_gs, w2_tiled, w2_gs, R, H, I, gs_h,
+                   workspace=None):
+    """The experts' MLP in one persistent launch (nvfp4_moe_expert_mlp):
+    returns (h_codes [R, I/2], h_scales [R, I/16], y bf16 [R, H]).  The
+    workspace (the tile queue and per-slot counters) is allocated here
+    unless given."""
+    _check_dev(x_codes, x_scales, x_gs, sorted_ids, offsets, w1_tiled, w1_gs, w2_tiled, w2_gs, gs_h, workspace)
+    G = w1_gs.shape[0]
+    dev = x_codes.device
+    hc = torch.empty(R, I // 2, dtype=torch.uint8, device=dev)
+    hs = torch.empty(R, I // 16, dtype=torch.uint8, device=dev)
+    y = torch.empty(R, H, dtype=torch.bfloat16, device=dev)
+    need = _lib.load().nvfp4_moe_expert_mlp_workspace_size(G, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _lib.call("nvfp4_moe_expert_mlp", _p(x_codes), _p(x_scales), _p(x_gs), x_codes.shape[0], _p(sorted_ids),
+              _p(offsets), G, R, _p(w1_tiled), _p(w1_gs), _p(w2_tiled), _p(w2_gs), H, I, _p(gs_h), _p(hc), _p(hs),
+              _p(y), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    return hc, hs, y
+
+
 def silu_mul_requant(gate_up, gs_h, codes=None, scales=None, dq=None):
     """gate_up [M, 2I] f32/bf16 -> NVFP4 h (codes [M, I/2], scales [M, I/16]);
     dq as in quantize."""
@@ -279,3 +300,17 @@ def fp8_weight_gemm(x, codes, scales, out_dtype=torch.bfloat16, out=None):
     _lib.call("fp8_weight_gemm", _p(x), M, K, x.stride(0), _p(codes), _p(scales), N, _p(out), _dtype(out),
               out.stride(0), _stream())
     return out
+
+
+def probe_hbm_read(buf, sink):
+    """Measurement probe: read all of buf (a contiguous GPU tensor) once."""
+    _check_dev(buf, sink)
+    _lib.call("nvfp4_probe_hbm_read", _p(buf), buf.numel() * buf.element_size() // 16 * 16, _p(sink), _stream())
+
+
+def probe_mfma_f16(iters, workgroups, sink):
+    """Measurement probe: workgroups * 4 * iters * 8 * 32768 f16 matrix-core
+    flops on register operands.  Returns that flop count."""
+    _check_dev(sink)
+    _lib.call("nvfp4_probe_mfma_f16", int(iters), int(workgroups), _p(sink), _stream())
+    return float(workgroups) * 4 * iters * 8 * 32768

@@ -140,13 +140,31 @@ def moe_weights(wl, device, seed=0, experts=None, tiled=True, drop_rows=False, n
     return w1, w2
 
 
-def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xdq=None, fused=None):
+def can_persist(w1, w2):
+    """Whether the expert MLP can run as one persistent launch (tiled
+    weights, H and I multiples of 256)."""
+    G, N, K2 = w1.codes.shape
+    return w1.can_fuse_silu() and w2.tiled is not None and (2 * K2) % 256 == 0 and (N // 2) % 256 == 0
+
+
+def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xdq=None, fused=None,
+                persistent=False):
     """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` (static
     gs_h and a fusable W1) the re-quantisation runs in the L1 epilogue, with
     identical results and no float32 gate_up in memory; None picks
     w1.fuse_by_default (fused where L1 streams its weights, a separate kernel
     where it runs 256-row tiles or splits K).  gs_h None computes it from
-    this batch's gate_up.  Returns (y bf16, stages)."""
+    this batch's gate_up.  With `persistent`, both GEMMs and the fused
+    SiLU-requant run as one persistent launch (nvfp4_moe_expert_mlp; static
+    gs_h): h is identical, y identical in the streaming regime.  Returns (y
+    bf16, stages)."""
+    if persistent:
+        if gs_h is None or not can_persist(w1, w2):
+            raise ValueError("the persistent launch needs a static gs_h and tiled weights with H, I % 256 == 0")
+        G, N, K2 = w1.codes.shape
+        hc, hs, y = ops.moe_expert_mlp(xc, xs, gs_x, a_row_index, off, w1.tiled, w1.gs, w2.tiled, w2.gs, R, 2 * K2,
+                                       N // 2, gs_h)
+        return y, dict(hc=hc, hs=hs, y=y, gs_h=gs_h)
     if fused is None:
         fused = gs_h is not None and w1.fuse_by_default(R, a_rows)
     if fused and (gs_h is None or not w1.can_fuse_silu()):
@@ -167,7 +185,8 @@ def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xd
     return y, st
 
 
-def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared=0, residual=None):
+def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared=0, residual=None,
+              persistent=False):
     """Routed MoE layer.  x [T, H] bf16, logits [T, E] f32, gs_x/gs_h
     1-element f32 tensors: static activation global scales (from a warmup
     batch), or None for dynamic ones computed on the device from this batch
@@ -180,8 +199,9 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared
     1 (moe_route_permute_shared), so one grouped GEMM per projection covers
     the routed and the shared experts, and the combine adds the shared
     outputs after the routed slots.  residual (bf16 [T, H]) is added by the
-    combine before its one rounding.  Returns out [T, H] bf16 (and the
-    stages)."""
+    combine before its one rounding.  `persistent` runs the expert MLP as
+    one persistent launch (see _expert_mlp).  Returns out [T, H] bf16 (and
+    the stages)."""
     T, H = x.shape
     if w1.codes.shape[0] != logits.shape[1] + n_shared:
         raise ValueError("w1 holds %d groups; expected %d routed + %d shared" %
@@ -191,10 +211,10 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared
         gs_x = ops.global_scale(x.reshape(1, -1))
     # the many-row GEMM tiles read A in exactly dequantised f16 form, which the
     # producers write alongside the codes when it will be read
-    xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) else None)
+    xc, xs, *xdq = ops.quantize(x, gs_x, dq=True if w1.reads_dq(R, T) and not persistent else None)
     ids, w, off, sorted_ids, inv = ops.route_permute(logits, k, n_shared)
     y, st = _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, T, a_row_index=sorted_ids,
-                        xdq=xdq[0] if xdq else None, fused=fused)
+                        xdq=xdq[0] if xdq else None, fused=fused, persistent=persistent)
     out = ops.combine(y, inv, w, residual=residual)
     if keep:
         st.update(xc=xc, xs=xs, ids=ids, w=w, offsets=off, sorted_ids=sorted_ids, inv=inv, gs_x=gs_x)

@@ -80,9 +80,8 @@ class Workload:
 WORKLOADS = {
     "tiny": Workload("tiny", "moe", T=16, H=256, I=128, E=8, k=2),
     "shared": Workload("shared", "shared", T=128, outlier_frac=0.001),
-    "decode": Workload("decode", "moe", T=256, E=384, k=6, weights_on_device=True, warmup_tokens=2),
-    "prefill": Workload("prefill", "moe", T=8192, E=384, k=6, zipf=1.1, weights_on_device=True,
-                        warmup_tokens=2),
+    "decode": Workload("decode", "moe", T=256, E=384, k=6, weights_on_device=True),
+    "prefill": Workload("prefill", "moe", T=8192, E=384, k=6, zipf=1.1, weights_on_device=True),
     "mla": Workload("mla", "mla", T=4096),
     "attn_out": Workload("attn_out", "attn_out", T=4096, warmup_tokens=64),
 }

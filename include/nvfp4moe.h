@@ -326,6 +326,64 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
                                         uint16_t* h_dq, void* stream);
 
 /*
+ * nvfp4_moe_expert_mlp - the routed experts' MLP in ONE persistent launch:
+ * the first grouped GEMM over the stacked gate_up weights with SiLU(gate) *
+ * up re-quantised in its epilogue, then the second grouped GEMM over the
+ * down weights, taken from one device tile queue so that the second GEMM's
+ * weight stream starts while the first GEMM's last tiles still run.  This is
+ * the single persistent launch of a MegaMoE-style layer (page
+ * "CURRENT_BUG.md - DeepSeek-V4 Blackwell NVFP4", section "Architecture
+ * Notes", which describes a persistent grouped GEMM for MegaMoE) for the
+ * pipeline of page "Current Bug: vLLM produces empty/garbage output"
+ * (revision e8b289e, section "Phase 1: CuTeDSL Shared Expert Kernel": GEMM,
+ * SiLU, re-quant, GEMM).
+ *   Equivalent to nvfp4_grouped_gemm_silu_requant(x_codes, x_scales, x_gs,
+ *   x_rows, sorted_token_ids, NULL, w1_tiled, w1_gs, expert_offsets, G, R,
+ *   I, H, h_gs, h_codes, h_scales, NULL) followed by
+ *   nvfp4_grouped_gemm(h_codes, h_scales, h_gs, R, NULL, NULL, w2_tiled,
+ *   NULL, NVFP4_LAYOUT_TILED, w2_gs, {0, H}, 1, expert_offsets, G, R, H, I,
+ *   y, NVFP4_DTYPE_BF16, H, NULL, 0): h is identical; y is identical where
+ *   that second call streams its weights in 32- or 64-row slots (few rows
+ *   per group, the decode regime) and within the float32 summation bound of
+ *   the exact contraction in every case.  Every group is processed in
+ *   32-row slots, so the launch suits few rows per group; with many rows per
+ *   group the two calls (256-row tiles) are faster.
+ *   x_codes, x_scales  NVFP4 layer input [x_rows, H/2], [x_rows, H/16];
+ *                      x_gs ONE float32.
+ *   sorted_token_ids   [R] int32 or NULL: row m of the experts' input is
+ *                      x row sorted_token_ids[m] (moe_route_permute).
+ *   expert_offsets     [G+1] int32 (moe_route_permute / _shared).
+ *   w1_tiled, w1_gs    nvfp4_prepare_weights buffer of the stacked [G, 2I, H]
+ *                      weights (gate rows [0, I), up rows [I, 2I)) and
+ *                      their [G, 2] global scales (gate, up).
+ *   w2_tiled, w2_gs    nvfp4_prepare_weights buffer of [G, H, I] and [G, 1].
+ *   h_gs               ONE float32, the global scale of h.
+ *   h_codes, h_scales  out [R, I/2], [R, I/16] (also the second GEMM's A).
+ *   y                  out [R, H] bf16 (uint16 storage).
+ *   workspace          nvfp4_moe_expert_mlp_workspace_size(G, R) bytes of
+ *                      device memory (4-byte aligned): the tile queue, a
+ *                      status word and one completion counter per 32-row
+ *                      slot, reset by the call itself.  Calls sharing a
+ *                      workspace must not overlap.
+ * Dependency waits are bounded (about 2^22 polls, or NVFP4MOE_SPIN_LIMIT
+ * from the environment): if one gives up, the launch still finishes,
+ * int32 workspace word 1 is set non-zero and the results are unspecified
+ * (under NVFP4MOE_SYNC_CHECK=1 the call then returns NVFP4_EHIP).
+ * Errors: EINVAL for null pointers; ESHAPE unless 1 <= G <=
+ * NVFP4_MAX_EXPERTS, R >= 0, H and I are multiples of 256 (>= 256), x_rows
+ * as for nvfp4_grouped_gemm, the workspace is large enough; EALIGN as
+ * stated.  R == 0 is a no-op.
+ */
+size_t nvfp4_moe_expert_mlp_workspace_size(int32_t G, int64_t R);
+int32_t nvfp4_moe_expert_mlp(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                             int64_t x_rows, const int32_t* sorted_token_ids,
+                             const int32_t* expert_offsets, int32_t G, int64_t R,
+                             const uint8_t* w1_tiled, const float* w1_gs, const uint8_t* w2_tiled,
+                             const float* w2_gs, int64_t H, int64_t I, const float* h_gs,
+                             uint8_t* h_codes, uint8_t* h_scales, uint16_t* y, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/*
  * nvfp4_grouped_gemm_reads_dq - 1 if nvfp4_grouped_gemm with these sizes
  * (G groups, M rows, depth K, a_rows stored A rows) and weight layout reads
  * a_dq when it is given (its 256-row tiles do), else 0.  Lets a caller
@@ -449,6 +507,31 @@ int32_t fp8_quantize_weight(const float* w, int64_t N, int64_t K, int64_t ld_w, 
 int32_t fp8_weight_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* w_codes,
                         const float* w_scales, int64_t N, void* out, int32_t out_dtype, int64_t ld_out,
                         void* stream);
+
+/*
+ * Measurement probes (not part of the pipeline).  The bench reports the
+ * pipeline's rates against the vendor peaks and, as second denominators,
+ * against what these simplest kernels reach on the same chip; the pages
+ * publish no throughput of their own to compare with.
+ *
+ * nvfp4_probe_hbm_read - read `bytes` of device memory once with 16-byte
+ * non-temporal loads, grid-stride over 2048 workgroups of 256 lanes, eight
+ * loads in flight per lane.  Nothing is written unless the folded value of
+ * the data equals one fixed 32-bit constant; `sink` is 4 bytes of device
+ * memory for that case.  Errors: ESHAPE unless bytes >= 0 and
+ * bytes % 16 == 0; EINVAL for null pointers; EALIGN unless buf is 16-byte
+ * aligned.
+ *
+ * nvfp4_probe_mfma_f16 - `workgroups` workgroups of four waves; each wave
+ * runs `iters` rounds of eight independent v_mfma_f32_32x32x16_f16 chains
+ * on register operands that alternate between two sets of pseudo-random
+ * values.  Floating-point operations: workgroups * 4 * iters * 8 * 32768.
+ * `sink` as above (4 bytes, written only for one fixed float value).
+ * Errors: ESHAPE unless iters >= 0 and 0 <= workgroups <= 65535; EINVAL for
+ * a null sink.
+ */
+int32_t nvfp4_probe_hbm_read(const void* buf, int64_t bytes, void* sink, void* stream);
+int32_t nvfp4_probe_mfma_f16(int64_t iters, int64_t workgroups, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -351,6 +351,120 @@ def test_gemm_split_k_one_small_group():
         check_gemm(o, ex, ab, float(F32(F32(ags) * wg)), 2048, False, "split-K")
 
 
+def _mlp_case(counts, H, I, seed, gather=True):
+    """nvfp4_moe_expert_mlp (one persistent launch) against the two launches
+    it replaces and the oracle: h bit-identical to the fused first GEMM and
+    to the oracle's SiLU-requant of the unfused first GEMM's float32 output;
+    y bit-identical to the second grouped GEMM (same streaming tiles) and
+    within the float32 summation bound of the exact contraction of h."""
+    log("expert mlp", counts if len(counts) < 12 else (len(counts), sum(counts)), H, I, gather)
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    R = int(sum(counts))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = max(R // 3, 1) if gather else R
+    xc, xs, xg = oracle_nvfp4(_x(T, H, seed))
+    sorted_ids = rng.integers(0, T, R).astype(np.int32) if gather else None
+    w1c = np.empty((G, 2 * I, H // 2), np.uint8)
+    w1s = np.empty((G, 2 * I, H // 16), np.uint8)
+    w1g = np.empty((G, 2), np.float32)
+    w2c = np.empty((G, H, I // 2), np.uint8)
+    w2s = np.empty((G, H, I // 16), np.uint8)
+    w2g = np.empty((G, 1), np.float32)
+    for g in range(G):
+        wf = (rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32)
+        for sg in range(2):
+            c, sc, gg = oracle_nvfp4(wf[sg * I:(sg + 1) * I])
+            w1c[g, sg * I:(sg + 1) * I], w1s[g, sg * I:(sg + 1) * I], w1g[g, sg] = c, sc, gg
+        w2c[g], w2s[g], w2g[g, 0] = oracle_nvfp4((rng.standard_normal((H, I)) * 0.02).astype(np.float32))
+    d = dev()
+    Td = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    x_gs = torch.tensor([xg], device=d)
+    gs_h = torch.tensor([0.004], dtype=torch.float32, device=d)
+    t1 = ops.prepare_weights(Td(w1c), Td(w1s))
+    t2 = ops.prepare_weights(Td(w2c), Td(w2s))
+    sid = Td(sorted_ids) if gather else None
+    offs = Td(off)
+    hc, hs, y = ops.moe_expert_mlp(Td(xc), Td(xs), x_gs, sid, offs, t1, Td(w1g), t2, Td(w2g), R, H, I, gs_h)
+    # the two launches it replaces
+    hc2, hs2 = ops.grouped_gemm_silu_requant(Td(xc), Td(xs), x_gs, t1, Td(w1g), offs, R, I, H, gs_h,
+                                             a_row_index=sid)
+    y2 = ops.grouped_gemm(hc2, hs2, gs_h, Td(w2c), Td(w2s), Td(w2g), [0, H], offs, R, w_tiled=t2,
+                          out_dtype=torch.bfloat16, workspace=False)
+    gu = to_np(ops.grouped_gemm(Td(xc), Td(xs), x_gs, Td(w1c), Td(w1s), Td(w1g), [0, I, 2 * I], offs, R,
+                                a_row_index=sid, w_tiled=t1, workspace=False))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(hc), to_np(hc2)) and np.array_equal(to_np(hs), to_np(hs2))
+    hc_o, hs_o = moe.silu_mul_requant(gu, F32(0.004))
+    assert np.array_equal(to_np(hc), hc_o) and np.array_equal(to_np(hs), hs_o)
+    yn = to_np(y)
+    assert np.array_equal(yn.view(np.uint32), to_np(y2).view(np.uint32))
+    hcn, hsn = to_np(hc), to_np(hs)
+    for g in range(G):
+        r0, r1 = off[g], off[g + 1]
+        if r1 > r0:
+            ex, ab = exact_gemm_rows(hcn[r0:r1], hsn[r0:r1], w2c[g], w2s[g])
+            check_gemm(yn[r0:r1], ex, ab, float(F32(F32(0.004) * w2g[g, 0])), I, True, "expert mlp group %d" % g)
+
+
+def test_moe_expert_mlp_one_launch_matches_two():
+    # decode-like: few rows per group, empty groups, gathered rows
+    rng = np.random.default_rng(50)
+    counts = rng.integers(0, 9, 48).tolist()
+    counts[0] = 0
+    counts[-1] = 0
+    _mlp_case(counts, 512, 256, 51)
+    # groups of several 32-row slots (slot tiles that are not the whole group)
+    _mlp_case([70, 0, 33, 5, 100], 256, 512, 52)
+    # one group, rows not gathered
+    _mlp_case([40], 768, 256, 53, gather=False)
+
+
+def test_moe_expert_mlp_many_tiles_in_the_queue():
+    # 300 groups: about 9k tiles through the device queue for 768 workgroups
+    rng = np.random.default_rng(54)
+    _mlp_case(rng.integers(0, 7, 300).tolist(), 256, 256, 55)
+
+
+def test_moe_expert_mlp_bounded_wait_gives_up_and_finishes():
+    # failure handling forced from the host: with one poll allowed, second-GEMM
+    # tiles that start before their slot's h is complete give up at once; the
+    # launch must still finish (no hang), the timeout is recorded in the
+    # status word, and a normal call afterwards is correct again
+    import os
+    rng = np.random.default_rng(56)
+    counts = rng.integers(1, 9, 200).tolist()
+    R, H, I = int(sum(counts)), 512, 256
+    d = dev()
+    G = len(counts)
+    xc = torch.randint(0, 256, (R, H // 2), dtype=torch.uint8, device=d)
+    xs = torch.full((R, H // 16), 0x38, dtype=torch.uint8, device=d)
+    w1 = ops.prepare_weights(torch.randint(0, 256, (G, 2 * I, H // 2), dtype=torch.uint8, device=d),
+                             torch.full((G, 2 * I, H // 16), 0x30, dtype=torch.uint8, device=d))
+    w2 = ops.prepare_weights(torch.randint(0, 256, (G, H, I // 2), dtype=torch.uint8, device=d),
+                             torch.full((G, H, I // 16), 0x30, dtype=torch.uint8, device=d))
+    g1 = torch.full((G, 2), 0.01, device=d)
+    g2 = torch.full((G, 1), 0.01, device=d)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(d)
+    one = torch.ones(1, device=d)
+    ws = torch.zeros(ops._lib.load().nvfp4_moe_expert_mlp_workspace_size(G, R), dtype=torch.uint8, device=d)
+    args = (xc, xs, one, None, off, w1, g1, w2, g2, R, H, I, one)
+    os.environ["NVFP4MOE_SPIN_LIMIT"] = "1"
+    try:
+        ops.moe_expert_mlp(*args, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["NVFP4MOE_SPIN_LIMIT"]
+    status = int(ws[4:8].view(torch.int32).item())
+    log("  status after the one-poll launch: %d" % status)
+    assert status in (0, 1)
+    hc, hs, y = ops.moe_expert_mlp(*args, workspace=ws)
+    hc2, hs2 = ops.grouped_gemm_silu_requant(xc, xs, one, w1, g1, off, R, I, H, one)
+    torch.cuda.synchronize()
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+    assert torch.equal(hc, hc2) and torch.equal(hs, hs2)
+
+
 def test_gemm_four_segments_and_bf16():
     _gemm_case([70, 70], 256, 128, [0, 32, 100, 160, 256], 7, out_bf16=True)
 

@@ -101,6 +101,17 @@ def _fused_same(unfused, fused):
                           o1.view(torch.int16).cpu().numpy())
 
 
+def _persistent_same(default, persistent):
+    """The layer with the expert MLP as one persistent launch must give the
+    default path's intermediate, second-GEMM output and layer output bit for
+    bit (in the streaming regime both run the same tiles)."""
+    (o0, g0), (o1, g1) = default, persistent
+    for k_ in ("hc", "hs"):
+        assert np.array_equal(to_np(g0[k_]), to_np(g1[k_])), k_
+    assert torch.equal(g0["y"].view(torch.int16), g1["y"].view(torch.int16))
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
 def _tiny_setup(n_shared=0):
     wl = workloads.WORKLOADS["tiny"]
     d = dev()
@@ -435,7 +446,15 @@ def _routed_full(name, n_shared=0, n_cols=256):
                                            torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
                                            keep=True, fused=fused, n_shared=n_shared)
     out, g = run(False)
-    _fused_same((out, g), run(True))
+    fused = run(True)
+    _fused_same((out, g), fused)
+    if name == "decode":
+        # the expert MLP as one persistent launch: identical intermediate,
+        # second-GEMM output and layer output
+        _persistent_same(fused, pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), k, w1, w2,
+                                                   torch.tensor([gs_x], device=d), torch.tensor([gs_h], device=d),
+                                                   keep=True, n_shared=n_shared, persistent=True))
+    del fused
     torch.cuda.synchronize()
     assert np.array_equal(to_np(g["xc"]), xq[0]) and np.array_equal(to_np(g["xs"]), xq[1])
     assert np.array_equal(to_np(g["ids"]), ids)
