@@ -385,7 +385,12 @@ int32_t nvfp4_moe_expert_mlp(const uint8_t* x_codes, const uint8_t* x_scales, co
 int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout) {
   if (G < 1 || M < 1 || K < 256 || K % 256 || a_rows < 1) return 0;
   if ((uint64_t)a_rows * (uint64_t)K * 2u >= ((uint64_t)1 << 32)) return 0;
-  return nvfp4::gemm_uses_big_tiles(G, M, w_layout == NVFP4_LAYOUT_TILED) ? 1 : 0;
+  const bool tiled = w_layout == NVFP4_LAYOUT_TILED;
+  // the 128-row tiles of one small group split over K read it too (N is not
+  // known here: a split is assumed whenever one 256-column tile would split,
+  // which may report a copy that a very wide GEMM then does not read)
+  const bool small = nvfp4::gemm_small_split(G, M, tiled) && nvfp4::gemm_splitk_bytes(G, M, 256, K, tiled) > 0;
+  return nvfp4::gemm_uses_big_tiles(G, M, tiled) || small ? 1 : 0;
 }
 
 size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K) {

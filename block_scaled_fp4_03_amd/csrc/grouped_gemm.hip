@@ -941,12 +941,16 @@ __global__ void zero_i32(int32_t* p, int64_t n) {
     p[i] = 0;
 }
 
-// Split-K tile for ranges of at most two 256-k steps (32 rows, 4 waves x
+// Split-K tile for ranges of at most two 256-k steps (32 RB rows, 4 waves x
 // NBW column blocks): every load of the range is issued before the first
 // MFMA, so a workgroup costs one memory round trip instead of a pipeline
 // fill per step.  Loads past the range's end repeat its last half-step and
 // are not used; rows past the group's end read its last row (not stored).
-template <int NBW>
+// (RB = 4, one workgroup for 128 rows of a group, reads each weight tile
+// once instead of four times, but measured slower on the 128-token shared
+// expert: every wave then dequantises all 128 rows of A; only RB = 1 is
+// launched.)
+template <int NBW, int RB>
 __device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
                                                  int wave, int lane, int64_t ks0, int64_t ks1, int split) {
   constexpr int NH = 4;   // half-steps held at once
@@ -957,11 +961,16 @@ __device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64
   if (n0 >= p.N) return;
   const int64_t K = p.K;
   const int64_t nks = K / 256;
-  const int64_t m_a = clampv<int64_t>(row0 + c, row0, row1 - 1);
-  int64_t a_row = p.a_row_index ? (int64_t)p.a_row_index[m_a] : m_a;
-  a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
-  const uint8_t* a_c = p.a_codes + a_row * (K / 2) + 32 * kh;
-  const uint8_t* a_s = p.a_scales + a_row * (K / 16) + 4 * kh;
+  const uint8_t* a_c[RB];
+  const uint8_t* a_s[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t m_a = clampv<int64_t>(row0 + 32 * rb + c, row0, row1 - 1);
+    int64_t a_row = p.a_row_index ? (int64_t)p.a_row_index[m_a] : m_a;
+    a_row = clampv<int64_t>(a_row, 0, p.a_rows > 0 ? p.a_rows - 1 : 0);
+    a_c[rb] = p.a_codes + a_row * (K / 2) + 32 * kh;
+    a_s[rb] = p.a_scales + a_row * (K / 16) + 4 * kh;
+  }
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
   const uint8_t* w_t[NBW];
 #pragma unroll
@@ -972,15 +981,18 @@ __device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64
   }
   const int64_t hs0 = 2 * ks0;
   const int nh = (int)(2 * (ks1 - ks0));
-  u32x4 a0[NH], a1[NH], w0[NH][NBW], w1[NH][NBW];
-  uint32_t as[NH], ws[NH][NBW];
+  u32x4 a0[NH][RB], a1[NH][RB], w0[NH][NBW], w1[NH][NBW];
+  uint32_t as[NH][RB], ws[NH][NBW];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int64_t hs = hs0 + (h < nh ? h : nh - 1);
     const int64_t ks = hs >> 1, hh = hs & 1;
-    a0[h] = *(const u32x4*)(a_c + ks * 128 + 64 * hh);
-    a1[h] = *(const u32x4*)(a_c + ks * 128 + 64 * hh + 16);
-    as[h] = *(const uint32_t*)(a_s + ks * 16 + 8 * hh);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      a0[h][rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * hh);
+      a1[h][rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * hh + 16);
+      as[h][rb] = *(const uint32_t*)(a_s[rb] + ks * 16 + 8 * hh);
+    }
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
       const uint8_t* t = w_t[cb] + ks * kTileBytes;
@@ -989,19 +1001,25 @@ __device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64
       ws[h][cb] = *(const uint32_t*)(t + 4096 + 256 * hh + 4 * lane);
     }
   }
-  floatx16_t acc[NBW];
+  floatx16_t acc[RB][NBW];
 #pragma unroll
-  for (int cb = 0; cb < NBW; ++cb) acc[cb] = floatx16_t{};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = floatx16_t{};
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     if (h >= nh) break;   // uniform
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const half8_t af = dequant8(j < 4 ? a0[h][j] : a1[h][j - 4], scale_pair(byte_of(as[h], j >> 1)));
+      half8_t bf[NBW];
 #pragma unroll
-      for (int cb = 0; cb < NBW; ++cb) {
-        const half8_t bf = dequant8(j < 4 ? w0[h][cb][j] : w1[h][cb][j - 4], scale_pair(byte_of(ws[h][cb], j >> 1)));
-        acc[cb] = mfma32(af, bf, acc[cb]);
+      for (int cb = 0; cb < NBW; ++cb)
+        bf[cb] = dequant8(j < 4 ? w0[h][cb][j] : w1[h][cb][j - 4], scale_pair(byte_of(ws[h][cb], j >> 1)));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const half8_t af = dequant8(j < 4 ? a0[h][rb][j] : a1[h][rb][j - 4], scale_pair(byte_of(as[h][rb], j >> 1)));
+#pragma unroll
+        for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = mfma32(af, bf[cb], acc[rb][cb]);
       }
     }
   }
@@ -1011,14 +1029,16 @@ __device__ __forceinline__ void split_short_tile(const GemmArgs& p, int g, int64
     const int64_t n = n0 + 32 * cb + c;
     if (n >= p.N) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t m = row0 + acc32_row(i, kh);
-      if (m < row1) part[m * p.N + n] = acc[cb][i];
-    }
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t m = row0 + 32 * rb + acc32_row(i, kh);
+        if (m < row1) part[m * p.N + n] = acc[rb][cb][i];
+      }
   }
 }
 
-template <int NBW>
+template <int NBW, int RB>
 __global__ __launch_bounds__(256) void gemm_splitk_short(GemmArgs p, int64_t n_tiles) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1029,11 +1049,11 @@ __global__ __launch_bounds__(256) void gemm_splitk_short(GemmArgs p, int64_t n_t
   const int64_t nt = t - slot * n_tiles;
   int g;
   int64_t row0, row1;
-  if (!find_tile(p.group_offsets, p.G, p.M, slot, 32, 1, 0, 0, g, row0, row1)) return;
+  if (!find_tile(p.group_offsets, p.G, p.M, slot, 32 * RB, 1, 0, 0, g, row0, row1)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   const int64_t nks = p.K / 256;
-  split_short_tile<NBW>(p, g, row0, row1, nt, wave, lane, nks * split / p.splits, nks * (split + 1) / p.splits,
-                        split);
+  split_short_tile<NBW, RB>(p, g, row0, row1, nt, wave, lane, nks * split / p.splits, nks * (split + 1) / p.splits,
+                            split);
 }
 
 // Split-K reduction: out[m, n] = alpha(g, n) * (part_0 + part_1 + ...) in
@@ -1383,7 +1403,7 @@ __device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds,
   }
 }
 
-template <int RB, bool FUSE, bool SPLIT = false>
+template <int RB, bool FUSE, bool SPLIT = false, int HALF = kAHalfBytes>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
                                             int64_t n0, int wave, int lane, int64_t hs0 = 0, int64_t hs1 = -1,
                                             int split = 0) {
@@ -1418,7 +1438,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
       (void*)p.a_dq, (short)0, (int)(uint32_t)(p.a_rows * K * 2), 0x00020000);
   auto a_copy = [&](int64_t hs, int buf, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        a_rsrc, (__attribute__((address_space(3))) void*)(lds + buf * kAHalfBytes + (8 * RB * wave + 4 * i) * 256),
+        a_rsrc, (__attribute__((address_space(3))) void*)(lds + buf * HALF + (8 * RB * wave + 4 * i) * 256),
         16, (int)a_off[i], (int)(hs * 256), 0, 0);
   };
 
@@ -1483,7 +1503,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     // the last half-step reloads itself (into the unused buffer and registers)
     const int64_t hn = hs + 1 < hs1 ? hs + 1 : hs;
     w_load(hn, nxt);
-    const uint8_t* abuf = lds + h * kAHalfBytes + c * 256;
+    const uint8_t* abuf = lds + h * HALF + c * 256;
     half8_t af[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[0]);
@@ -1632,20 +1652,85 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
   }
 }
 
+// gemm_big32_dq4: 128 x 256 tiles of the same loop (RB = 4: each wave 128
+// rows x 64 columns, 128 accumulators), at most 256 registers per lane and
+// 64 KiB of local memory, so two workgroups share a compute unit: each SIMD
+// runs one wave of each, and while one workgroup waits at its per-half-step
+// barrier, or runs a tile's prologue or epilogue, the other's waves keep the
+// matrix core busy.  A W fragment feeds four MFMAs instead of eight (twice
+// the dequantisation work per MFMA), which the second wave hides.  A group's
+// last tile of 65-127 rows is a 128-row tile too; fewer rows are left to the
+// streaming kernel.
+constexpr int BIG4 = 128;
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t slot, nt;
+  xcd_tile((int64_t)blockIdx.x, n_tiles, slot, nt);
+  int g;
+  int64_t row0, row1;
+  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG4, kBigMinLast, 0, 0, g, row0, row1)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane((int)row0);
+  row1 = __builtin_amdgcn_readfirstlane((int)row1);
+  big_dq_tile<4, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+}
+
+// One group of at most 128 rows (the shared expert), A in f16 form, K split:
+// block b takes column tile b % n_tiles and k range b / n_tiles of the
+// 128 x 256 tile loop above (A through local memory, each weight tile read
+// once for all rows), writing raw partial sums that splitk_reduce adds in
+// range order.  No tile search: the group is rows [offsets[0], offsets[1]).
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_small_dq4_split(GemmArgs p, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = (int)(blockIdx.x / n_tiles);
+  const int64_t nt = (int64_t)blockIdx.x - split * n_tiles;
+  const int64_t row0 = clampv<int64_t>(p.group_offsets[0], 0, p.M);
+  int64_t row1 = clampv<int64_t>(p.group_offsets[1], 0, p.M);
+  row1 = clampv<int64_t>(row1, row0, row0 + BIG4);
+  if (row1 <= row0) return;
+  const int64_t nks = p.K / 256;
+  big_dq_tile<4, false, true, BIG4 * 256>(p, lds, 0, row0, row1, nt * BIG, wave, lane, 2 * (nks * split / p.splits),
+                                          2 * (nks * (split + 1) / p.splits), split);
+}
+
+// whether launch_tiled runs gemm_small_dq4_split (given A in f16 form)
+bool gemm_small_split(int64_t G, int64_t M, bool tiled) { return tiled && G == 1 && M >= 1 && M <= BIG4; }
+
 // ---------------------------------------------------------------------------
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled) { return tiled && M >= BIG && M >= 64 * G; }
 
 template <bool FUSE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+  if constexpr (!FUSE) {
+    if (a.a_dq && a.splits > 1 && a.ws && gemm_small_split(a.G, a.M, true)) {
+      // one group of at most 128 rows: the 128-row tiles split over K, then
+      // the partial sums reduced in order
+      const int64_t n_tiles = (a.N + BIG - 1) / BIG;
+      hipLaunchKernelGGL(gemm_small_dq4_split, dim3((unsigned)(n_tiles * a.splits)), dim3(kBigThreads), 0, s, a,
+                         n_tiles);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a, 0, 0);
+      return hipGetLastError();
+    }
+  }
   // a workgroup covers 256 weight rows: 256 output columns, or (fused) 128
   // columns of h from 128 gate and 128 up rows
   if (gemm_uses_big_tiles(a.G, a.M, true) && (a.a_dq || !FUSE)) {
-    // many rows per group: 256-row tiles on the matrix-core kernel (with A
-    // in f16 form also a group's last tile if it has kBigMinLast rows or
-    // more), the rows left over at the end of each group on the streaming
-    // kernel.  Tile counts are upper bounds (the group sizes are on the
-    // device); workgroups without a tile exit.
+    // many rows per group: 128-row (A in f16 form) or 256-row tiles on the
+    // matrix-core kernels (with A in f16 form also a group's last tile if it
+    // has kBigMinLast rows or more), the rows left over at the end of each
+    // group on the streaming kernel.  Tile counts are upper bounds (the
+    // group sizes are on the device); workgroups without a tile exit.
     const bool dq = a.a_dq != nullptr;
+    // A in f16 form, no split K, plain output: 128-row tiles, two workgroups
+    // per compute unit (gemm_big32_dq4); else 256-row tiles
+    const bool dq4 = dq && !FUSE && !(a.splits > 1 && a.ws);
+    const int tile_rows = dq4 ? BIG4 : BIG;
     const int skip_min = dq ? kBigMinLast : BIG;
     constexpr int NBW = 2, RB = 1;
     const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
@@ -1657,11 +1742,11 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     // persistent: three workgroups per compute unit (164 VGPRs with two
     // half-steps of loads in flight)
     const int64_t grid_s = std::min<int64_t>(work_s, 768);
+    const int64_t n_tiles = (a.N + BIG - 1) / BIG;
     hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a, n_tiles_s,
-                       BIG, skip_min, work_s);
+                       tile_rows, skip_min, work_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n_tiles = (a.N + BIG - 1) / BIG;
     const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
     if constexpr (!FUSE) {
       if (dq && a.splits > 1 && a.ws) {
@@ -1677,7 +1762,10 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
         return hipGetLastError();
       }
     }
-    if (dq)
+    if (dq4) {
+      const int64_t slots4 = (a.M / BIG4 + a.G + 7) / 8 * 8;
+      hipLaunchKernelGGL(gemm_big32_dq4, dim3((unsigned)(slots4 * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
+    } else if (dq)
       hipLaunchKernelGGL(gemm_big32_dq<FUSE>, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a,
                          n_tiles);
     else if constexpr (!FUSE)
@@ -1692,7 +1780,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
       // few workgroups for the chip: split K, then reduce in split order
       const int64_t nks = a.K / 256;
       if ((nks + a.splits - 1) / a.splits <= 2)
-        hipLaunchKernelGGL(gemm_splitk_short<NBW>, dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a, n_tiles);
+        hipLaunchKernelGGL((gemm_splitk_short<NBW, 1>), dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a,
+                           n_tiles);
       else
         hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, true>), dim3((unsigned)(work * a.splits)),
                            dim3(256), 0, s, a, n_tiles, 0, 0, work);

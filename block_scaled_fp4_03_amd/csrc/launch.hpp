@@ -99,6 +99,9 @@ int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tile
 size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled);
 // true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
 bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
+// true when launch_tiled, given A in f16 form and a split-K workspace, runs
+// one group of at most 128 rows on the 128-row tiles split over K
+bool gemm_small_split(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 // the expert MLP in one persistent launch: l1 the first GEMM with the fused
 // SiLU-requant epilogue, l2 the second GEMM over the same groups (A = h);

@@ -264,8 +264,10 @@ def test_gemm_64_row_streaming_slots():
 
 
 def test_gemm_big_tiles_every_last_tile_height():
-    # group sizes whose last tile takes each of the 256/128/64/32-row forms
-    # (1, 31, 32, 33, 64, 65, 128, 129, 255 left-over rows)
+    # group sizes whose last tile takes each form: with A in f16 form a
+    # 128-row tile for 65..127 rows past the full 128-row tiles and the
+    # streaming kernel for 1..64; without it (the 256-row kernel) the
+    # left-over rows 1, 31, 32, 33, 64, 65, 128, 129, 255
     _gemm_case([257, 287, 288, 289, 320, 321, 384, 385, 511, 256], 96, 256, [0, 40, 96], 14, gather=True)
     _gemm_case([257, 288, 289, 320, 321, 384, 385], 64, 4608, [0, 64], 17, gather=True)
 
