@@ -1659,9 +1659,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int6
 // barrier, or runs a tile's prologue or epilogue, the other's waves keep the
 // matrix core busy.  A W fragment feeds four MFMAs instead of eight (twice
 // the dequantisation work per MFMA), which the second wave hides.  A group's
-// last tile of 65-127 rows is a 128-row tile too; fewer rows are left to the
+// last tile of kBig4MinLast rows or more is a tile of this launch too, 32, 64
+// or 128 rows high (the smallest that holds it); fewer rows are left to the
 // streaming kernel.
 constexpr int BIG4 = 128;
+#ifndef NVFP4_BIG4_MIN_LAST
+#define NVFP4_BIG4_MIN_LAST 1
+#endif
+constexpr int kBig4MinLast = NVFP4_BIG4_MIN_LAST;
 __global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int64_t n_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
   const int lane = threadIdx.x & 63;
@@ -1670,11 +1675,17 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int
   xcd_tile((int64_t)blockIdx.x, n_tiles, slot, nt);
   int g;
   int64_t row0, row1;
-  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG4, kBigMinLast, 0, 0, g, row0, row1)) return;
+  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG4, kBig4MinLast, 0, 0, g, row0, row1)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   row0 = __builtin_amdgcn_readfirstlane((int)row0);
   row1 = __builtin_amdgcn_readfirstlane((int)row1);
-  big_dq_tile<4, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+  const int64_t rows = row1 - row0;
+  if (rows > 64 || kBig4MinLast > 64)
+    big_dq_tile<4, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+  else if (rows > 32 || kBig4MinLast > 32)
+    big_dq_tile<2, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+  else
+    big_dq_tile<1, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
 }
 
 // One group of at most 128 rows (the shared expert), A in f16 form, K split:
@@ -1731,22 +1742,25 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     // per compute unit (gemm_big32_dq4); else 256-row tiles
     const bool dq4 = dq && !FUSE && !(a.splits > 1 && a.ws);
     const int tile_rows = dq4 ? BIG4 : BIG;
-    const int skip_min = dq ? kBigMinLast : BIG;
-    constexpr int NBW = 2, RB = 1;
-    const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-    // a group leaves fewer than skip_min rows over: at most that many 32-row
-    // tiles per group, and at most M / 32 + G in all
-    const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
-    const int64_t work_s =
-        std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
-    // persistent: three workgroups per compute unit (164 VGPRs with two
-    // half-steps of loads in flight)
-    const int64_t grid_s = std::min<int64_t>(work_s, 768);
+    const int skip_min = dq4 ? kBig4MinLast : dq ? kBigMinLast : BIG;
+    hipError_t e = hipSuccess;
+    if (skip_min > 1) {
+      constexpr int NBW = 2, RB = 1;
+      const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+      // a group leaves fewer than skip_min rows over: at most that many
+      // 32-row tiles per group, and at most M / 32 + G in all
+      const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
+      const int64_t work_s =
+          std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
+      // persistent: three workgroups per compute unit (164 VGPRs with two
+      // half-steps of loads in flight)
+      const int64_t grid_s = std::min<int64_t>(work_s, 768);
+      hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a,
+                         n_tiles_s, tile_rows, skip_min, work_s);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-    hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a, n_tiles_s,
-                       tile_rows, skip_min, work_s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
     if constexpr (!FUSE) {
       if (dq && a.splits > 1 && a.ws) {
