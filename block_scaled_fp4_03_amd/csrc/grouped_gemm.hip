@@ -1403,7 +1403,9 @@ __device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds,
   }
 }
 
-template <int RB, bool FUSE, bool SPLIT = false, int HALF = kAHalfBytes>
+// s_waitcnt immediate: vmcnt 6, expcnt 0, lgkmcnt 0
+constexpr int kVmcnt6 = 6;
+template <int RB, bool FUSE, bool SPLIT = false, int HALF = kAHalfBytes, int PF = 1>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
                                             int64_t n0, int wave, int lane, int64_t hs0 = 0, int64_t hs1 = -1,
                                             int split = 0) {
@@ -1476,12 +1478,17 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = floatx16_t{};
 
-  // half-steps hs0 .. hs1 - 1 (all of K unless split); hs0 is in buffer 0
+  // half-steps hs0 .. hs1 - 1 (all of K unless split); hs0 is in buffer 0.
+  // PF = 1: a half-step's W words are loaded at the start of the one before
+  // (into nxt).  PF = 2: two half-steps ahead, after that half-step's A
+  // copies (at its substep 4), into nxt and far alternately; the wait at the
+  // end of a half-step then leaves those six loads in flight.
   if (hs1 < 0) hs1 = 2 * nks;
-  WWords cur, nxt;
+  WWords cur, nxt, far;
 #pragma unroll
   for (int i = 0; i < NC; ++i) a_copy(hs0, 0, i);
   w_load(hs0, cur);
+  if constexpr (PF == 2) w_load(hs0 + 1 < hs1 ? hs0 + 1 : hs0, nxt);
   half8_t bf[CB];
   // the half-step's four scale bytes per column block as two f16 pairs
   half2_t sc_lo[CB], sc_hi[CB], sc_n[CB];
@@ -1496,19 +1503,30 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   int chunk_ofs[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) chunk_ofs[j] = ((8 * kh + j) ^ x) << 4;
-  __builtin_amdgcn_s_waitcnt(0);       // this wave's copies of the first half-tile have landed
+  // this wave's copies of the first half-tile have landed (PF = 2: the six
+  // loads of the second half-step's W words may still be in flight)
+  if constexpr (PF == 2)
+    __builtin_amdgcn_s_waitcnt(kVmcnt6);
+  else
+    __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int64_t hs = hs0; hs < hs1; ++hs) {
+  // one half-step: cu holds its W words, nx the next half-step's (PF = 1:
+  // loaded here), fa receives the words two half-steps ahead (PF = 2)
+  auto half_step = [&](int64_t hs, const WWords& cu, WWords& nx, WWords& fa) __attribute__((always_inline)) {
     const int h = (int)((hs - hs0) & 1);
     // the last half-step reloads itself (into the unused buffer and registers)
     const int64_t hn = hs + 1 < hs1 ? hs + 1 : hs;
-    w_load(hn, nxt);
+    if constexpr (PF == 1) w_load(hn, nx);
     const uint8_t* abuf = lds + h * HALF + c * 256;
     half8_t af[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[0]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      if constexpr (PF == 2) {
+        // after the A copies of substeps 0-3 (sched_barrier keeps the order)
+        if (j == 4) w_load(hs + 2 < hs1 ? hs + 2 : hs1 - 1, fa);
+      }
       half2_t sfn[CB];
       half8_t bn[CB];
 #pragma unroll
@@ -1532,8 +1550,8 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
       // next half-step), interleaved by the scheduler with the MFMAs above
 #pragma unroll
       for (int wc = 0; wc < CB; ++wc) {
-        const uint32_t word = j < 7 ? (j + 1 < 4 ? cur.w0[wc][j + 1] : cur.w1[wc][j + 1 - 4]) : nxt.w0[wc][0];
-        if (j == 6) sc_n[wc] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nxt.ws[wc], 1.0f, false);
+        const uint32_t word = j < 7 ? (j + 1 < 4 ? cu.w0[wc][j + 1] : cu.w1[wc][j + 1 - 4]) : nx.w0[wc][0];
+        if (j == 6) sc_n[wc] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nx.ws[wc], 1.0f, false);
         const half2_t sp = j < 7 ? (((j + 1) >> 1) < 2 ? sc_lo[wc] : sc_hi[wc]) : sc_n[wc];
         const _Float16 sv = j < 7 ? sp[((j + 1) >> 1) & 1] : sp[0];
         sfn[wc] = half2_t{sv, sv};
@@ -1550,14 +1568,34 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
       // scheduler would otherwise move the loads towards their first use)
       __builtin_amdgcn_sched_barrier(0);
     }
-    cur = nxt;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       sc_lo[cb] = sc_n[cb];
-      sc_hi[cb] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.ws[cb], 1.0f, true);
+      sc_hi[cb] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nx.ws[cb], 1.0f, true);
     }
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next half-tile have landed
+    // this wave's copies of the next half-tile have landed
+    if constexpr (PF == 2)
+      __builtin_amdgcn_s_waitcnt(kVmcnt6);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  if constexpr (PF == 2) {
+    // the three register sets rotate: unrolled by three, so that no set is
+    // ever copied (a copy of a set with loads in flight would wait for them)
+    int64_t hs = hs0;
+    for (; hs + 3 <= hs1; hs += 3) {
+      half_step(hs, cur, nxt, far);
+      half_step(hs + 1, nxt, far, cur);
+      half_step(hs + 2, far, cur, nxt);
+    }
+    if (hs < hs1) half_step(hs, cur, nxt, far);
+    if (hs + 1 < hs1) half_step(hs + 1, nxt, far, cur);
+  } else {
+    for (int64_t hs = hs0; hs < hs1; ++hs) {
+      half_step(hs, cur, nxt, far);
+      cur = nxt;
+    }
   }
 
   if constexpr (FUSE) {
@@ -1667,6 +1705,11 @@ constexpr int BIG4 = 128;
 #define NVFP4_BIG4_MIN_LAST 1
 #endif
 constexpr int kBig4MinLast = NVFP4_BIG4_MIN_LAST;
+#ifndef NVFP4_BIG4_PREFETCH
+#define NVFP4_BIG4_PREFETCH 2
+#endif
+constexpr int kBig4Prefetch = NVFP4_BIG4_PREFETCH;
+template <bool FUSE>
 __global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int64_t n_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
   const int lane = threadIdx.x & 63;
@@ -1681,11 +1724,11 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int
   row1 = __builtin_amdgcn_readfirstlane((int)row1);
   const int64_t rows = row1 - row0;
   if (rows > 64 || kBig4MinLast > 64)
-    big_dq_tile<4, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+    big_dq_tile<4, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
   else if (rows > 32 || kBig4MinLast > 32)
-    big_dq_tile<2, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+    big_dq_tile<2, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
   else
-    big_dq_tile<1, false, false, BIG4 * 256>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+    big_dq_tile<1, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
 }
 
 // One group of at most 128 rows (the shared expert), A in f16 form, K split:
@@ -1740,7 +1783,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     const bool dq = a.a_dq != nullptr;
     // A in f16 form, no split K, plain output: 128-row tiles, two workgroups
     // per compute unit (gemm_big32_dq4); else 256-row tiles
-    const bool dq4 = dq && !FUSE && !(a.splits > 1 && a.ws);
+    const bool dq4 = dq && !(!FUSE && a.splits > 1 && a.ws);
     const int tile_rows = dq4 ? BIG4 : BIG;
     const int skip_min = dq4 ? kBig4MinLast : dq ? kBigMinLast : BIG;
     hipError_t e = hipSuccess;
@@ -1778,7 +1821,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     }
     if (dq4) {
       const int64_t slots4 = (a.M / BIG4 + a.G + 7) / 8 * 8;
-      hipLaunchKernelGGL(gemm_big32_dq4, dim3((unsigned)(slots4 * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
+      hipLaunchKernelGGL(gemm_big32_dq4<FUSE>, dim3((unsigned)(slots4 * n_tiles)), dim3(kBigThreads), 0, s, a,
+                         n_tiles);
     } else if (dq)
       hipLaunchKernelGGL(gemm_big32_dq<FUSE>, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a,
                          n_tiles);
