@@ -74,88 +74,183 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
-// One block per expert e.  Pass 1 counts the flat (token, slot) entries with
-// an id below e (that count is e's offset) and equal to e.  Pass 2 gives each
-// entry of e its rank among e's entries in flat order: every wave owns one
-// contiguous range of flat indices, ranks inside the wave come from a ballot,
-// and the ranges are offset by the counts of the waves before.  No atomics, so
-// the permutation is the same on every run.  Both passes read a wave's range
-// kPermBatch x 64 ids at a time, all loads issued before the first is used,
-// so that a pass costs one memory round trip per batch instead of one per 64
-// ids; pass 2 still takes the batch's 64-id chunks in flat order.
+// The stable group-by-expert permutation as a counting sort.  The flat
+// (token, slot) entries are cut into nb contiguous chunks, one block each;
+// inside a block, wave w owns the w-th contiguous part of the chunk.
+//  * count (nb > 1): block b counts its chunk per group into row b of a
+//    scratch table (nb x G ints; the sorted_ids array serves, nb * G <= R).
+//  * scan: thread e turns column e into group e's offset (the exclusive sum
+//    of all groups' totals, a block scan) and each block's first position for
+//    e (the offset plus e's entries in the chunks before).
+//  * rank: each wave counts its part per group (local atomic adds: counts
+//    only, their order does not matter); thread e turns the block's first
+//    position for e into each wave's; then each wave walks its part in flat
+//    order, 64 entries at a time: the lanes holding the same id find each
+//    other with one ballot per id bit, an entry's position is its wave's
+//    running position for that id plus the number of equal ids in lower
+//    lanes, and the highest such lane advances the running position.
+//  * scatter (nb > 1): sorted_ids[inv[f]] = token of f, once the scratch
+//    table is no longer read.
+// With nb == 1 one block does the scan and the rank and writes every output.
+// Every position follows from the flat order alone, so the permutation is the
+// same on every run; the work is O(R + G * nb).
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kPermBatch = 8;
+constexpr int kPermMaxGroups = 1024;
+constexpr int64_t kPermChunk = 4096;          // entries per block when nb > 1
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int64_t R,
-                                                               int k, int E, int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ sorted_ids,
-                                                               int32_t* __restrict__ inv) {
-  __shared__ int32_t wave_eq[kPermWaves];
-  __shared__ int32_t wave_lt[kPermWaves];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int64_t per_wave = (R + kPermWaves - 1) / kPermWaves;
-  const int64_t lo = wv * per_wave;
-  const int64_t hi = lo + per_wave < R ? lo + per_wave : R;
-  int32_t n_lt = 0, n_eq = 0;
-  for (int64_t b = lo; b < hi; b += 64 * kPermBatch) {
-    int32_t v[kPermBatch];
+// wave-level inclusive scan of x, then the block-level exclusive prefix of
+// the block's threads in order; returns the exclusive prefix of this thread
+// and writes the block total to *sum_out (all threads)
+__device__ __forceinline__ int32_t block_excl_scan(int32_t x, int32_t* wave_sum, int32_t& block_total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int32_t incl = x;
 #pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
-      const int64_t f = b + 64 * u + lane;
-      v[u] = f < hi ? ids[f] : INT32_MAX;
-    }
-#pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
-      n_lt += v[u] < e;
-      n_eq += v[u] == e;
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    n_lt += __shfl_xor(n_lt, o, 64);
-    n_eq += __shfl_xor(n_eq, o, 64);
+  if (lane == 63) wave_sum[wv] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  block_total = 0;
+  for (int w = 0; w < kPermWaves; ++w) {
+    if (w < wv) before += wave_sum[w];
+    block_total += wave_sum[w];
   }
-  if (lane == 0) {
-    wave_lt[wv] = n_lt;
-    wave_eq[wv] = n_eq;
+  return before + incl - x;
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(const int32_t* __restrict__ ids, int64_t R, int G,
+                                                                  int32_t* __restrict__ table) {
+  __shared__ int32_t cnt[kPermMaxGroups];
+  for (int e = threadIdx.x; e < G; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * kPermChunk;
+  const int64_t hi = lo + kPermChunk < R ? lo + kPermChunk : R;
+  for (int64_t f = lo + threadIdx.x; f < hi; f += kPermThreads) {
+    const int32_t v = ids[f];
+    if (v >= 0 && v < G) atomicAdd(&cnt[v], 1);
   }
   __syncthreads();
-  int32_t base = 0, total_lt = 0, total_eq = 0;
-  for (int i = 0; i < kPermWaves; ++i) {
-    if (i < wv) base += wave_eq[i];
-    total_lt += wave_lt[i];
-    total_eq += wave_eq[i];
+  for (int e = threadIdx.x; e < G; e += kPermThreads) table[(int64_t)blockIdx.x * G + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(int nb, int G, int32_t* __restrict__ table,
+                                                                 int32_t* __restrict__ offsets) {
+  __shared__ int32_t wave_sum[kPermWaves];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < G)
+    for (int b = 0; b < nb; ++b) total += table[(int64_t)b * G + e];
+  int32_t all;
+  const int32_t off = block_excl_scan(total, wave_sum, all);
+  if (e < G) {
+    offsets[e] = off;
+    int32_t run = off;
+    for (int b = 0; b < nb; ++b) {
+      const int32_t c = table[(int64_t)b * G + e];
+      table[(int64_t)b * G + e] = run;
+      run += c;
+    }
   }
-  if (threadIdx.x == 0) {
-    offsets[e] = total_lt;
-    if (e == E - 1) offsets[E] = total_lt + total_eq;
-  }
-  if (total_eq == 0) return;
-  int32_t pos = total_lt + base;
+  if (e == 0) offsets[G] = all;
+}
+
+// rank: block b takes chunk b (nb > 1: of kPermChunk entries, its first
+// positions in row b of `table`; nb == 1: every entry, first positions from
+// its own scan, offsets and sorted_ids written here)
+__global__ __launch_bounds__(kPermThreads) void perm_rank_kernel(const int32_t* __restrict__ ids, int64_t R, int k,
+                                                                 int G, int nb, const int32_t* table,
+                                                                 int32_t* __restrict__ offsets, int32_t* sorted_ids,
+                                                                 int32_t* __restrict__ inv) {
+  __shared__ int32_t cnt[kPermWaves * kPermMaxGroups];   // [wave][group], row stride G
+  __shared__ int32_t wave_sum[kPermWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  for (int i = tid; i < kPermWaves * G; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t c_lo = nb > 1 ? (int64_t)blockIdx.x * kPermChunk : 0;
+  const int64_t c_hi = nb > 1 ? (c_lo + kPermChunk < R ? c_lo + kPermChunk : R) : R;
+  const int64_t per_wave = (c_hi - c_lo + kPermWaves - 1) / kPermWaves;
+  const int64_t lo = c_lo + wv * per_wave < c_hi ? c_lo + wv * per_wave : c_hi;
+  const int64_t hi = lo + per_wave < c_hi ? lo + per_wave : c_hi;
   for (int64_t b = lo; b < hi; b += 64 * kPermBatch) {
     int32_t v[kPermBatch];
 #pragma unroll
     for (int u = 0; u < kPermBatch; ++u) {
       const int64_t f = b + 64 * u + lane;
-      v[u] = f < hi ? ids[f] : INT32_MAX;
+      v[u] = f < hi ? ids[f] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u)
+      if (v[u] >= 0 && v[u] < G) atomicAdd(&cnt[wv * G + v[u]], 1);
+  }
+  __syncthreads();
+  // the block's first position for group e: from the table, or (one block)
+  // the exclusive scan of the totals, which is also e's offset
+  const int e = tid;
+  int32_t first = 0;
+  if (nb > 1) {
+    if (e < G) first = table[(int64_t)blockIdx.x * G + e];
+  } else {
+    int32_t total = 0;
+    if (e < G)
+      for (int w = 0; w < kPermWaves; ++w) total += cnt[w * G + e];
+    int32_t all;
+    first = block_excl_scan(total, wave_sum, all);
+    if (e < G) offsets[e] = first;
+    if (e == 0) offsets[G] = all;
+  }
+  if (e < G) {
+    int32_t run = first;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int32_t c = cnt[w * G + e];
+      cnt[w * G + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < G) ++nbits;
+  const uint64_t lower = lane ? ((~0ull) >> (64 - lane)) : 0ull;
+  for (int64_t b = lo; b < hi; b += 64 * kPermBatch) {
+    int32_t v[kPermBatch];
 #pragma unroll
     for (int u = 0; u < kPermBatch; ++u) {
       const int64_t f = b + 64 * u + lane;
-      const bool mine = v[u] == e;     // INT32_MAX (past the range) is never an expert id
-      const uint64_t mask = __ballot(mine);
-      const uint64_t below = lane ? (mask & ((~0ull) >> (64 - lane))) : 0ull;
-      if (mine) {
-        const int32_t p = pos + (int32_t)__popcll(below);
-        sorted_ids[p] = (int32_t)(f / k);
+      v[u] = f < hi ? ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      if (b + 64 * u >= hi) break;       // (uniform) the rest of the batch is past the part
+      const int64_t f = b + 64 * u + lane;
+      const bool valid = v[u] >= 0 && v[u] < G;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (v[u] >> bit) & 1;
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+      }
+      if (valid) {
+        const int32_t p = cnt[wv * G + v[u]] + (int32_t)__popcll(peers & lower);
+        if (nb == 1) sorted_ids[p] = (int32_t)(f / k);
         inv[f] = p;
       }
-      pos += (int32_t)__popcll(mask);
+      // one wave's local-memory operations complete in program order: every
+      // lane has read its running position before the highest lane of each
+      // id advances it
+      if (valid && (peers >> lane) == 1ull) cnt[wv * G + v[u]] += (int32_t)__popcll(peers);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ inv, int64_t R, int k,
+                                                           int32_t* __restrict__ sorted_ids) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f < R) sorted_ids[inv[f]] = (int32_t)(f / k);
 }
 
 __global__ void zero_offsets_kernel(int32_t* offsets, int n) {
@@ -175,8 +270,28 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int E, int k, in
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(256), 0, s, logits, T, E, k, ns, ids, w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)G), dim3(kPermThreads), 0, s, ids, T * kk, kk, G,
-                     offsets, sorted_ids, inv);
+  if (G > kPermMaxGroups) return hipErrorInvalidValue;   // (the C ABI admits at most 1024 groups)
+  const int64_t R = T * kk;
+  // blocks of kPermChunk entries, as long as their table fits sorted_ids
+  int64_t nb = (R + kPermChunk - 1) / kPermChunk;
+  if (nb * G > R) nb = 1;
+  if (nb == 1) {
+    hipLaunchKernelGGL(perm_rank_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, R, kk, G, 1,
+                       (const int32_t*)nullptr, offsets, sorted_ids, inv);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nb), dim3(kPermThreads), 0, s, ids, R, G, sorted_ids);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, (int)nb, G, sorted_ids, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nb), dim3(kPermThreads), 0, s, ids, R, kk, G, (int)nb,
+                     (const int32_t*)sorted_ids, offsets, sorted_ids, inv);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, inv, R, kk,
+                     sorted_ids);
   return hipGetLastError();
 }
 

@@ -104,8 +104,10 @@ def _route_case(T, E, k, seed, zipf=0.0, ties=False):
                                              (8192, 384, 6, 1.1, False), (100, 384, 6, 0, True),
                                              (5, 1, 1, 0, False), (3, 16, 16, 0, True),
                                              (77, 1024, 16, 0, False), (1, 64, 6, 0, True),
-                                             (3001, 384, 7, 1.1, False)])
+                                             (3001, 384, 7, 1.1, False), (4096, 1024, 8, 0.5, True)])
 def test_route_permute_bit_exact(T, E, k, zipf, ties):
+    # R = T * k entries: up to 4096 in one block, else in blocks of 4096 (the
+    # last one ragged) with a table of first positions between the passes
     log("route", T, E, k, zipf, ties)
     lg = _route_case(T, E, k, T * 7 + E, zipf, ties)
     ids_r, w_r = moe.route_topk(lg, k)
@@ -119,7 +121,8 @@ def test_route_permute_bit_exact(T, E, k, zipf, ties):
 
 
 @pytest.mark.parametrize("T,E,k,ns,ties", [(16, 8, 2, 1, False), (256, 384, 6, 1, False), (100, 384, 6, 2, True),
-                                           (5, 1, 1, 1, False), (3, 16, 15, 1, True), (1, 1022, 6, 2, False)])
+                                           (5, 1, 1, 1, False), (3, 16, 15, 1, True), (1, 1022, 6, 2, False),
+                                           (8192, 384, 6, 1, False)])
 def test_route_permute_shared_bit_exact(T, E, k, ns, ties):
     # the shared experts folded in: routed slots as without them, then slots
     # k.. with ids E.. and weight 1; the permutation over E + ns groups
