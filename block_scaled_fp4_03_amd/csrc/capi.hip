@@ -390,7 +390,7 @@ int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_r
   // known here: a split is assumed whenever one 256-column tile would split,
   // which may report a copy that a very wide GEMM then does not read)
   const bool small = nvfp4::gemm_small_split(G, M, tiled) && nvfp4::gemm_splitk_bytes(G, M, 256, K, tiled) > 0;
-  return nvfp4::gemm_uses_big_tiles(G, M, tiled) || small ? 1 : 0;
+  return nvfp4::gemm_uses_big_tiles(G, M, K, tiled) || small ? 1 : 0;
 }
 
 size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K) {

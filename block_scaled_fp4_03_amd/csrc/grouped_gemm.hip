@@ -1755,7 +1755,16 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_small_dq4_split(GemmArgs 
 bool gemm_small_split(int64_t G, int64_t M, bool tiled) { return tiled && G == 1 && M >= 1 && M <= BIG4; }
 
 // ---------------------------------------------------------------------------
-bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled) { return tiled && M >= BIG && M >= 64 * G; }
+// The matrix-core tiles from 32 rows per group on average (16 where K <=
+// 4096, the second GEMM of the layer); below that the streaming kernel,
+// which reads each group's weights once per 32-row slot from HBM, is faster.
+// Measured on the routed layer (384 experts, top-6): T = 2048 3.98 -> 3.16
+// ms and T = 3072 4.41 -> 3.48 ms against the 64-row rule of the 256-row
+// tiles; at T = 1024 (16 rows) the tiles gain on the second GEMM (1.01 ->
+// 0.90 ms) and lose on the first (1.72 -> 1.75 ms)
+bool gemm_uses_big_tiles(int64_t G, int64_t M, int64_t K, bool tiled) {
+  return tiled && M >= BIG && M >= (K > 4096 ? 32 : 16) * G;
+}
 
 template <bool FUSE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
@@ -1774,7 +1783,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   }
   // a workgroup covers 256 weight rows: 256 output columns, or (fused) 128
   // columns of h from 128 gate and 128 up rows
-  if (gemm_uses_big_tiles(a.G, a.M, true) && (a.a_dq || !FUSE)) {
+  if (gemm_uses_big_tiles(a.G, a.M, a.K, true) && (a.a_dq || !FUSE)) {
     // many rows per group: 128-row (A in f16 form) or 256-row tiles on the
     // matrix-core kernels (with A in f16 form also a group's last tile if it
     // has kBigMinLast rows or more), the rows left over at the end of each
@@ -1849,17 +1858,6 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if (a.M > 40 * a.G) {
-    // between 40 and 64 rows per group on average (below the 256-row
-    // tiles): 64-row slots read each group's weights half as often as
-    // 32-row slots, which outweighs their lower occupancy (two workgroups
-    // per compute unit instead of three); measured on the routed layer:
-    // T = 3072 (48 rows per group) 4.87 -> 4.35 ms, T = 2048 (32) even,
-    // T = 1536 (24) 20% slower
-    const int64_t work2 = ((a.M + 63) / 64 + a.G) * n_tiles;
-    hipLaunchKernelGGL((gemm_stream32<NBW, 2, FUSE>), dim3((unsigned)work2), dim3(256), 0, s, a, n_tiles, 0, 0, work2);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL((gemm_stream32<NBW, 1, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0, work);
   return hipGetLastError();
 }
@@ -1897,7 +1895,7 @@ int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tile
   // the streaming path with fewer than 512 workgroups (two per compute unit)
   // splits K; the reduction's grid has one row per block
   if (!tiled || M < 1 || M > 65535 || K % 256) return 1;
-  if (gemm_uses_big_tiles(G, M, tiled)) {
+  if (gemm_uses_big_tiles(G, M, K, tiled)) {
     // one group whose 256-row tiles would leave half the compute units idle
     // or more: about 256 workgroups over k ranges of at least one 256-k
     // step (used with the f16 form of A only)

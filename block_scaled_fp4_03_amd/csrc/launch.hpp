@@ -97,8 +97,8 @@ struct GemmArgs {
 // of partial sums it needs
 int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled);
 size_t gemm_splitk_bytes(int64_t G, int64_t M, int64_t N, int64_t K, bool tiled);
-// true when launch_grouped_gemm runs the 256 x 256 tiles (which read a_dq)
-bool gemm_uses_big_tiles(int64_t G, int64_t M, bool tiled);
+// true when launch_grouped_gemm runs the matrix-core tiles (which read a_dq)
+bool gemm_uses_big_tiles(int64_t G, int64_t M, int64_t K, bool tiled);
 // true when launch_tiled, given A in f16 form and a split-K workspace, runs
 // one group of at most 128 rows on the 128-row tiles split over K
 bool gemm_small_split(int64_t G, int64_t M, bool tiled);

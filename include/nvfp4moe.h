@@ -240,8 +240,9 @@ int32_t moe_route_permute_shared(const float* logits, int64_t T, int32_t E, int3
  *                      dequantised without its global scale, as the dq
  *                      output of nvfp4_quantize or silu_mul_requant writes
  *                      it.  It MUST agree with a_codes/a_scales: a kernel
- *                      reads whichever form suits it (the 256-row tiles of
- *                      the tiled layout copy it straight into local memory),
+ *                      reads whichever form suits it (the matrix-core tiles
+ *                      of the tiled layout copy it straight into local
+ *                      memory),
  *                      and both give the same products.  Ignored when
  *                      a_rows * K * 2 >= 2^32.
  *   w_codes, w_scales  [G, N, K/2], [G, N, K/16] when w_layout is
@@ -343,11 +344,11 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
  *   nvfp4_grouped_gemm(h_codes, h_scales, h_gs, R, NULL, NULL, w2_tiled,
  *   NULL, NVFP4_LAYOUT_TILED, w2_gs, {0, H}, 1, expert_offsets, G, R, H, I,
  *   y, NVFP4_DTYPE_BF16, H, NULL, 0): h is identical; y is identical where
- *   that second call streams its weights in 32- or 64-row slots (few rows
- *   per group, the decode regime) and within the float32 summation bound of
- *   the exact contraction in every case.  Every group is processed in
- *   32-row slots, so the launch suits few rows per group; with many rows per
- *   group the two calls (256-row tiles) are faster.
+ *   that second call streams its weights in 32-row slots (few rows per
+ *   group, the decode regime) and within the float32 summation bound of the
+ *   exact contraction in every case.  Every group is processed in 32-row
+ *   slots, so the launch suits few rows per group; with many rows per group
+ *   the two calls (matrix-core tiles) are faster.
  *   x_codes, x_scales  NVFP4 layer input [x_rows, H/2], [x_rows, H/16];
  *                      x_gs ONE float32.
  *   sorted_token_ids   [R] int32 or NULL: row m of the experts' input is
@@ -386,8 +387,10 @@ int32_t nvfp4_moe_expert_mlp(const uint8_t* x_codes, const uint8_t* x_scales, co
 /*
  * nvfp4_grouped_gemm_reads_dq - 1 if nvfp4_grouped_gemm with these sizes
  * (G groups, M rows, depth K, a_rows stored A rows) and weight layout reads
- * a_dq when it is given (its 256-row tiles do), else 0.  Lets a caller
- * produce the f16 form of A only where it is used.  Pure host function; it
+ * a_dq when it is given, else 0: the tiled layout's matrix-core tiles read
+ * it, which run from 32 rows per group on average (16 where K <= 4096) and
+ * for one group of at most 128 rows split over K.  Lets a caller produce the
+ * f16 form of A only where it is used.  Pure host function; it
  * neither fails nor sets the last error.
  */
 int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_rows, int32_t w_layout);

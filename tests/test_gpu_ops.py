@@ -259,36 +259,44 @@ def test_gemm_big_tiles_with_remainders():
     _gemm_case([1024, 255, 257], 256, 768, [0, 256], 13, out_bf16=True)
 
 
-def test_gemm_64_row_streaming_slots():
-    # 40..64 rows per group on average (below the 256-row tiles): 64-row
-    # slots, with an empty group, a group of two slots, partial column tiles
+def test_gemm_tiles_from_16_or_32_rows_per_group():
+    # 16..64 rows per group on average: the matrix-core tiles from 32 rows
+    # per group (16 where K <= 4096), each group's rows as 32/64/128-row
+    # tiles; with an empty group, a group of two slots, partial column tiles
+    assert ops.gemm_reads_dq(7, 336, 512, 336, True)
+    assert ops.gemm_reads_dq(16, 16 * 17, 4096, 16 * 17, True)
+    assert not ops.gemm_reads_dq(16, 16 * 17, 4352, 16 * 17, True)
     _gemm_case([40, 55, 0, 47, 63, 41, 90], 320, 512, [0, 160, 320], 31, gather=True)
+    _gemm_case([17] * 15 + [30], 320, 4096, [0, 320], 35, gather=True, out_bf16=True)
+    # below 256 rows in all: the streaming kernel
+    assert not ops.gemm_reads_dq(5, 224, 768, 224, True)
     _gemm_case([65, 44, 50, 64, 1], 200, 768, [0, 200], 32, gather=True, out_bf16=True)
 
 
 def test_gemm_big_tiles_every_last_tile_height():
     # group sizes whose last tile takes each form: with A in f16 form a
-    # 128-row tile for 65..127 rows past the full 128-row tiles and the
-    # streaming kernel for 1..64; without it (the 256-row kernel) the
-    # left-over rows 1, 31, 32, 33, 64, 65, 128, 129, 255
+    # 32-, 64- or 128-row tile past the full 128-row tiles; without it (the
+    # 256-row kernel) the streaming kernel takes the left-over rows 1, 31,
+    # 32, 33, 64, 65, 128, 129, 255
     _gemm_case([257, 287, 288, 289, 320, 321, 384, 385, 511, 256], 96, 256, [0, 40, 96], 14, gather=True)
     _gemm_case([257, 288, 289, 320, 321, 384, 385], 64, 4608, [0, 64], 17, gather=True)
 
 
 def test_gemm_big_tiles_last_tile_heights_at_model_depths():
     # the last-tile forms at the depths of the MoE layer's two GEMMs (K = 7168
-    # for gate_up, 3072 for down): 65..128 left-over rows as a 128-row tile,
-    # 129..255 as a 256-row tile, <= 64 on the streaming kernel
+    # for gate_up, 3072 for down): left-over rows past the full 128-row tiles
+    # as a 32-, 64- or 128-row tile
     _gemm_case([257, 300, 320, 321, 384, 385, 511, 64], 64, 7168, [0, 32, 64], 33, gather=True)
     _gemm_case([260, 289, 330, 400, 449, 600, 33], 96, 3072, [0, 96], 34, gather=True, out_bf16=True)
 
 
 def test_gemm_left_over_rows_beyond_one_round_of_the_persistent_grid():
-    # 400 groups of 257..320 rows at N = 1024: each group's 1..64 rows past
-    # its 256-row tile go to the persistent streaming kernel, about 600
-    # 32-row slots x 4 column tiles = 2400 tiles for its 768 workgroups, so
-    # every workgroup runs several rounds.  Codes and scales are random bytes
-    # (any NVFP4 operand is valid input); A comes with its f16 form.
+    # 400 groups of 257..320 rows at N = 1024.  Without A's f16 form each
+    # group's 1..64 rows past its 256-row tile go to the persistent streaming
+    # kernel, about 600 32-row slots x 4 column tiles = 2400 tiles for its
+    # 768 workgroups, so every workgroup runs several rounds; with it they
+    # are 32- and 64-row tiles of the 128-row launch.  Codes and scales are
+    # random bytes (any NVFP4 operand is valid input).
     log("gemm left-over rounds")
     rng = np.random.default_rng(40)
     G, N, K = 400, 1024, 256
@@ -308,16 +316,18 @@ def test_gemm_left_over_rows_beyond_one_round_of_the_persistent_grid():
     assert ops.gemm_reads_dq(G, M, K, M, True)
     tiled = ops.prepare_weights(T(wc), T(ws))
     a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16))
-    out = to_np(ops.grouped_gemm(T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), [0, N],
-                                 T(off), M, w_tiled=tiled, a_dq=a_dq))
-    worst = 0.0
-    for g in range(G):
-        r0, r1 = int(off[g]), int(off[g + 1])
-        # every left-over row, and 8 rows of the group's 256-row tile
-        rows = np.concatenate([np.arange(r0 + 256, r1), r0 + rng.choice(256, 8, replace=False)])
-        ex, ab = exact_gemm_rows(ac[rows], as_[rows], wc[g], ws[g])
-        worst = max(worst, check_gemm(out[rows], ex, ab, float(F32(ags * wgs[g, 0])), K, False, "group %d" % g))
-    log("  %d left-over slots x %d column tiles; max err / rms = %.3g" % (slots, N // 256, worst))
+    for dq in (None, a_dq):
+        out = to_np(ops.grouped_gemm(T(ac), T(as_), torch.tensor([ags], device=d), T(wc), T(ws), T(wgs), [0, N],
+                                     T(off), M, w_tiled=tiled, a_dq=dq))
+        worst = 0.0
+        for g in range(G):
+            r0, r1 = int(off[g]), int(off[g + 1])
+            # every left-over row, and 8 rows of the group's first 256 rows
+            rows = np.concatenate([np.arange(r0 + 256, r1), r0 + rng.choice(256, 8, replace=False)])
+            ex, ab = exact_gemm_rows(ac[rows], as_[rows], wc[g], ws[g])
+            worst = max(worst, check_gemm(out[rows], ex, ab, float(F32(ags * wgs[g, 0])), K, False, "group %d" % g))
+        log("  %s: %d left-over slots x %d column tiles; max err / rms = %.3g" % (
+            "f16 A" if dq is not None else "codes A", slots, N // 256, worst))
 
 
 def test_gemm_big_tiles_split_k_one_group():
