@@ -580,14 +580,19 @@ def test_fused_silu_requant_decode_shaped():
 
 
 def test_fused_silu_requant_big_tiles():
-    # 256-row tiles, last tiles of every size class, with and without A's f16 form
+    # many rows per group: with A's f16 form 128-row tiles and last tiles of
+    # 32, 64 and 128 rows; without it the fused GEMM streams in 32-row slots
     counts = [456, 3, 256, 0, 611, 70, 385]
     _fused_case(counts, 256, 512, 22, use_dq=True)
     _fused_case(counts, 256, 512, 23, use_dq=False)
 
 
-def test_fused_silu_requant_64_row_slots():
+def test_fused_silu_requant_32_to_128_row_groups():
+    # 16..64 rows per group on average: without A's f16 form the fused GEMM
+    # streams in 32-row slots; with it, each group is one 32-, 64- or
+    # 128-row matrix-core tile (or two)
     _fused_case([40, 55, 0, 47, 63, 41, 90], 160, 512, 26)
+    _fused_case([40, 55, 0, 47, 63, 41, 90], 160, 512, 27, use_dq=True)
 
 
 def test_fused_silu_requant_one_group_no_gather():
