@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_short(GemmArgs p, int64_t n_t
 // tile_bm > 0: only rows that tiles of tile_bm rows cover (a group's full
 // tiles and its last tile when that has at least tile_last_min rows); the
 // other rows belong to another kernel's launch.
-__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, int tile_bm, int tile_last_min) {
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   const int64_t m = blockIdx.y;
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (n >= p.N) return;
@@ -1078,10 +1078,6 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, int tile_bm, in
   const int64_t g0 = clampv<int64_t>(p.group_offsets[lo], 0, p.M);
   const int64_t g1 = clampv<int64_t>(p.group_offsets[lo + 1], 0, p.M);
   if (m < g0 || m >= g1) return;
-  if (tile_bm > 0) {
-    const int64_t rows = g1 - g0, rest = rows % tile_bm;
-    if (m - g0 >= rows - rest + (rest >= tile_last_min ? rest : 0)) return;
-  }
   float sum = p.ws[m * p.N + n];
   for (int sp = 1; sp < p.splits; ++sp) sum += p.ws[((int64_t)sp * p.M + m) * p.N + n];
   store_out(p, m, n, alpha_for(p, lo, n, *p.a_gs) * sum);
@@ -1123,11 +1119,6 @@ __device__ __forceinline__ void xcd_tile(int64_t bid, int64_t n_tiles, int64_t& 
 }
 
 constexpr int BIG = 256;
-// with A in f16 form, the last tile of a group goes to the 256-row kernel
-// when it has at least this many rows (65..128 rows: a 128-row tile), fewer
-// to the streaming kernel.  Measured on the prefill layer against 129, 97,
-// 81, 49 and 33: 65 was fastest (1.4-2% of the layer against 129)
-constexpr int kBigMinLast = 65;
 constexpr int kAHalfBytes = BIG * 256;           // 64 KiB per f16 half-tile
 constexpr int kBigThreads = 256;
 
@@ -1328,28 +1319,26 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big32(GemmArgs p, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// gemm_big32_dq: the 256 x 256 tiles of gemm_big32 when A also comes in its
-// exactly dequantised f16 form (a_dq), for every row of every group: the
-// last tile of a group may be partial.  A half-tiles go from global memory
-// straight into local memory (global_load_lds_dwordx4, 1 KiB = four 256-byte
-// rows per wave instruction), so A costs the waves neither vector registers
-// nor conversion work, and the vector unit only dequantises W.
-//  * A tile of R = 32 RB rows (RB = 8, or 4, 2, 1 for the last tile of a
-//    group with at most 128, 64, 32 rows) is copied by the four waves, wave w
+// big_dq_tile: one tile of up to 128 rows x 256 columns when A also comes in
+// its exactly dequantised f16 form (a_dq).  A half-tiles go from global
+// memory straight into local memory (buffer loads into LDS, 1 KiB = four
+// 256-byte rows per wave instruction), so A costs the waves neither vector
+// registers nor conversion work, and the vector unit only dequantises W.
+//  * The tile has R = 32 RB rows (RB = 4, or 2 or 1 for a group's last tile
+//    of at most 64 or 32 rows); each wave computes all R rows x 64 columns
+//    (RB x 2 blocks of 32 x 32).  The four waves copy the rows, wave w
 //    taking rows 8 RB w .. 8 RB w + 8 RB - 1 in 2 RB copies: copy i fills
 //    rows 8 RB w + 4 i .. +3, lane l writing physical chunk l % 16 of row
 //    8 RB w + 4 i + l / 16.  That chunk holds logical chunk (l % 16) ^ (row %
 //    16) (the swizzle of gemm_big32), so the lane reads those 16 bytes of
 //    the row.  Rows past the group's end copy its last row; their results
 //    are not stored.
-//  * The next half-tile's copies are spread over substeps 0-3; the next
-//    half-step's W words are loaded at substep 0 into a second register set.
-//    Nothing is waited for before substep 7, when the next half-step's first
-//    W fragment is dequantised; the copies have landed by the barrier.
-//    (The compiler waits for all outstanding vector memory operations once
-//    copies into local memory and register loads are both in flight, so no
-//    load is issued after substep 0 that substeps 1-6 would wait for.)
-// Output of one wave's block of the 256-row tile (RB row blocks of 32, two
+//  * The next half-tile's copies are spread over substeps 0-3.  W words are
+//    loaded two half-steps ahead (PF = 2: after the half-step's copies, at
+//    substep 4, into three register sets that rotate) or one (PF = 1: at
+//    substep 0, into a second set); the barrier at the end of a half-step
+//    waits for the copies only.
+// Output of one wave's block of a tile (RB row blocks of 32, two
 // column blocks of 32) staged through LDS, 32 rows at a time, so that every
 // lane stores 16 contiguous bytes of one row: a quarter (f32) or an eighth
 // (bf16) of the store instructions of one element per lane, and no address
@@ -1405,7 +1394,9 @@ __device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds,
 
 // s_waitcnt immediate: vmcnt 6, expcnt 0, lgkmcnt 0
 constexpr int kVmcnt6 = 6;
-template <int RB, bool FUSE, bool SPLIT = false, int HALF = kAHalfBytes, int PF = 1>
+constexpr int BIG4 = 128;
+constexpr int kA4HalfBytes = BIG4 * 256;   // 32 KiB per f16 half-tile
+template <int RB, bool FUSE, bool SPLIT = false, int PF = 2>
 __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int g, int64_t row0, int64_t row1,
                                             int64_t n0, int wave, int lane, int64_t hs0 = 0, int64_t hs1 = -1,
                                             int split = 0) {
@@ -1440,7 +1431,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
       (void*)p.a_dq, (short)0, (int)(uint32_t)(p.a_rows * K * 2), 0x00020000);
   auto a_copy = [&](int64_t hs, int buf, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        a_rsrc, (__attribute__((address_space(3))) void*)(lds + buf * HALF + (8 * RB * wave + 4 * i) * 256),
+        a_rsrc, (__attribute__((address_space(3))) void*)(lds + buf * kA4HalfBytes + (8 * RB * wave + 4 * i) * 256),
         16, (int)a_off[i], (int)(hs * 256), 0, 0);
   };
 
@@ -1517,7 +1508,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
     // the last half-step reloads itself (into the unused buffer and registers)
     const int64_t hn = hs + 1 < hs1 ? hs + 1 : hs;
     if constexpr (PF == 1) w_load(hn, nx);
-    const uint8_t* abuf = lds + h * HALF + c * 256;
+    const uint8_t* abuf = lds + h * kA4HalfBytes + c * 256;
     half8_t af[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) af[rb] = *(const half8_t*)(abuf + rb * 32 * 256 + chunk_ofs[0]);
@@ -1653,105 +1644,66 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   }
 }
 
-// SPLIT: the grid is splits x tiles (split-major); each split sums its k
-// range into the float32 workspace (splitk_reduce adds the ranges in order).
-template <bool FUSE, bool SPLIT = false>
-__global__ __launch_bounds__(kBigThreads, 1) void gemm_big32_dq(GemmArgs p, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAHalfBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tiles = SPLIT ? gridDim.x / p.splits : gridDim.x;
-  const int split = SPLIT ? (int)(blockIdx.x / tiles) : 0;
-  int64_t slot, nt;
-  xcd_tile((int64_t)blockIdx.x - split * tiles, n_tiles, slot, nt);
-  int g;
-  int64_t row0, row1;
-  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG, kBigMinLast, 0, 0, g, row0, row1)) return;
-  g = __builtin_amdgcn_readfirstlane(g);
-  row0 = __builtin_amdgcn_readfirstlane((int)row0);
-  row1 = __builtin_amdgcn_readfirstlane((int)row1);
-  const int64_t n0 = nt * BIG;
-  const int64_t rows = row1 - row0;
-  if constexpr (SPLIT) {
-    const int64_t nks = p.K / 256;
-    big_dq_tile<8, false, true>(p, lds, g, row0, row1, n0, wave, lane, 2 * (nks * split / p.splits),
-                                2 * (nks * (split + 1) / p.splits), split);
-  } else if constexpr (kBigMinLast > 128) {
-    big_dq_tile<8, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
-  } else {
-    if (rows > 128)
-      big_dq_tile<8, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
-    else if (rows > 64 || kBigMinLast > 64)
-      big_dq_tile<4, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
-    else if (rows > 32 || kBigMinLast > 32)
-      big_dq_tile<2, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
-    else
-      big_dq_tile<1, FUSE>(p, lds, g, row0, row1, n0, wave, lane);
-  }
-}
-
-// gemm_big32_dq4: 128 x 256 tiles of the same loop (RB = 4: each wave 128
-// rows x 64 columns, 128 accumulators), at most 256 registers per lane and
-// 64 KiB of local memory, so two workgroups share a compute unit: each SIMD
-// runs one wave of each, and while one workgroup waits at its per-half-step
-// barrier, or runs a tile's prologue or epilogue, the other's waves keep the
-// matrix core busy.  A W fragment feeds four MFMAs instead of eight (twice
-// the dequantisation work per MFMA), which the second wave hides.  A group's
-// last tile of kBig4MinLast rows or more is a tile of this launch too, 32, 64
-// or 128 rows high (the smallest that holds it); fewer rows are left to the
-// streaming kernel.
-constexpr int BIG4 = 128;
-#ifndef NVFP4_BIG4_MIN_LAST
-#define NVFP4_BIG4_MIN_LAST 1
-#endif
-constexpr int kBig4MinLast = NVFP4_BIG4_MIN_LAST;
-#ifndef NVFP4_BIG4_PREFETCH
-#define NVFP4_BIG4_PREFETCH 2
-#endif
-constexpr int kBig4Prefetch = NVFP4_BIG4_PREFETCH;
+// gemm_big32_dq4: the 128 x 256 tiles (RB = 4: each wave 128 rows x 64
+// columns, 128 accumulators), at most 256 registers per lane and 64 KiB of
+// local memory, so two workgroups share a compute unit: each SIMD runs one
+// wave of each, and while one workgroup waits at its per-half-step barrier,
+// or runs a tile's prologue or epilogue, the other's waves keep the matrix
+// core busy.  Every group's rows are cut into 128-row tiles, the last one 32,
+// 64 or 128 rows high (the smallest that holds it).
 template <bool FUSE>
 __global__ __launch_bounds__(kBigThreads, 2) void gemm_big32_dq4(GemmArgs p, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kA4HalfBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t slot, nt;
   xcd_tile((int64_t)blockIdx.x, n_tiles, slot, nt);
   int g;
   int64_t row0, row1;
-  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG4, kBig4MinLast, 0, 0, g, row0, row1)) return;
+  if (!find_tile_batched(p.group_offsets, p.G, p.M, slot, BIG4, 1, 0, 0, g, row0, row1)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   row0 = __builtin_amdgcn_readfirstlane((int)row0);
   row1 = __builtin_amdgcn_readfirstlane((int)row1);
   const int64_t rows = row1 - row0;
-  if (rows > 64 || kBig4MinLast > 64)
-    big_dq_tile<4, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
-  else if (rows > 32 || kBig4MinLast > 32)
-    big_dq_tile<2, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+  if (rows > 64)
+    big_dq_tile<4, FUSE>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+  else if (rows > 32)
+    big_dq_tile<2, FUSE>(p, lds, g, row0, row1, nt * BIG, wave, lane);
   else
-    big_dq_tile<1, FUSE, false, BIG4 * 256, kBig4Prefetch>(p, lds, g, row0, row1, nt * BIG, wave, lane);
+    big_dq_tile<1, FUSE>(p, lds, g, row0, row1, nt * BIG, wave, lane);
 }
 
-// One group of at most 128 rows (the shared expert), A in f16 form, K split:
-// block b takes column tile b % n_tiles and k range b / n_tiles of the
-// 128 x 256 tile loop above (A through local memory, each weight tile read
-// once for all rows), writing raw partial sums that splitk_reduce adds in
-// range order.  No tile search: the group is rows [offsets[0], offsets[1]).
-__global__ __launch_bounds__(kBigThreads, 2) void gemm_small_dq4_split(GemmArgs p, int64_t n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BIG4 * 256];
+// One group (G = 1) with few tiles for the chip, A in f16 form, K split:
+// block b takes k range b / (n_slots n_tiles), then row slot and column tile
+// of the 128 x 256 tile loop above (A through local memory, each weight tile
+// read once per 128 rows), writing raw partial sums that splitk_reduce adds
+// in range order.  No tile search: the group is rows [offsets[0],
+// offsets[1]), cut into 128-row slots (the last one partial).
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_dq4_split(GemmArgs p, int64_t n_slots, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kA4HalfBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = (int)(blockIdx.x / n_tiles);
-  const int64_t nt = (int64_t)blockIdx.x - split * n_tiles;
-  const int64_t row0 = clampv<int64_t>(p.group_offsets[0], 0, p.M);
-  int64_t row1 = clampv<int64_t>(p.group_offsets[1], 0, p.M);
-  row1 = clampv<int64_t>(row1, row0, row0 + BIG4);
+  const int64_t per_split = n_slots * n_tiles;
+  const int split = (int)(blockIdx.x / per_split);
+  const int64_t rem = (int64_t)blockIdx.x - split * per_split;
+  const int64_t slot = rem / n_tiles, nt = rem - slot * n_tiles;
+  const int64_t g0 = clampv<int64_t>(p.group_offsets[0], 0, p.M);
+  const int64_t g1 = clampv<int64_t>(p.group_offsets[1], g0, p.M);
+  const int64_t row0 = g0 + slot * BIG4;
+  const int64_t row1 = row0 + BIG4 < g1 ? row0 + BIG4 : g1;
   if (row1 <= row0) return;
   const int64_t nks = p.K / 256;
-  big_dq_tile<4, false, true, BIG4 * 256>(p, lds, 0, row0, row1, nt * BIG, wave, lane, 2 * (nks * split / p.splits),
-                                          2 * (nks * (split + 1) / p.splits), split);
+  const int64_t hs0 = 2 * (nks * split / p.splits), hs1 = 2 * (nks * (split + 1) / p.splits);
+  if (row1 - row0 > 64)
+    big_dq_tile<4, false, true>(p, lds, 0, row0, row1, nt * BIG, wave, lane, hs0, hs1, split);
+  else if (row1 - row0 > 32)
+    big_dq_tile<2, false, true>(p, lds, 0, row0, row1, nt * BIG, wave, lane, hs0, hs1, split);
+  else
+    big_dq_tile<1, false, true>(p, lds, 0, row0, row1, nt * BIG, wave, lane, hs0, hs1, split);
 }
 
-// whether launch_tiled runs gemm_small_dq4_split (given A in f16 form)
+// whether launch_tiled, given A in f16 form and a split-K workspace, runs
+// one group of at most 128 rows on gemm_dq4_split
 bool gemm_small_split(int64_t G, int64_t M, bool tiled) { return tiled && G == 1 && M >= 1 && M <= BIG4; }
 
 // ---------------------------------------------------------------------------
@@ -1769,74 +1721,51 @@ bool gemm_uses_big_tiles(int64_t G, int64_t M, int64_t K, bool tiled) {
 template <bool FUSE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   if constexpr (!FUSE) {
-    if (a.a_dq && a.splits > 1 && a.ws && gemm_small_split(a.G, a.M, true)) {
-      // one group of at most 128 rows: the 128-row tiles split over K, then
-      // the partial sums reduced in order
+    if (a.a_dq && a.splits > 1 && a.ws && a.G == 1) {
+      // one group with few tiles for the chip (gemm_splitk_splits): the
+      // 128-row tiles split over K, then the partial sums reduced in order
       const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-      hipLaunchKernelGGL(gemm_small_dq4_split, dim3((unsigned)(n_tiles * a.splits)), dim3(kBigThreads), 0, s, a,
-                         n_tiles);
+      const int64_t n_slots = (a.M + BIG4 - 1) / BIG4;
+      hipLaunchKernelGGL(gemm_dq4_split, dim3((unsigned)(n_slots * n_tiles * a.splits)), dim3(kBigThreads), 0, s,
+                         a, n_slots, n_tiles);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a, 0, 0);
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
   // a workgroup covers 256 weight rows: 256 output columns, or (fused) 128
   // columns of h from 128 gate and 128 up rows
   if (gemm_uses_big_tiles(a.G, a.M, a.K, true) && (a.a_dq || !FUSE)) {
-    // many rows per group: 128-row (A in f16 form) or 256-row tiles on the
-    // matrix-core kernels (with A in f16 form also a group's last tile if it
-    // has kBigMinLast rows or more), the rows left over at the end of each
-    // group on the streaming kernel.  Tile counts are upper bounds (the
-    // group sizes are on the device); workgroups without a tile exit.
-    const bool dq = a.a_dq != nullptr;
-    // A in f16 form, no split K, plain output: 128-row tiles, two workgroups
-    // per compute unit (gemm_big32_dq4); else 256-row tiles
-    const bool dq4 = dq && !(!FUSE && a.splits > 1 && a.ws);
-    const int tile_rows = dq4 ? BIG4 : BIG;
-    const int skip_min = dq4 ? kBig4MinLast : dq ? kBigMinLast : BIG;
-    hipError_t e = hipSuccess;
-    if (skip_min > 1) {
-      constexpr int NBW = 2, RB = 1;
-      const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
-      // a group leaves fewer than skip_min rows over: at most that many
-      // 32-row tiles per group, and at most M / 32 + G in all
-      const int64_t per_group = (skip_min - 1 + 32 * RB - 1) / (32 * RB);
-      const int64_t work_s =
-          std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, per_group * a.G) * n_tiles_s;
-      // persistent: three workgroups per compute unit (164 VGPRs with two
-      // half-steps of loads in flight)
-      const int64_t grid_s = std::min<int64_t>(work_s, 768);
-      hipLaunchKernelGGL((gemm_stream32<NBW, RB, FUSE, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a,
-                         n_tiles_s, tile_rows, skip_min, work_s);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    // many rows per group.  Tile counts are upper bounds (the group sizes are
+    // on the device); workgroups without a tile exit.
     const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-    const int64_t slots = (a.M / BIG + (dq ? a.G : 0) + 7) / 8 * 8;
-    if constexpr (!FUSE) {
-      if (dq && a.splits > 1 && a.ws) {
-        // one group with fewer tiles than compute units: K split, the
-        // partial sums reduced in order (only the rows of these tiles: the
-        // left-over rows are already in out)
-        hipLaunchKernelGGL((gemm_big32_dq<false, true>), dim3((unsigned)(slots * n_tiles * a.splits)),
-                           dim3(kBigThreads), 0, s, a, n_tiles);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a,
-                           BIG, kBigMinLast);
-        return hipGetLastError();
-      }
-    }
-    if (dq4) {
+    if (a.a_dq) {
+      // A in f16 form: 128-row tiles, two workgroups per compute unit, each
+      // group's last tile 32, 64 or 128 rows high
       const int64_t slots4 = (a.M / BIG4 + a.G + 7) / 8 * 8;
       hipLaunchKernelGGL(gemm_big32_dq4<FUSE>, dim3((unsigned)(slots4 * n_tiles)), dim3(kBigThreads), 0, s, a,
                          n_tiles);
-    } else if (dq)
-      hipLaunchKernelGGL(gemm_big32_dq<FUSE>, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a,
-                         n_tiles);
-    else if constexpr (!FUSE)
+      return hipGetLastError();
+    }
+    if constexpr (!FUSE) {
+      // A as codes only: full 256-row tiles (gemm_big32), the rows each
+      // group leaves over on the streaming kernel, persistent: three
+      // workgroups per compute unit (164 VGPRs with two half-steps of loads
+      // in flight)
+      constexpr int NBW = 2, RB = 1;
+      const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+      // a group leaves fewer than 256 rows over: at most 8 32-row tiles per
+      // group, and at most M / 32 + G in all
+      const int64_t work_s = std::min<int64_t>((a.M + 32 * RB - 1) / (32 * RB) + a.G, 8 * a.G) * n_tiles_s;
+      const int64_t grid_s = std::min<int64_t>(work_s, 768);
+      hipLaunchKernelGGL((gemm_stream32<NBW, RB, false, false, true>), dim3((unsigned)grid_s), dim3(256), 0, s, a,
+                         n_tiles_s, BIG, BIG, work_s);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t slots = (a.M / BIG + 7) / 8 * 8;
       hipLaunchKernelGGL(gemm_big32, dim3((unsigned)(slots * n_tiles)), dim3(kBigThreads), 0, s, a, n_tiles);
+    }
     return hipGetLastError();
   }
   constexpr int NBW = 2;
@@ -1854,7 +1783,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
                            dim3(256), 0, s, a, n_tiles, 0, 0, work);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a, 0, 0);
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -1896,13 +1825,13 @@ int32_t gemm_splitk_splits(int64_t G, int64_t M, int64_t N, int64_t K, bool tile
   // splits K; the reduction's grid has one row per block
   if (!tiled || M < 1 || M > 65535 || K % 256) return 1;
   if (gemm_uses_big_tiles(G, M, K, tiled)) {
-    // one group whose 256-row tiles would leave half the compute units idle
-    // or more: about 256 workgroups over k ranges of at least one 256-k
-    // step (used with the f16 form of A only)
+    // one group whose 128-row tiles would leave a compute unit without its
+    // second workgroup: about 512 workgroups over k ranges of at least one
+    // 256-k step (used with the f16 form of A only)
     if (G != 1) return 1;
-    const int64_t tiles = ((M + BIG - 1) / BIG) * ((N + BIG - 1) / BIG);
-    if (tiles > 128) return 1;
-    const int64_t sp = std::min<int64_t>(std::min<int64_t>(256 / tiles, K / 256), 8);
+    const int64_t tiles = ((M + BIG4 - 1) / BIG4) * ((N + BIG - 1) / BIG);
+    if (tiles > 256) return 1;
+    const int64_t sp = std::min<int64_t>(std::min<int64_t>(512 / tiles, K / 256), 8);
     return sp > 1 ? (int32_t)sp : 1;
   }
   const int64_t base = ((M + 31) / 32 + G) * ((N + 255) / 256);

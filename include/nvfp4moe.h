@@ -284,8 +284,8 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
  * nvfp4_grouped_gemm_workspace_size - bytes of device workspace with which
  * nvfp4_grouped_gemm of these sizes and weight layout splits K (0: it never
  * does).  With few workgroups for the chip (tiled layout: few groups and
- * rows, up to 16 ranges; or one group of at least 256 rows whose 256-row
- * tiles number at most 128 and whose A comes in f16 form, up to 8 ranges), K
+ * rows, up to 16 ranges; or one group whose 128-row tiles number at most 256
+ * and whose A comes in f16 form, up to 8 ranges), K
  * is cut into ranges whose raw float32 partial sums are written to the
  * workspace and then added in range order by a second kernel
  * (deterministic), which applies alpha once.  A NULL or smaller workspace

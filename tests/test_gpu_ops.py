@@ -331,10 +331,9 @@ def test_gemm_left_over_rows_beyond_one_round_of_the_persistent_grid():
 
 
 def test_gemm_big_tiles_split_k_one_group():
-    # one group with few 256-row tiles: K is split over the tiles (f16 A);
-    # the partial sums are reduced only on the tiles' rows, the left-over rows
-    # (50 here) come from the streaming kernel, a last tile of 140 rows from
-    # the split tiles
+    # one group with few 128-row tiles: K is split over them (f16 A, 8
+    # ranges), every row, the last partial slot (50 or 12 rows) included,
+    # from the split tiles and the reduction
     assert ops.gemm_workspace_size(1, 562, 512, 2048, True) > 0
     _gemm_case([562], 512, 2048, [0, 300, 512], 18)
     _gemm_case([652], 512, 2048, [0, 512], 19, gather=True, out_bf16=True)
