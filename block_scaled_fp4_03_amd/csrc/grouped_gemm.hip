@@ -50,6 +50,13 @@ __device__ __forceinline__ T clampv(T v, T lo, T hi) {
 // row add 0), then the last lane of row 0 (of row 2) is added to row 1 (row 3),
 // and lane 31 to rows 2 and 3.  No local-memory round trips, unlike a
 // shuffle-based scan.
+// x of another lane of the same DPP row (16 lanes), by a DPP control that
+// reads within the row (every lane has a source)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
@@ -514,19 +521,24 @@ __device__ __forceinline__ void silu_requant_block(const GemmArgs& p, const floa
     const float gv = alpha_g * gacc[i];
     const float uv = alpha_u * uacc[i];
     const float h = silu_mul(gv, uv);
+    // the block's 16 lanes are one DPP row: max over each quad (two quad
+    // permutations), then over the two quads of each half row (half-row
+    // mirror), then over the two halves (row mirror); every lane ends with
+    // the row's maximum
     float bmax = __builtin_fabsf(h);
-    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 1, 64));
-    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 2, 64));
-    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 4, 64));
-    bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 8, 64));
+    bmax = __builtin_fmaxf(bmax, dpp_f32<0xB1>(bmax));    // quad_perm [1,0,3,2]
+    bmax = __builtin_fmaxf(bmax, dpp_f32<0x4E>(bmax));    // quad_perm [2,3,0,1]
+    bmax = __builtin_fmaxf(bmax, dpp_f32<0x141>(bmax));   // row_half_mirror
+    bmax = __builtin_fmaxf(bmax, dpp_f32<0x140>(bmax));   // row_mirror
     float r;
     bool zero;
     const uint32_t sq = block_scale(bmax, gs, r, zero);
     const uint32_t code = e2m1_code(h, r, zero);
     uint32_t word = code << (4 * (c & 7));
-    word |= __shfl_xor(word, 1, 64);
-    word |= __shfl_xor(word, 2, 64);
-    word |= __shfl_xor(word, 4, 64);
+    // OR over the 8 lanes of each half row (the lane with c % 8 == 0 stores)
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xf, 0xf, false);
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xf, 0xf, false);
+    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x141, 0xf, 0xf, false);
     if (m < row1) {
       if ((c & 7) == 0) *(uint32_t*)(p.h_codes + m * (I / 2) + hcol / 2) = word;
       if ((c & 15) == 0) p.h_scales[m * (I / 16) + hcol / 16] = (uint8_t)sq;
