@@ -506,63 +506,16 @@ __device__ __forceinline__ int acc32_row(int i, int kh) { return 8 * (i >> 2) + 
 // Each value is formed exactly as the unfused GEMM stores it (alpha times
 // the sum, float32), then h = SiLU(gate) * up and its NVFP4 re-quantisation
 // follow the operation sequence of silu_mul_requant, so codes, scales and
-// the f16 copy are identical to the unfused pair of launches.  A 16-element
-// block of h (one row, columns 16 q .. 16 q + 15) lies in the 16 lanes
-// c = 16 q .. 16 q + 15 of one half of the wave: its amax is a 4-step
-// exchange, and lanes c % 8 == 0 store 8 codes as one 32-bit word.
-// One 32-row block (gate accumulators gacc, up accumulators uacc) of the
-// fused epilogue.
-__device__ __forceinline__ void silu_requant_block(const GemmArgs& p, const floatx16_t& gacc, const floatx16_t& uacc,
-                                                   int64_t rbase, int64_t row1, int64_t I, int64_t hcol, int c,
-                                                   int kh, float alpha_g, float alpha_u, float gs) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t m = rbase + acc32_row(i, kh);
-    const float gv = alpha_g * gacc[i];
-    const float uv = alpha_u * uacc[i];
-    const float h = silu_mul(gv, uv);
-    // the block's 16 lanes are one DPP row: max over each quad (two quad
-    // permutations), then over the two quads of each half row (half-row
-    // mirror), then over the two halves (row mirror); every lane ends with
-    // the row's maximum
-    float bmax = __builtin_fabsf(h);
-    bmax = __builtin_fmaxf(bmax, dpp_f32<0xB1>(bmax));    // quad_perm [1,0,3,2]
-    bmax = __builtin_fmaxf(bmax, dpp_f32<0x4E>(bmax));    // quad_perm [2,3,0,1]
-    bmax = __builtin_fmaxf(bmax, dpp_f32<0x141>(bmax));   // row_half_mirror
-    bmax = __builtin_fmaxf(bmax, dpp_f32<0x140>(bmax));   // row_mirror
-    float r;
-    bool zero;
-    const uint32_t sq = block_scale(bmax, gs, r, zero);
-    const uint32_t code = e2m1_code(h, r, zero);
-    uint32_t word = code << (4 * (c & 7));
-    // OR over the 8 lanes of each half row (the lane with c % 8 == 0 stores)
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xf, 0xf, false);
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x4E, 0xf, 0xf, false);
-    word |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0x141, 0xf, 0xf, false);
-    if (m < row1) {
-      if ((c & 7) == 0) *(uint32_t*)(p.h_codes + m * (I / 2) + hcol / 2) = word;
-      if ((c & 15) == 0) p.h_scales[m * (I / 16) + hcol / 16] = (uint8_t)sq;
-      if (p.h_dq) p.h_dq[m * I + hcol] = dq_f16(code, e4m3_decode(sq));
-    }
-  }
-}
-
-// The row blocks rb = RB0 .. RB - 1, by compile-time recursion so that every
-// accumulator index is a constant (a loop the compiler did not unroll would
-// index the accumulators at run time and move them to scratch memory).
-template <int RB, int RB0>
-__device__ __forceinline__ void silu_requant_rows(const GemmArgs& p, const floatx16_t (&acc)[RB][2], int64_t row0,
-                                                  int64_t row1, int64_t I, int64_t hcol, int c, int kh,
-                                                  float alpha_g, float alpha_u, float gs) {
-  if constexpr (RB0 < RB) {
-    silu_requant_block(p, acc[RB0][0], acc[RB0][1], row0 + 32 * RB0, row1, I, hcol, c, kh, alpha_g, alpha_u, gs);
-    silu_requant_rows<RB, RB0 + 1>(p, acc, row0, row1, I, hcol, c, kh, alpha_g, alpha_u, gs);
-  }
-}
-
+// the f16 copy are identical to the unfused pair of launches.
+// h of a 32-row block goes through the wave's own staging area in local
+// memory (32 rows x kHStride floats, st) and comes back one quantisation
+// block per lane: lane l takes row l % 32, columns 32 j + 16 (l / 32) .. +15,
+// so the block's amax, scale, 16 codes and f16 copy are formed once, by one
+// lane, and stored as 8 + 1 + 32 contiguous bytes.
+constexpr int kHStride = 36;   // floats per staged row: 32, plus 4 to shift the next row's banks
 template <int RB>
 __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const floatx16_t (&acc)[RB][2], int g,
-                                                      int64_t row0, int64_t row1, int64_t j, int lane) {
+                                                      int64_t row0, int64_t row1, int64_t j, int lane, float* st) {
   const int c = lane & 31;
   const int kh = lane >> 5;
   const int64_t I = p.N / 2;
@@ -570,7 +523,55 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
   const float a_gs = *p.a_gs;
   const float alpha_g = a_gs * p.w_gs[(int64_t)g * 2];
   const float alpha_u = a_gs * p.w_gs[(int64_t)g * 2 + 1];
-  silu_requant_rows<RB, 0>(p, acc, row0, row1, I, 32 * j + c, c, kh, alpha_g, alpha_u, *p.h_gs);
+  const float gs = *p.h_gs;
+  const int r = lane & 31, hb = lane >> 5;      // after the transpose: row r, half hb of the 32 columns
+  const int64_t hcol = 32 * j + 16 * hb;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float gv = alpha_g * acc[rb][0][i];
+      const float uv = alpha_u * acc[rb][1][i];
+      st[acc32_row(i, kh) * kHStride + c] = silu_mul(gv, uv);
+    }
+    // one wave's local-memory operations complete in issue order: the reads
+    // below see the writes above, and the next block's writes follow them
+    float h[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4_t v = *(const floatx4_t*)(st + r * kHStride + 16 * hb + 4 * q);
+      h[4 * q] = v[0];
+      h[4 * q + 1] = v[1];
+      h[4 * q + 2] = v[2];
+      h[4 * q + 3] = v[3];
+    }
+    float bmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bmax = __builtin_fmaxf(bmax, __builtin_fabsf(h[e]));
+    float rcp;
+    bool zero;
+    const uint32_t sq = block_scale(bmax, gs, rcp, zero);
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t code = e2m1_code(h[e], rcp, zero);
+      if (e < 8) lo |= code << (4 * e);
+      else hi |= code << (4 * (e - 8));
+    }
+    const int64_t m = row0 + 32 * rb + r;
+    if (m < row1) {
+      uint32_t* hc = (uint32_t*)(p.h_codes + m * (I / 2) + hcol / 2);
+      hc[0] = lo;
+      hc[1] = hi;
+      p.h_scales[m * (I / 16) + hcol / 16] = (uint8_t)sq;
+      if (p.h_dq) {
+        // code times the decoded scale, exact in f16 (the values dq_f16 gives)
+        const half2_t sf2 = scale_pair(sq);
+        *(half8_t*)(p.h_dq + m * I + hcol) = dequant8(lo, sf2);
+        *(half8_t*)(p.h_dq + m * I + hcol + 8) = dequant8(hi, sf2);
+      }
+    }
+  }
 }
 
 // gemm_stream32: 32*RB rows x (4 waves x NBW x 32) columns per workgroup; each
@@ -628,7 +629,7 @@ __device__ __forceinline__ void tile_signal(const TileSync& sy) {
 template <int NBW, int RB, bool FUSE, bool SPLIT, bool NT>
 __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t row0, int64_t row1, int64_t nt,
                                               int wave, int lane, int64_t ks0, int64_t ks1, int split,
-                                              const TileSync& sy = TileSync()) {
+                                              const TileSync& sy = TileSync(), float* st = nullptr) {
   static_assert(!FUSE || NBW == 2, "the fused epilogue pairs one gate and one up column block");
   constexpr int BN = 4 * NBW * 32;
   const int c = lane & 31;
@@ -756,7 +757,7 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   if (hs + 1 < nhs) step(hs + 1, s1, s0);
 
   if constexpr (FUSE) {
-    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
+    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane, st);
     return;
   }
   if constexpr (SPLIT) {
@@ -802,10 +803,13 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
   // the group offsets, staged once per workgroup (all loads in flight
   // together) so that the tile search costs no further global round trips
   __shared__ int32_t s_off[kMaxGroups + 1];
+  // the fused epilogue's staging area, 32 rows x kHStride floats per wave
+  __shared__ __attribute__((aligned(16))) float s_epi[FUSE ? 4 * 32 * kHStride : 4];
   for (int i = threadIdx.x; i <= p.G; i += blockDim.x) s_off[i] = p.group_offsets[i];
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* const st = s_epi + (FUSE ? wave * 32 * kHStride : 0);
   // split-K: the grid is splits x (slots x column tiles), split-major
   const int64_t work = SPLIT ? gridDim.x / p.splits : gridDim.x;
   const int split = SPLIT ? (int)(blockIdx.x / work) : 0;
@@ -821,9 +825,9 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
     if (!find_tile(s_off, p.G, p.M, slot, 32 * RB, 1, skip_bm, skip_min, g, row0, row1)) return;
     g = __builtin_amdgcn_readfirstlane(g);
     if (row0 == s_off[g] && row1 == s_off[g + 1])
-      stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+      stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split, TileSync(), st);
     else
-      stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split);
+      stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, lane, ks0, ks1, split, TileSync(), st);
   } else {
     // tiles t0, t0 + grid, ... below `total`; slots grow with t, and the
     // tiles that exist come first, so the first missing one ends the loop
@@ -839,9 +843,9 @@ __global__ __launch_bounds__(256) void gemm_stream32(GemmArgs p, int64_t n_tiles
       int ln = lane;
       asm volatile("" : "+v"(ln));
       if (row0 == s_off[g] && row1 == s_off[g + 1])
-        stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
+        stream32_tile<NBW, RB, FUSE, SPLIT, true>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split, TileSync(), st);
       else
-        stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split);
+        stream32_tile<NBW, RB, FUSE, SPLIT, false>(p, g, row0, row1, nt, wave, ln, ks0, ks1, split, TileSync(), st);
     }
   }
 }
@@ -888,11 +892,14 @@ __global__ __launch_bounds__(256) void gemm_moe_persistent(GemmArgs p1, GemmArgs
                                                           int64_t n_tiles2, int64_t max_slots, int32_t spin_limit) {
   __shared__ int32_t s_off[kMaxGroups + 1];
   __shared__ int64_t s_next[2];
+  // the fused epilogue's staging area, 32 rows x kHStride floats per wave
+  __shared__ __attribute__((aligned(16))) float s_epi[4 * 32 * kHStride];
   for (int i = threadIdx.x; i <= p1.G; i += blockDim.x) s_off[i] = p1.group_offsets[i];
   if (threadIdx.x == 0) s_next[0] = atomicAdd(ctr, 1);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* const st = s_epi + wave * 32 * kHStride;
   // (at most the counters there are: offsets that are not a partition of
   // [0, M) cannot index past them)
   const int64_t slots = std::min<int64_t>(count_tiles(s_off, p1.G, p1.M, 32), max_slots);
@@ -924,9 +931,9 @@ __global__ __launch_bounds__(256) void gemm_moe_persistent(GemmArgs p1, GemmArgs
       sy.spin_limit = spin_limit;
       if (first) {
         if (whole)
-          stream32_tile<2, 1, true, false, true>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy);
+          stream32_tile<2, 1, true, false, true>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy, st);
         else
-          stream32_tile<2, 1, true, false, false>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy);
+          stream32_tile<2, 1, true, false, false>(p1, g, row0, row1, nt, wave, ln, 0, nks1, 0, sy, st);
         // every wave's h stores have reached memory, then one signal for
         // the workgroup's column tile
         __builtin_amdgcn_s_waitcnt(0);
@@ -1602,7 +1609,7 @@ __device__ __forceinline__ void big_dq_tile(const GemmArgs& p, uint8_t* lds, int
   }
 
   if constexpr (FUSE) {
-    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane);
+    silu_requant_epilogue<RB>(p, acc, g, row0, row1, j, lane, (float*)lds + wave * 32 * kHStride);
     return;
   }
   if constexpr (SPLIT) {

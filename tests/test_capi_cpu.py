@@ -205,8 +205,8 @@ def test_global_scale_validation_and_workspace(L):
 
 
 def test_fused_silu_default_choice(L):
-    # the pipeline fuses SiLU-requant into the first GEMM where that GEMM
-    # streams its weights in one pass, and not on 256-row tiles or split K
+    # the pipeline fuses SiLU-requant into the first GEMM wherever the fused
+    # launch applies (streaming and matrix-core tiles), not where K is split
     import torch
     from block_scaled_fp4_03_amd.pipeline import NVFP4Weights
 
@@ -216,7 +216,7 @@ def test_fused_silu_default_choice(L):
                             tiled=m(1) if tiled else None)
 
     assert w1(384).fuse_by_default(1536, 256)                 # decode: 384 experts, 6 x 256 rows
-    assert not w1(384).fuse_by_default(49152, 8192)           # prefill: 256-row tiles
+    assert w1(384).fuse_by_default(49152, 8192)               # prefill: 128-row matrix-core tiles
     assert not w1(1).fuse_by_default(128, 128)                # shared expert: K split
     assert not w1(384, tiled=False).fuse_by_default(1536, 256)  # row-major weights: no fused kernel
     assert not w1(8, I=48).fuse_by_default(64, 32)            # I % 32 != 0
