@@ -97,8 +97,11 @@ class Layer:
         self.dq1 = True if self.w1.reads_dq(R, self.x.shape[0]) else None
         self.dq2 = True if self.w2.reads_dq(R, R) else None
         # the pipeline's default SiLU-requant path for this shape (in the first
-        # GEMM's epilogue where that GEMM streams its weights)
+        # GEMM's epilogue unless it splits K)
         self.fused_default = self.w1.fuse_by_default(R, self.x.shape[0])
+        # the one-launch expert MLP streams every tile in 32-row slots: timed
+        # where the first GEMM streams its weights too (few rows per expert)
+        self.streams = self.dq1 is None
         # workspace of the one-launch expert MLP (tile queue, slot counters)
         self.mlp_ws = torch.empty(max(16, lib.load().nvfp4_moe_expert_mlp_workspace_size(wl.E, R)),
                                   dtype=torch.uint8, device=device)
@@ -285,7 +288,7 @@ def run_gpu(workload, steps, warmup, tokens=None):
     # untimed steps before the first timed block: right after the weight
     # preparation the first blocks of steps measure about 2% slow
     for _ in range(SETTLE_STEPS):
-        layer.step()
+        layer.step(fused=fused)
     torch.cuda.synchronize()
     ms, per_op, pct = time_layer(layer, steps, warmup, fused=fused)
     n_touched = layer.touched_experts()
@@ -306,7 +309,7 @@ def run_gpu(workload, steps, warmup, tokens=None):
         res["other"] = dict(fused=not fused, ms=oms, l1_ms=oper_op["gemm_l1"], tokens_per_s=wl.T / (oms * 1e-3))
     # and with the expert MLP as one persistent launch (where the first GEMM
     # streams its weights: the regime that launch is built for)
-    if fused:
+    if fused and layer.streams:
         pms, pper_op, ppct = time_layer(layer, steps, warmup, persistent=True)
         res["persistent"] = dict(ms=pms, mlp_ms=pper_op["gemm_l1"] + pper_op["silu_mul_requant"] + pper_op["gemm_l2"],
                                  tokens_per_s=wl.T / (pms * 1e-3), step_pct=ppct)
