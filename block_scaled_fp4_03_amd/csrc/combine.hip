@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      o[e] = (uint32_t)bf16_from_float(acc[2 * e]) | ((uint32_t)bf16_from_float(acc[2 * e + 1]) << 16);
+      o[e] = bf16x2_from_float(acc[2 * e], acc[2 * e + 1]);
     *(uint4*)(out + t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }

@@ -1391,10 +1391,10 @@ __device__ __forceinline__ void store_block_vec(const GemmArgs& p, uint8_t* lds,
         const int64_t m = mb + r, n = nw + 8 * ch;
         if (m < row1 && n < p.N) {
           u32x4 w;
-          w[0] = (uint32_t)bf16_from_float(lo[0]) | ((uint32_t)bf16_from_float(lo[1]) << 16);
-          w[1] = (uint32_t)bf16_from_float(lo[2]) | ((uint32_t)bf16_from_float(lo[3]) << 16);
-          w[2] = (uint32_t)bf16_from_float(hi[0]) | ((uint32_t)bf16_from_float(hi[1]) << 16);
-          w[3] = (uint32_t)bf16_from_float(hi[2]) | ((uint32_t)bf16_from_float(hi[3]) << 16);
+          w[0] = bf16x2_from_float(lo[0], lo[1]);
+          w[1] = bf16x2_from_float(lo[2], lo[3]);
+          w[2] = bf16x2_from_float(hi[0], hi[1]);
+          w[3] = bf16x2_from_float(hi[2], hi[3]);
           *(u32x4*)((uint16_t*)p.out + m * p.ld_out + n) = w;
         }
       }

@@ -134,10 +134,17 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 <-> float (round to nearest-even; inputs are finite).
-__device__ __forceinline__ uint16_t bf16_from_float(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// bf16 <-> float (round to nearest-even; inputs are finite).  gfx950
+// converts with v_cvt_pk_bf16_f32, two values per instruction; an in-bounds
+// check over every finite float32 bit pattern (subnormals included) found it
+// equal to round-to-nearest-even by integer arithmetic, (u + 0x7FFF +
+// ((u >> 16) & 1)) >> 16, in all of them.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t bf16_from_float(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values as one word, a in the low half
+__device__ __forceinline__ uint32_t bf16x2_from_float(float a, float b) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
