@@ -24,9 +24,14 @@
 //  * gemm_stream32 - prepared weights, 32*RB rows x (4 waves x NBW x 32)
 //    columns per workgroup, every wave streaming its columns of W over the
 //    whole K with no shared memory: the weight-streaming kernel for few rows
-//    per group (decode) and for the rows a 256-row tile leaves over.
-//  * gemm_big32    - prepared weights, 256 x 256 tiles, A dequantised once per
-//    workgroup into LDS, software-pipelined: many rows per group (prefill).
+//    per group (decode) and for the rows a 256-row tile leaves over when A
+//    comes without its f16 form.
+//  * gemm_big32_dq4 / gemm_dq4_split - prepared weights and A in f16 form,
+//    128 x 256 tiles (the last tile of a group 32, 64 or 128 rows high), A
+//    copied into LDS by DMA, two workgroups per compute unit: many rows per
+//    group (prefill), and one group split over K.
+//  * gemm_big32    - prepared weights, A as codes only, 256 x 256 tiles, A
+//    dequantised once per workgroup into LDS (fallback).
 //  * gemm_stream16 / gemm_tile16 - row-major weights (any K % 32 == 0).
 // A workgroup finds its (group, row range) from the device group offsets, so
 // the launch needs no host-side knowledge of the group sizes; workgroups past
@@ -1103,8 +1108,9 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// gemm_big32: 256 x 256 output tiles for groups with many rows, 4 waves (one
-// per SIMD), each wave all 256 rows x 64 columns = 8 x 2 blocks of 32 x 32
+// gemm_big32: 256 x 256 output tiles for groups with many rows when A comes
+// as codes only (with its f16 form the 128-row tiles below run instead), 4
+// waves (one per SIMD), each wave all 256 rows x 64 columns = 8 x 2 blocks of 32 x 32
 // (256 accumulators, held in the accumulation registers).  A W fragment is
 // dequantised once per wave and feeds 8 MFMAs; on gfx950 a 32x32x16 MFMA
 // hides only two or three vector instructions, so the dequantisation work
@@ -1125,7 +1131,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
 //    vector work: the next substep's W fragments, and in substeps 2..7 the
 //    conversion and store of chunks of the next A half-tile.
 // Workgroups are mapped to tiles by xcd_tile.
-// Workgroup -> (row slot, column tile) for the 256 x 256 kernels.  The
+// Workgroup -> (row slot, column tile) for the tile kernels.  The
 // hardware sends workgroup b to XCD b % 8; XCD x takes slots x, x + 8, ...,
 // each with all its column tiles in turn, so a slot's A rows stay in one
 // XCD's L2 while its neighbours' run on the others, and slots without a tile
