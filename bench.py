@@ -439,13 +439,24 @@ def cpu_baseline(res, n_experts=24):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    flops = 6.0 * wl.T * wl.k * wl.H * wl.I
     return {"value": round(wl.T / est, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "gflops": round(flops / est / 1e9, 2),
             "sample": "oracle in its float32 mode (dequantise to float32, float32 library matmul); "
                       "%d of %d touched experts with all their %d routed rows (L1, SiLU-requant, L2), "
                       "scaled by %d/%d; quantise, route, permute and combine over all %d tokens; "
-                      "timed %.1fs of CPU work; host %d logical CPUs" % (
+                      "timed %.1fs of CPU work; host %d logical CPUs (%s)" % (
                           len(experts), n_t, int(sum(counts)), n_t, len(experts), wl.T, t_tok + t_exp,
-                          os.cpu_count())}
+                          os.cpu_count(), cpu_model)}
 
 
 def time_scrubbed(step, steps, warmup):
