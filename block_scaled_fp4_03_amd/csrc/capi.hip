@@ -242,7 +242,8 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
                                         int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
                                         const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets,
                                         int32_t G, int64_t M, int64_t I, int64_t K, const float* h_gs,
-                                        uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* stream) {
+                                        uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* workspace,
+                                        size_t ws_bytes, void* stream) {
   const char* who = "nvfp4_grouped_gemm_silu_requant";
   if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
   if (M < 0 || I < 32 || I % 32 || K < 256 || K % 256)
@@ -286,6 +287,13 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
   a.h_codes = h_codes;
   a.h_scales = h_scales;
   a.h_dq = h_dq;
+  // split-K as nvfp4_grouped_gemm of the stacked gate_up would (same ranges,
+  // same summation order), then SiLU-requant of the reduced sums
+  const size_t need = nvfp4::gemm_splitk_bytes(G, M, 2 * I, K, true);
+  if (need && workspace && ws_bytes >= need && aligned(workspace, 16)) {
+    a.splits = nvfp4::gemm_splitk_splits(G, M, 2 * I, K, true);
+    a.ws = (float*)workspace;
+  }
   hipStream_t s = (hipStream_t)stream;
   return finish(who, nvfp4::launch_grouped_gemm(a, s), s);
 }

@@ -1107,6 +1107,77 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   store_out(p, m, n, alpha_for(p, lo, n, *p.a_gs) * sum);
 }
 
+// Split K with SiLU-requant (the first GEMM of the expert MLP): four lanes
+// (a DPP quad) per 16-element block of h, each with 4 gate and the matching
+// 4 up columns of row m, so that a wave's loads cover 1 KB of contiguous
+// partial sums.  Each value is the sum of the raw partial sums in split
+// order times alpha, exactly as splitk_reduce stores it; then SiLU(gate) *
+// up, the block amax (a max over the quad: order-free), the E4M3 scale and
+// the E2M1 codes follow silu_mul_requant's float32 steps, so codes, scales
+// and the f16 copy are those of the unfused calls.
+__global__ __launch_bounds__(256) void splitk_reduce_silu_requant(GemmArgs p) {
+  const int64_t I = p.N / 2, bpr = I / 16;
+  const int64_t nq = p.M * bpr * 4;   // a multiple of 4: a quad shares every trip
+  const float a_gs = *p.a_gs;
+  const float gs = *p.h_gs;
+  const int64_t plane = p.M * p.N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nq; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = t / (bpr * 4);
+    const int64_t rem = t - m * bpr * 4;
+    const int64_t cb = rem >> 2;
+    const int qd = (int)(rem & 3);
+    // the group holding row m (as splitk_reduce finds it); the quad agrees
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      const int64_t om = clampv<int64_t>(p.group_offsets[mid], 0, p.M);
+      if (om <= m) lo = mid;
+      else hi = mid;
+    }
+    const int64_t g0 = clampv<int64_t>(p.group_offsets[lo], 0, p.M);
+    const int64_t g1 = clampv<int64_t>(p.group_offsets[lo + 1], 0, p.M);
+    if (m < g0 || m >= g1) continue;
+    const int64_t n = 16 * cb + 4 * qd;
+    const float* wg = p.ws + m * p.N + n;
+    floatx4_t sg = *(const floatx4_t*)wg, su = *(const floatx4_t*)(wg + I);
+#pragma unroll 4
+    for (int sp = 1; sp < p.splits; ++sp) {
+      const floatx4_t tg = *(const floatx4_t*)(wg + sp * plane), tu = *(const floatx4_t*)(wg + sp * plane + I);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sg[e] += tg[e];
+        su[e] += tu[e];
+      }
+    }
+    const float alpha_g = alpha_for(p, lo, n, a_gs);
+    const float alpha_u = alpha_for(p, lo, I + n, a_gs);
+    float h[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = silu_mul(alpha_g * sg[e], alpha_u * su[e]);
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(h[e]));
+    }
+    amax = __builtin_fmaxf(amax, dpp_f32<0xB1>(amax));   // quad_perm [1,0,3,2]
+    amax = __builtin_fmaxf(amax, dpp_f32<0x4E>(amax));   // quad_perm [2,3,0,1]
+    float r;
+    bool zero;
+    const uint32_t sq = block_scale(amax, gs, r, zero);
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= e2m1_code(h[e], r, zero) << (4 * e);
+    *(uint16_t*)(p.h_codes + m * (I / 2) + cb * 8 + 2 * qd) = (uint16_t)bits;
+    if (qd == 0) p.h_scales[m * bpr + cb] = (uint8_t)sq;
+    if (p.h_dq) {
+      const half2_t sf2 = scale_pair(sq);
+      uint2 v;
+      v.x = __builtin_bit_cast(uint32_t, dequant_pair(bits, 0, sf2));
+      v.y = __builtin_bit_cast(uint32_t, dequant_pair(bits, 1, sf2));
+      *(uint2*)(p.h_dq + m * I + n) = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gemm_big32: 256 x 256 output tiles for groups with many rows when A comes
 // as codes only (with its f16 form the 128-row tiles below run instead), 4
@@ -1743,21 +1814,46 @@ bool gemm_uses_big_tiles(int64_t G, int64_t M, int64_t K, bool tiled) {
   return tiled && M >= BIG && M >= (K > 4096 ? 32 : 16) * G;
 }
 
+// The raw partial sums of a split-K GEMM into a.ws (splits x [M, N] float32,
+// split-major): one group with A in f16 form on the 128-row tiles, else the
+// weight-streaming kernels (short ranges where 16 of them cover K).
+hipError_t launch_split_partials(const GemmArgs& a, hipStream_t s) {
+  if (a.a_dq && a.G == 1) {
+    const int64_t n_tiles = (a.N + BIG - 1) / BIG;
+    const int64_t n_slots = (a.M + BIG4 - 1) / BIG4;
+    hipLaunchKernelGGL(gemm_dq4_split, dim3((unsigned)(n_slots * n_tiles * a.splits)), dim3(kBigThreads), 0, s, a,
+                       n_slots, n_tiles);
+    return hipGetLastError();
+  }
+  constexpr int NBW = 2;
+  const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
+  const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
+  const int64_t nks = a.K / 256;
+  if ((nks + a.splits - 1) / a.splits <= 2)
+    hipLaunchKernelGGL((gemm_splitk_short<NBW, 1>), dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a, n_tiles);
+  else
+    hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, true>), dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a,
+                       n_tiles, 0, 0, work);
+  return hipGetLastError();
+}
+
 template <bool FUSE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
-  if constexpr (!FUSE) {
-    if (a.a_dq && a.splits > 1 && a.ws && a.G == 1) {
-      // one group with few tiles for the chip (gemm_splitk_splits): the
-      // 128-row tiles split over K, then the partial sums reduced in order
-      const int64_t n_tiles = (a.N + BIG - 1) / BIG;
-      const int64_t n_slots = (a.M + BIG4 - 1) / BIG4;
-      hipLaunchKernelGGL(gemm_dq4_split, dim3((unsigned)(n_slots * n_tiles * a.splits)), dim3(kBigThreads), 0, s,
-                         a, n_slots, n_tiles);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+  if (a.splits > 1 && a.ws && (a.G == 1 && a.a_dq || !gemm_uses_big_tiles(a.G, a.M, a.K, true))) {
+    // few workgroups for the chip (gemm_splitk_splits): K split, then the
+    // partial sums reduced in split order, to the output or (fused) through
+    // SiLU-requant
+    hipError_t e = launch_split_partials(a, s);
+    if (e != hipSuccess) return e;
+    if constexpr (FUSE) {
+      // 64-lane workgroups: a few per compute unit even for a 128-row call
+      const int64_t nq = a.M * (a.N / 2 / 16) * 4;
+      const int64_t grid = std::min<int64_t>((nq + 63) / 64, 1 << 20);
+      hipLaunchKernelGGL(splitk_reduce_silu_requant, dim3((unsigned)grid), dim3(64), 0, s, a);
+    } else {
       hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
-      return hipGetLastError();
     }
+    return hipGetLastError();
   }
   // a workgroup covers 256 weight rows: 256 output columns, or (fused) 128
   // columns of h from 128 gate and 128 up rows
@@ -1796,22 +1892,6 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   constexpr int NBW = 2;
   const int64_t n_tiles = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
   const int64_t work = ((a.M + 31) / 32 + a.G) * n_tiles;
-  if constexpr (!FUSE) {
-    if (a.splits > 1 && a.ws) {
-      // few workgroups for the chip: split K, then reduce in split order
-      const int64_t nks = a.K / 256;
-      if ((nks + a.splits - 1) / a.splits <= 2)
-        hipLaunchKernelGGL((gemm_splitk_short<NBW, 1>), dim3((unsigned)(work * a.splits)), dim3(256), 0, s, a,
-                           n_tiles);
-      else
-        hipLaunchKernelGGL((gemm_stream32<NBW, 1, false, true>), dim3((unsigned)(work * a.splits)),
-                           dim3(256), 0, s, a, n_tiles, 0, 0, work);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-  }
   hipLaunchKernelGGL((gemm_stream32<NBW, 1, FUSE>), dim3((unsigned)work), dim3(256), 0, s, a, n_tiles, 0, 0, work);
   return hipGetLastError();
 }

@@ -185,12 +185,13 @@ def grouped_gemm(a_codes, a_scales, a_gs, w_codes, w_scales, w_gs, n_seg, group_
 
 
 def grouped_gemm_silu_requant(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, M, I, K, gs_h,
-                              a_row_index=None, a_dq=None, dq=None, codes=None, scales=None):
+                              a_row_index=None, a_dq=None, dq=None, codes=None, scales=None, workspace=None):
     """First GEMM of the expert MLP with SiLU(gate)*up re-quantised in its
     epilogue: the same codes and scales (and f16 copy with dq) as
     silu_mul_requant over grouped_gemm's float32 [M, 2I] output, without
     that output.  w_tiled: prepare_weights buffer of the stacked [G, 2I, K]
-    weights; w_gs [G, 2]."""
+    weights; w_gs [G, 2].  workspace as for grouped_gemm (None allocates the
+    split-K workspace the library asks for, False runs without one)."""
     _check_dev(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, gs_h, a_row_index, a_dq,
                None if dq is True else dq)
     G = w_gs.shape[0]
@@ -201,9 +202,14 @@ def grouped_gemm_silu_requant(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offs
         scales = torch.empty(M, I // 16, dtype=torch.uint8, device=dev)
     want_dq = dq is not None
     dq = _dq_out(dq, M, I, dev)
+    ws_bytes = _lib.load().nvfp4_grouped_gemm_workspace_size(G, M, 2 * I, K, _lib.LAYOUT_TILED) \
+        if (workspace is None and M > 0) else (0 if workspace is None or workspace is False else workspace.numel())
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsp = workspace if workspace is not None and workspace is not False else None
     _lib.call("nvfp4_grouped_gemm_silu_requant", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
               _p(a_row_index), _p(a_dq), _p(w_tiled), _p(w_gs), _p(group_offsets), G, M, I, K, _p(gs_h),
-              _p(codes), _p(scales), _p(dq), _stream())
+              _p(codes), _p(scales), _p(dq), _p(wsp), ws_bytes if wsp is not None else 0, _stream())
     return (codes, scales, dq) if want_dq else (codes, scales)
 
 

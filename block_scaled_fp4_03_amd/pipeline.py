@@ -78,11 +78,9 @@ class NVFP4Weights:
     def fuse_by_default(self, M, a_rows):
         """Whether a first GEMM of M rows runs SiLU-requant in its epilogue by
         default: wherever the fused launch applies (it measures faster on the
-        weight-streaming and the matrix-core kernels and keeps no float32
-        gate_up), not where the GEMM splits K (the fused epilogue needs whole
-        sums)."""
-        G, N, K2 = self.codes.shape
-        return self.can_fuse_silu() and ops.gemm_workspace_size(G, M, N, 2 * K2, True) == 0
+        weight-streaming and the matrix-core kernels, and where K is split the
+        reduction re-quantises directly; no float32 gate_up either way)."""
+        return self.can_fuse_silu()
 
     def gemm_silu_requant(self, a_codes, a_scales, a_gs, group_offsets, M, gs_h, **kw):
         G, N, K2 = self.codes.shape
@@ -150,7 +148,7 @@ def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xd
     """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` (static
     gs_h and a fusable W1) the re-quantisation runs in the L1 epilogue, with
     identical results and no float32 gate_up in memory; None picks
-    w1.fuse_by_default (fused unless L1 splits K).  gs_h None computes it from
+    w1.fuse_by_default (fused wherever W1 allows it).  gs_h None computes it from
     this batch's gate_up.  With `persistent`, both GEMMs and the fused
     SiLU-requant run as one persistent launch (nvfp4_moe_expert_mlp; static
     gs_h): h is identical, y identical in the streaming regime.  Returns (y

@@ -313,6 +313,15 @@ size_t nvfp4_grouped_gemm_workspace_size(int32_t G, int64_t M, int64_t N, int64_
  *   h_codes, h_scales  out [M, I/2], [M, I/16]; h_dq out [M, I] f16 or NULL
  *                      (as silu_mul_requant writes them).  Rows outside every
  *                      group are left untouched.
+ *   workspace          device memory of ws_bytes (16-byte aligned) or NULL,
+ *                      sized by nvfp4_grouped_gemm_workspace_size(G, M, 2I,
+ *                      K, NVFP4_LAYOUT_TILED).  With it K is split exactly as
+ *                      in nvfp4_grouped_gemm given the same workspace, and a
+ *                      second kernel adds the partial sums in range order,
+ *                      applies alpha and re-quantises SiLU(gate) * up, so the
+ *                      equivalence above holds with that workspace passed to
+ *                      both.  Caller-owned; calls that share one workspace
+ *                      must not overlap.
  * Errors: EINVAL for null pointers; ESHAPE unless 1 <= G <=
  * NVFP4_MAX_EXPERTS, M >= 0, I >= 32 with I % 32 == 0, K >= 256 with
  * K % 256 == 0, a_rows as for nvfp4_grouped_gemm; EALIGN unless codes,
@@ -324,7 +333,7 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
                                         const uint8_t* w_tiled, const float* w_gs,
                                         const int32_t* group_offsets, int32_t G, int64_t M, int64_t I,
                                         int64_t K, const float* h_gs, uint8_t* h_codes, uint8_t* h_scales,
-                                        uint16_t* h_dq, void* stream);
+                                        uint16_t* h_dq, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * nvfp4_moe_expert_mlp - the routed experts' MLP in ONE persistent launch:

@@ -123,7 +123,8 @@ def test_fused_gemm_silu_validation(L):
                  w_gs=FAKE, off=FAKE, G=1, M=8, I=64, K=256, h_gs=FAKE, hc=FAKE, hs=FAKE, hdq=NULL)
         a.update(kw)
         return f(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"], a["a_dq"], a["w"],
-                 a["w_gs"], a["off"], a["G"], a["M"], a["I"], a["K"], a["h_gs"], a["hc"], a["hs"], a["hdq"], NULL)
+                 a["w_gs"], a["off"], a["G"], a["M"], a["I"], a["K"], a["h_gs"], a["hc"], a["hs"], a["hdq"], NULL,
+                 0, NULL)
     assert call(I=48) == lib.ESHAPE            # I % 32
     assert call(K=384) == lib.ESHAPE           # K % 256
     assert call(G=0) == lib.ESHAPE
@@ -217,7 +218,7 @@ def test_fused_silu_default_choice(L):
 
     assert w1(384).fuse_by_default(1536, 256)                 # decode: 384 experts, 6 x 256 rows
     assert w1(384).fuse_by_default(49152, 8192)               # prefill: 128-row matrix-core tiles
-    assert not w1(1).fuse_by_default(128, 128)                # shared expert: K split
+    assert w1(1).fuse_by_default(128, 128)                    # shared expert: split K, fused reduction
     assert not w1(384, tiled=False).fuse_by_default(1536, 256)  # row-major weights: no fused kernel
     assert not w1(8, I=48).fuse_by_default(64, 32)            # I % 32 != 0
 

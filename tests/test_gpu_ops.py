@@ -531,11 +531,12 @@ def test_gemm_deterministic():
 
 # --- fused first GEMM + SiLU-requant ----------------------------------------------
 
-def _fused_case(counts, I, K, seed, gather=True, use_dq=False):
+def _fused_case(counts, I, K, seed, gather=True, use_dq=False, split=None):
     """nvfp4_grouped_gemm_silu_requant against the unfused pair (grouped
     GEMM to float32, then silu_mul_requant): codes, scales and the f16 copy
-    must be identical."""
-    log("fused gemm+silu", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq)
+    must be identical.  Both GEMMs get the split-K workspace the library
+    asks for, or none with split=False; split=True asserts that K is split."""
+    log("fused gemm+silu", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq, split)
     rng = np.random.default_rng(seed)
     G, M = len(counts), int(sum(counts))
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -557,17 +558,23 @@ def _fused_case(counts, I, K, seed, gather=True, use_dq=False):
     a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16)) if use_dq else None
     ri = T(row_index) if gather else None
     args = (T(ac), T(as_), torch.tensor([ags], device=d))
+    if split is True:
+        assert ops.gemm_workspace_size(G, M, N, K, True) > 0
+    wsp = False if split is False else None
     gu = ops.grouped_gemm(*args, T(wc), T(ws), T(wgs), [0, I, N], T(off), M, a_row_index=ri, w_tiled=tiled,
-                          a_dq=a_dq)
+                          a_dq=a_dq, workspace=wsp)
     gs_h = ops.silu_mul_global_scale(gu)
     hc, hs, hdq = ops.silu_mul_requant(gu, gs_h, dq=True)
+    # sentinels: rows outside every group stay untouched
+    fc = torch.full((M, I // 2), 0xA5, dtype=torch.uint8, device=d)
+    fs = torch.full((M, I // 16), 0x5A, dtype=torch.uint8, device=d)
     fc, fs, fdq = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
-                                                a_dq=a_dq, dq=True)
+                                                a_dq=a_dq, dq=True, codes=fc, scales=fs, workspace=wsp)
     assert np.array_equal(to_np(fc), to_np(hc)), "codes"
     assert np.array_equal(to_np(fs), to_np(hs)), "scales"
     assert np.array_equal(to_np(fdq).view(np.uint16), to_np(hdq).view(np.uint16)), "f16 copy"
     fc2, fs2 = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
-                                             a_dq=a_dq)
+                                             a_dq=a_dq, workspace=wsp)
     assert np.array_equal(to_np(fc2), to_np(hc)) and np.array_equal(to_np(fs2), to_np(hs))
 
 
@@ -595,8 +602,24 @@ def test_fused_silu_requant_32_to_128_row_groups():
 
 
 def test_fused_silu_requant_one_group_no_gather():
-    _fused_case([300], 96, 768, 24, gather=False, use_dq=True)
+    _fused_case([300], 96, 768, 24, gather=False, use_dq=True, split=True)
+    _fused_case([300], 96, 768, 24, gather=False, use_dq=True, split=False)
     _fused_case([17], 128, 256, 25, gather=False)
+
+
+def test_fused_silu_requant_split_k():
+    # few workgroups for the chip: K is split into ranges and the fused
+    # reduction re-quantises the sums.  One group of 128 and 100 rows (the
+    # shared expert's form) over short ranges (2 k-steps), 3-step ranges on
+    # the streaming kernel, and 128-row matrix-core tiles with A's f16 form
+    _fused_case([128], 128, 4096, 30, gather=False, split=True)
+    _fused_case([100], 128, 9216, 31, gather=False, split=True)
+    _fused_case([128], 256, 2048, 32, gather=False, use_dq=True, split=True)
+    _fused_case([100], 64, 2048, 33, gather=False, use_dq=True, split=True)
+    # several groups (an empty one, a ragged last row block) with gathered A
+    _fused_case([5, 0, 40, 19], 96, 4096, 34, split=True)
+    _fused_case([5, 0, 40, 19], 96, 4096, 35, use_dq=True, split=True)
+    _fused_case([5, 0, 40, 19], 96, 4096, 35, use_dq=True, split=False)
 
 
 # --- SiLU-requant and combine ---------------------------------------------------
