@@ -1107,6 +1107,56 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   store_out(p, m, n, alpha_for(p, lo, n, *p.a_gs) * sum);
 }
 
+// splitk_reduce for N % 4 == 0, four columns per lane (16-byte loads of the
+// partial sums, a wave covering 1 KB of a row per load): the same sums in
+// the same order and the same alpha per column.  Block (x, y): row y,
+// columns 1024 x .. 1024 x + 1023.  vec: out takes whole 4-column stores
+// (16-byte aligned rows for float32, 8-byte for bf16).
+__global__ __launch_bounds__(256) void splitk_reduce4(GemmArgs p, bool vec) {
+  const int64_t m = blockIdx.y;
+  const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= p.N) return;
+  int lo = 0, hi = p.G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    const int64_t om = clampv<int64_t>(p.group_offsets[mid], 0, p.M);
+    if (om <= m) lo = mid;
+    else hi = mid;
+  }
+  const int64_t g0 = clampv<int64_t>(p.group_offsets[lo], 0, p.M);
+  const int64_t g1 = clampv<int64_t>(p.group_offsets[lo + 1], 0, p.M);
+  if (m < g0 || m >= g1) return;
+  const int64_t plane = p.M * p.N;
+  const float* w = p.ws + m * p.N + n;
+  floatx4_t sum = *(const floatx4_t*)w;
+#pragma unroll 4
+  for (int sp = 1; sp < p.splits; ++sp) {
+    const floatx4_t t = *(const floatx4_t*)(w + sp * plane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] += t[e];
+  }
+  const float a_gs = *p.a_gs;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = alpha_for(p, lo, n + e, a_gs) * sum[e];
+  if (vec) {
+    if (p.out_bf16) {
+      uint2 o;
+      o.x = bf16x2_from_float(v[0], v[1]);
+      o.y = bf16x2_from_float(v[2], v[3]);
+      *(uint2*)((uint16_t*)p.out + m * p.ld_out + n) = o;
+    } else {
+      floatx4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = v[e];
+      *(floatx4_t*)((float*)p.out + m * p.ld_out + n) = o;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(p, m, n + e, v[e]);
+  }
+}
+
 // Split K with SiLU-requant (the first GEMM of the expert MLP): four lanes
 // (a DPP quad) per 16-element block of h, each with 4 gate and the matching
 // 4 up columns of row m, so that a wave's loads cover 1 KB of contiguous
@@ -1850,6 +1900,10 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
       const int64_t nq = a.M * (a.N / 2 / 16) * 4;
       const int64_t grid = std::min<int64_t>((nq + 63) / 64, 1 << 20);
       hipLaunchKernelGGL(splitk_reduce_silu_requant, dim3((unsigned)grid), dim3(64), 0, s, a);
+    } else if (a.N % 4 == 0) {
+      const bool vec = a.ld_out % 4 == 0 && ((uintptr_t)a.out & (a.out_bf16 ? 7 : 15)) == 0;
+      hipLaunchKernelGGL(splitk_reduce4, dim3((unsigned)((a.N + 1023) / 1024), (unsigned)a.M), dim3(256), 0, s, a,
+                         vec);
     } else {
       hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((a.N + 255) / 256), (unsigned)a.M), dim3(256), 0, s, a);
     }

@@ -345,6 +345,10 @@ def test_gemm_split_k_one_small_group():
     # workspace too, and for determinism
     _gemm_case([100], 320, 2048, [0, 160, 320], 15, gather=False)
     _gemm_case([61, 40], 256, 2048, [0, 256], 16, gather=True, out_bf16=True)
+    # the reduction's four-column lanes: a segment boundary inside one
+    # lane's columns; N % 4 != 0 (one column per lane)
+    _gemm_case([100], 320, 2048, [0, 162, 320], 36, gather=False)
+    _gemm_case([70], 322, 2048, [0, 322], 37, gather=False, out_bf16=True)
     d = dev()
     rng = np.random.default_rng(17)
     ac, as_, ags = oracle_nvfp4(_x(100, 2048, 17))
@@ -360,6 +364,13 @@ def test_gemm_split_k_one_small_group():
     a2 = to_np(ops.grouped_gemm(*args, w_tiled=tiled))
     a3 = to_np(ops.grouped_gemm(*args, w_tiled=tiled, workspace=False))
     assert np.array_equal(a1, a2)                       # deterministic
+    for dt in (torch.float32, torch.bfloat16):
+        # rows of 322 elements: the reduction stores column by column, with
+        # the same values as into whole rows
+        wide = torch.full((100, 322), 7.0, dtype=dt, device=d)
+        ops.grouped_gemm(*args, w_tiled=tiled, out=wide[:, :320])
+        whole = ops.grouped_gemm(*args, w_tiled=tiled, out_dtype=dt)
+        assert torch.equal(wide[:, :320], whole) and bool((wide[:, 320:] == 7.0).all())
     ex, ab = exact_gemm_rows(ac, as_, wc, ws)
     for o in (a1, a3):
         check_gemm(o, ex, ab, float(F32(F32(ags) * wg)), 2048, False, "split-K")
