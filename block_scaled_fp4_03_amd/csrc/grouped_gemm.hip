@@ -659,14 +659,20 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     a_c[rb] = p.a_codes + a_row * KB + 32 * kh;
     a_s[rb] = p.a_scales + a_row * KS + 4 * kh;
   }
+  // W through one buffer resource per column block: the lane's offset in a
+  // VGPR set once, the half-step's offset in an SGPR (no 64-bit address
+  // arithmetic per load); the non-temporal bit in the cache-policy field
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
-  const uint8_t* w_t[NBW];
+  __amdgpu_buffer_rsrc_t w_rsrc[NBW];
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     int64_t nb = FUSE ? j + cb * (p.N / 64) : n0 / 32 + cb;
     nb = nb < nb_per_g ? nb : nb_per_g - 1;
-    w_t[cb] = p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes;
+    w_rsrc[cb] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes),
+                                                   (short)0, (int)(nks * kTileBytes), 0x00020000);
   }
+  constexpr int kPol = NT ? 2 : 0;
+  const int w_lo = 16 * lane, w_hi = 16 * lane + 1024, w_sc = 4 * lane + 4096;
 
   floatx16_t acc[RB][NBW];
 #pragma unroll
@@ -681,36 +687,32 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   };
   auto load_a = [&](int64_t hs, Ops& d) {
     const int64_t ks = hs >> 1, h = hs & 1;
+    // lanes past the tile's last row load nothing and keep whatever their
+    // registers held: every row of the product depends only on its own A
+    // row, and rows >= row1 are never stored.  (Zeroing them made the
+    // compiler wait for every load in flight, the next half-steps' weights
+    // included, wherever a row block was partial; loading a valid row on
+    // every lane instead costs the address unit 64 lanes per load.)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (a_valid[rb]) {
         d.a0[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h);
         d.a1[rb] = *(const u32x4*)(a_c[rb] + ks * 128 + 64 * h + 16);
         d.as[rb] = *(const uint32_t*)(a_s[rb] + ks * 16 + 8 * h);
-      } else {
-        d.a0[rb] = u32x4{0u, 0u, 0u, 0u};
-        d.a1[rb] = d.a0[rb];
-        d.as[rb] = 0u;
       }
     }
   };
   auto load_w = [&](int64_t hs, Ops& d) {
-    const int64_t ks = hs >> 1, h = hs & 1;
+    const int ks = (int)(hs >> 1), h = (int)(hs & 1);
+    // (uniform by construction; said so, or the compiler keeps them in
+    // vector registers and loops over the lanes' distinct values)
+    const int so = __builtin_amdgcn_readfirstlane(ks * kTileBytes + 2048 * h);
+    const int ss = __builtin_amdgcn_readfirstlane(ks * kTileBytes + 256 * h);
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
-      const uint8_t* t = w_t[cb] + ks * kTileBytes;
-      const u32x4* t0 = (const u32x4*)(t + 2048 * h + 16 * lane);
-      const u32x4* t1 = (const u32x4*)(t + 2048 * h + 1024 + 16 * lane);
-      const uint32_t* ts = (const uint32_t*)(t + 4096 + 256 * h + 4 * lane);
-      if constexpr (NT) {
-        d.w0[cb] = __builtin_nontemporal_load(t0);
-        d.w1[cb] = __builtin_nontemporal_load(t1);
-        d.ws[cb] = __builtin_nontemporal_load(ts);
-      } else {
-        d.w0[cb] = *t0;
-        d.w1[cb] = *t1;
-        d.ws[cb] = *ts;
-      }
+      d.w0[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_lo, so, kPol);
+      d.w1[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_hi, so, kPol);
+      d.ws[cb] = __builtin_amdgcn_raw_buffer_load_b32(w_rsrc[cb], w_sc, ss, kPol);
     }
   };
   auto load = [&](int64_t hs, Ops& d) {
@@ -718,15 +720,32 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     load_w(hs, d);
   };
   auto compute = [&](const Ops& o) {
+    // the four E4M3 scale bytes of each word, two per conversion (exact:
+    // every E4M3 value is an f16 value)
+    half2_t wsc[NBW][2], asc[RB][2];
+#pragma unroll
+    for (int cb = 0; cb < NBW; ++cb) {
+      wsc[cb][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.ws[cb], 1.0f, false);
+      wsc[cb][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.ws[cb], 1.0f, true);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      asc[rb][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.as[rb], 1.0f, false);
+      asc[rb][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.as[rb], 1.0f, true);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const int q = j >> 1;    // the block of the substep's 8 codes
       half8_t bf[NBW];
 #pragma unroll
-      for (int cb = 0; cb < NBW; ++cb)
-        bf[cb] = dequant8(j < 4 ? o.w0[cb][j] : o.w1[cb][j - 4], scale_pair(byte_of(o.ws[cb], j >> 1)));
+      for (int cb = 0; cb < NBW; ++cb) {
+        const _Float16 sv = wsc[cb][q >> 1][q & 1];
+        bf[cb] = dequant8(j < 4 ? o.w0[cb][j] : o.w1[cb][j - 4], half2_t{sv, sv});
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const half8_t af = dequant8(j < 4 ? o.a0[rb][j] : o.a1[rb][j - 4], scale_pair(byte_of(o.as[rb], j >> 1)));
+        const _Float16 sv = asc[rb][q >> 1][q & 1];
+        const half8_t af = dequant8(j < 4 ? o.a0[rb][j] : o.a1[rb][j - 4], half2_t{sv, sv});
 #pragma unroll
         for (int cb = 0; cb < NBW; ++cb) acc[rb][cb] = mfma32(af, bf[cb], acc[rb][cb]);
       }
@@ -750,6 +769,9 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   // (the last two half-steps reload the last one: no branch around a load)
   auto step = [&](int64_t hs, const Ops& cur, Ops& ld) {
     load(hs + 2 < nhs ? hs + 2 : nhs - 1, ld);
+    // the loads go out before the half-step's conversions and MFMAs (the
+    // scheduler would otherwise sink them towards their use)
+    __builtin_amdgcn_sched_barrier(0);
     compute(cur);
   };
   int64_t hs = h0;
