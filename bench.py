@@ -265,7 +265,7 @@ def measure_ceilings(steps=10):
     t_mfma = timed(lambda: ops.probe_mfma_f16(iters, wgs, sink))
     torch.cuda.empty_cache()
     return {"hbm_read_gbs": round((1 << 32) / t_read / 1e9, 1),
-            "hbm_read_probe": "4 GiB read once, 16-byte non-temporal loads, 8 in flight per lane, 2048 workgroups",
+            "hbm_read_probe": "4 GiB read once, each of 8192 waves one contiguous 512 KiB chunk, 16 non-temporal 1 KiB wave-loads in flight",
             "f16_mfma_tflops": round(flops / t_mfma / 1e12, 1),
             "f16_mfma_probe": "v_mfma_f32_32x32x16_f16, 8 independent chains per wave, 4 waves per "
                               "workgroup, 512 workgroups, operands alternating between two random sets"}
