@@ -687,9 +687,10 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   };
   auto load_a = [&](int64_t hs, Ops& d) {
     const int64_t ks = hs >> 1, h = hs & 1;
-    // lanes past the tile's last row load nothing and keep whatever their
-    // registers held: every row of the product depends only on its own A
-    // row, and rows >= row1 are never stored.  (Zeroing them made the
+    // lanes past the tile's last row load nothing and keep an earlier
+    // half-step's values (or the zeros the sets start with): every row of
+    // the product depends only on its own A row, and rows >= row1 are never
+    // stored.  (Zeroing them made the
     // compiler wait for every load in flight, the next half-steps' weights
     // included, wherever a row block was partial; loading a valid row on
     // every lane instead costs the address unit 64 lanes per load.)
@@ -755,7 +756,9 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   // loads in flight; the three operand sets rotate (no copy of registers
   // with loads pending)
   const int64_t h0 = 2 * ks0, nhs = 2 * ks1;
-  Ops s0, s1, s2;
+  // zeroed once, so that lanes past the last row (which never load A) hold
+  // defined values
+  Ops s0{}, s1{}, s2{};
   if (sy.wait_ctr) {
     load_w(h0, s0);
     load_w(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
