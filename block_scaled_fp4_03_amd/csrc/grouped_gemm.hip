@@ -33,6 +33,9 @@
 //  * gemm_big32    - prepared weights, A as codes only, 256 x 256 tiles, A
 //    dequantised once per workgroup into LDS (fallback).
 //  * gemm_stream16 / gemm_tile16 - row-major weights (any K % 32 == 0).
+//  * splitk_reduce4 / splitk_reduce / splitk_reduce_silu_requant - the
+//    split-K partial sums added in range order, times alpha, to the output
+//    or (the first GEMM of the expert MLP) through SiLU-requant.
 // A workgroup finds its (group, row range) from the device group offsets, so
 // the launch needs no host-side knowledge of the group sizes; workgroups past
 // the last tile exit at once.
@@ -581,10 +584,10 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
 
 // gemm_stream32: 32*RB rows x (4 waves x NBW x 32) columns per workgroup; each
 // wave streams its NBW 32-column blocks of W over the whole K with two
-// half-steps of loads in flight (three register sets; at 148 VGPRs three
-// workgroups fit a compute unit, which keeps more bytes in flight per compute
-// unit than four workgroups with one half-step each), with no shared memory
-// and no barriers.  With skip_bm > 0
+// half-steps of loads in flight (three register sets; at about 145
+// registers three workgroups fit a compute unit, which keeps more bytes in
+// flight per compute unit than four workgroups with one half-step each),
+// with no shared memory and no barriers.  With skip_bm > 0
 // it takes only the rows a skip_bm-row tile launch leaves over at the end of
 // each group.
 // NT: the tile holds every row of its group, so each weight byte it streams
@@ -1951,8 +1954,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     if constexpr (!FUSE) {
       // A as codes only: full 256-row tiles (gemm_big32), the rows each
       // group leaves over on the streaming kernel, persistent: three
-      // workgroups per compute unit (164 VGPRs with two half-steps of loads
-      // in flight)
+      // workgroups per compute unit (about 150 registers with two half-steps
+      // of loads in flight)
       constexpr int NBW = 2, RB = 1;
       const int64_t n_tiles_s = (a.N + 4 * NBW * 32 - 1) / (4 * NBW * 32);
       // a group leaves fewer than 256 rows over: at most 8 32-row tiles per
