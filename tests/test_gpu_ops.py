@@ -542,14 +542,18 @@ def test_gemm_deterministic():
 
 # --- fused first GEMM + SiLU-requant ----------------------------------------------
 
-def _fused_case(counts, I, K, seed, gather=True, use_dq=False, split=None):
+def _fused_case(counts, I, K, seed, gather=True, use_dq=False, split=None, extra_rows=0):
     """nvfp4_grouped_gemm_silu_requant against the unfused pair (grouped
     GEMM to float32, then silu_mul_requant): codes, scales and the f16 copy
     must be identical.  Both GEMMs get the split-K workspace the library
-    asks for, or none with split=False; split=True asserts that K is split."""
-    log("fused gemm+silu", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq, split)
+    asks for, or none with split=False; split=True asserts that K is split.
+    extra_rows: M exceeds the last group offset by that many rows, which
+    every call must leave untouched."""
+    log("fused gemm+silu", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq, split,
+        extra_rows)
     rng = np.random.default_rng(seed)
-    G, M = len(counts), int(sum(counts))
+    G, M = len(counts), int(sum(counts)) + extra_rows
+    Mg = int(sum(counts))
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     a_rows = M + 5 if gather else M
     ac, as_, ags = oracle_nvfp4(_x(a_rows, K, seed, outliers=True))
@@ -574,19 +578,22 @@ def _fused_case(counts, I, K, seed, gather=True, use_dq=False, split=None):
     wsp = False if split is False else None
     gu = ops.grouped_gemm(*args, T(wc), T(ws), T(wgs), [0, I, N], T(off), M, a_row_index=ri, w_tiled=tiled,
                           a_dq=a_dq, workspace=wsp)
-    gs_h = ops.silu_mul_global_scale(gu)
-    hc, hs, hdq = ops.silu_mul_requant(gu, gs_h, dq=True)
+    gs_h = ops.silu_mul_global_scale(gu[:Mg])
+    hc, hs, hdq = ops.silu_mul_requant(gu[:Mg].contiguous(), gs_h, dq=True)
     # sentinels: rows outside every group stay untouched
     fc = torch.full((M, I // 2), 0xA5, dtype=torch.uint8, device=d)
     fs = torch.full((M, I // 16), 0x5A, dtype=torch.uint8, device=d)
+    fq = torch.full((M, I), 0x3C00, dtype=torch.int16, device=d).view(torch.float16)
     fc, fs, fdq = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
-                                                a_dq=a_dq, dq=True, codes=fc, scales=fs, workspace=wsp)
-    assert np.array_equal(to_np(fc), to_np(hc)), "codes"
-    assert np.array_equal(to_np(fs), to_np(hs)), "scales"
-    assert np.array_equal(to_np(fdq).view(np.uint16), to_np(hdq).view(np.uint16)), "f16 copy"
+                                                a_dq=a_dq, dq=fq, codes=fc, scales=fs, workspace=wsp)
+    assert np.array_equal(to_np(fc)[:Mg], to_np(hc)), "codes"
+    assert np.array_equal(to_np(fs)[:Mg], to_np(hs)), "scales"
+    assert np.array_equal(to_np(fdq).view(np.uint16)[:Mg], to_np(hdq).view(np.uint16)), "f16 copy"
+    assert (to_np(fc)[Mg:] == 0xA5).all() and (to_np(fs)[Mg:] == 0x5A).all(), "rows outside every group"
+    assert (to_np(fdq).view(np.uint16)[Mg:] == 0x3C00).all(), "f16 copy of rows outside every group"
     fc2, fs2 = ops.grouped_gemm_silu_requant(*args, tiled, T(wgs), T(off), M, I, K, gs_h, a_row_index=ri,
                                              a_dq=a_dq, workspace=wsp)
-    assert np.array_equal(to_np(fc2), to_np(hc)) and np.array_equal(to_np(fs2), to_np(hs))
+    assert np.array_equal(to_np(fc2)[:Mg], to_np(hc)) and np.array_equal(to_np(fs2)[:Mg], to_np(hs))
 
 
 def test_fused_silu_requant_decode_shaped():
@@ -627,6 +634,10 @@ def test_fused_silu_requant_split_k():
     _fused_case([100], 128, 9216, 31, gather=False, split=True)
     _fused_case([128], 256, 2048, 32, gather=False, use_dq=True, split=True)
     _fused_case([100], 64, 2048, 33, gather=False, use_dq=True, split=True)
+    # rows past the last group offset (left untouched by the partial GEMM,
+    # the reduction and the f16 copy)
+    _fused_case([100], 128, 4096, 36, gather=False, split=True, extra_rows=20)
+    _fused_case([100], 128, 2048, 37, gather=False, use_dq=True, split=True, extra_rows=20)
     # several groups (an empty one, a ragged last row block) with gathered A
     _fused_case([5, 0, 40, 19], 96, 4096, 34, split=True)
     _fused_case([5, 0, 40, 19], 96, 4096, 35, use_dq=True, split=True)
