@@ -238,13 +238,13 @@ size_t nvfp4_grouped_gemm_workspace_size(int32_t G, int64_t M, int64_t N, int64_
   return nvfp4::gemm_splitk_bytes(G, M, N, K, w_layout == NVFP4_LAYOUT_TILED);
 }
 
-int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
-                                        int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
-                                        const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets,
-                                        int32_t G, int64_t M, int64_t I, int64_t K, const float* h_gs,
-                                        uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* workspace,
-                                        size_t ws_bytes, void* stream) {
-  const char* who = "nvfp4_grouped_gemm_silu_requant";
+// The checks and GemmArgs shared by the two fused first-GEMM calls (h
+// re-quantised, or h in float32): sizes, the A and W operands, group offsets.
+// Returns NVFP4_OK with *a filled, or the error (set as the last error).
+static int32_t fused_gemm_args(const char* who, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                               int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                               const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets, int32_t G,
+                               int64_t M, int64_t I, int64_t K, nvfp4::GemmArgs* a) {
   if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
   if (M < 0 || I < 32 || I % 32 || K < 256 || K % 256)
     return fail(NVFP4_ESHAPE, "%s: need M >= 0, I >= 32 with I %% 32 == 0, K >= 256 with K %% 256 == 0", who);
@@ -252,37 +252,53 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
     return fail(NVFP4_ESHAPE, "%s: M and 2 I must be below 2^31", who);
   if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
     return fail(NVFP4_ESHAPE, "%s: a_rows too small", who);
-  if (M == 0) return NVFP4_OK;
-  if (!a_codes || !a_scales || !a_gs || !w_tiled || !w_gs || !group_offsets || !h_gs || !h_codes || !h_scales)
+  if (M > 0 && (!a_codes || !a_scales || !a_gs || !w_tiled || !w_gs || !group_offsets))
     return fail(NVFP4_EINVAL, "%s: null pointer", who);
   if (!aligned(a_codes, 16) || !aligned(w_tiled, 16) || !aligned(a_scales, 4) || !aligned(a_gs, 4) ||
-      !aligned(w_gs, 4) || !aligned(group_offsets, 4) || !aligned(a_row_index, 4) || !aligned(a_dq, 16) ||
-      !aligned(h_gs, 4) || !aligned(h_codes, 16) || !aligned(h_dq, 16))
-    return fail(NVFP4_EALIGN, "%s: codes, a_dq, h_codes and h_dq must be 16-byte aligned, scales 4-byte", who);
-  nvfp4::GemmArgs a{};
-  a.a_codes = a_codes;
-  a.a_scales = a_scales;
-  a.a_gs = a_gs;
-  a.a_rows = a_row_index ? a_rows : M;
-  a.a_row_index = a_row_index;
-  a.a_dq = a_dq && (uint64_t)a.a_rows * (uint64_t)K * 2u < ((uint64_t)1 << 32) ? a_dq : nullptr;
-  a.w_codes = w_tiled;
-  a.w_scales = nullptr;
-  a.w_tiled = 1;
-  a.w_gs = w_gs;
-  a.n_seg[0] = 0;
-  a.n_seg[1] = (int32_t)I;
-  for (int i = 2; i < 5; ++i) a.n_seg[i] = (int32_t)(2 * I);
-  a.n_segs = 2;
-  a.group_offsets = group_offsets;
-  a.G = G;
-  a.M = M;
-  a.N = 2 * I;
-  a.K = K;
-  a.out = nullptr;
-  a.out_bf16 = 0;
-  a.ld_out = 2 * I;
-  a.fuse = 1;
+      !aligned(w_gs, 4) || !aligned(group_offsets, 4) || !aligned(a_row_index, 4) || !aligned(a_dq, 16))
+    return fail(NVFP4_EALIGN, "%s: codes, tiled weights and a_dq must be 16-byte aligned, the rest 4-byte", who);
+  *a = nvfp4::GemmArgs{};
+  a->a_codes = a_codes;
+  a->a_scales = a_scales;
+  a->a_gs = a_gs;
+  a->a_rows = a_row_index ? a_rows : M;
+  a->a_row_index = a_row_index;
+  a->a_dq = a_dq && (uint64_t)a->a_rows * (uint64_t)K * 2u < ((uint64_t)1 << 32) ? a_dq : nullptr;
+  a->w_codes = w_tiled;
+  a->w_scales = nullptr;
+  a->w_tiled = 1;
+  a->w_gs = w_gs;
+  a->n_seg[0] = 0;
+  a->n_seg[1] = (int32_t)I;
+  for (int i = 2; i < 5; ++i) a->n_seg[i] = (int32_t)(2 * I);
+  a->n_segs = 2;
+  a->group_offsets = group_offsets;
+  a->G = G;
+  a->M = M;
+  a->N = 2 * I;
+  a->K = K;
+  a->out = nullptr;
+  a->out_bf16 = 0;
+  a->ld_out = 2 * I;
+  a->fuse = 1;
+  return NVFP4_OK;
+}
+
+int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                        int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                                        const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets,
+                                        int32_t G, int64_t M, int64_t I, int64_t K, const float* h_gs,
+                                        uint8_t* h_codes, uint8_t* h_scales, uint16_t* h_dq, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  const char* who = "nvfp4_grouped_gemm_silu_requant";
+  nvfp4::GemmArgs a;
+  const int32_t rc = fused_gemm_args(who, a_codes, a_scales, a_gs, a_rows, a_row_index, a_dq, w_tiled, w_gs,
+                                     group_offsets, G, M, I, K, &a);
+  if (rc != NVFP4_OK) return rc;
+  if (M == 0) return NVFP4_OK;
+  if (!h_gs || !h_codes || !h_scales) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(h_gs, 4) || !aligned(h_codes, 16) || !aligned(h_dq, 16))
+    return fail(NVFP4_EALIGN, "%s: h_codes and h_dq must be 16-byte aligned, h_gs 4-byte", who);
   a.h_gs = h_gs;
   a.h_codes = h_codes;
   a.h_scales = h_scales;
@@ -294,6 +310,34 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
     a.splits = nvfp4::gemm_splitk_splits(G, M, 2 * I, K, true);
     a.ws = (float*)workspace;
   }
+  hipStream_t s = (hipStream_t)stream;
+  return finish(who, nvfp4::launch_grouped_gemm(a, s), s);
+}
+
+size_t nvfp4_grouped_gemm_silu_f32_partials(int32_t G, int64_t M, int64_t I) {
+  if (G < 1 || M < 1 || I < 32) return 0;
+  return (size_t)nvfp4::gemm_silu_f32_amax_slots(G, M, I);
+}
+
+int32_t nvfp4_grouped_gemm_silu_f32(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                    int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                                    const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets,
+                                    int32_t G, int64_t M, int64_t I, int64_t K, float* h, float* amax_partials,
+                                    int64_t n_partials, void* stream) {
+  const char* who = "nvfp4_grouped_gemm_silu_f32";
+  nvfp4::GemmArgs a;
+  const int32_t rc = fused_gemm_args(who, a_codes, a_scales, a_gs, a_rows, a_row_index, a_dq, w_tiled, w_gs,
+                                     group_offsets, G, M, I, K, &a);
+  if (rc != NVFP4_OK) return rc;
+  if (M == 0) return NVFP4_OK;
+  if (!h || !amax_partials) return fail(NVFP4_EINVAL, "%s: null pointer", who);
+  if (!aligned(h, 16) || !aligned(amax_partials, 4))
+    return fail(NVFP4_EALIGN, "%s: h must be 16-byte aligned, amax_partials 4-byte", who);
+  if (n_partials < nvfp4::gemm_silu_f32_amax_slots(G, M, I))
+    return fail(NVFP4_ESHAPE, "%s: n_partials below nvfp4_grouped_gemm_silu_f32_partials", who);
+  a.h_f32 = h;
+  a.h_amax = amax_partials;
+  a.h_amax_n = n_partials;
   hipStream_t s = (hipStream_t)stream;
   return finish(who, nvfp4::launch_grouped_gemm(a, s), s);
 }

@@ -531,9 +531,11 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
   const float a_gs = *p.a_gs;
   const float alpha_g = a_gs * p.w_gs[(int64_t)g * 2];
   const float alpha_u = a_gs * p.w_gs[(int64_t)g * 2 + 1];
-  const float gs = *p.h_gs;
+  const bool to_f32 = p.h_f32 != nullptr;
+  const float gs = to_f32 ? 0.0f : *p.h_gs;
   const int r = lane & 31, hb = lane >> 5;      // after the transpose: row r, half hb of the 32 columns
   const int64_t hcol = 32 * j + 16 * hb;
+  float wmax = 0.0f;     // float32 h: the largest |h| of this wave's rows
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -556,6 +558,16 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
     float bmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) bmax = __builtin_fmaxf(bmax, __builtin_fabsf(h[e]));
+    if (to_f32) {
+      const int64_t m = row0 + 32 * rb + r;
+      if (m < row1) {
+        floatx4_t* dst = (floatx4_t*)(p.h_f32 + m * I + hcol);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = floatx4_t{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+        wmax = __builtin_fmaxf(wmax, bmax);
+      }
+      continue;
+    }
     float rcp;
     bool zero;
     const uint32_t sq = block_scale(bmax, gs, rcp, zero);
@@ -579,6 +591,14 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
         *(half8_t*)(p.h_dq + m * I + hcol + 8) = dequant8(hi, sf2);
       }
     }
+  }
+  if (to_f32) {
+    // the wave's largest |h| (a max: any reduction order gives the same
+    // value), at its workgroup's slot (one tile per workgroup)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) wmax = __builtin_fmaxf(wmax, __shfl_xor(wmax, o, 64));
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (lane == 0 && slot < p.h_amax_n) p.h_amax[slot] = wmax;
   }
 }
 
@@ -1917,6 +1937,15 @@ hipError_t launch_split_partials(const GemmArgs& a, hipStream_t s) {
 
 template <bool FUSE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+  if (FUSE && a.h_f32) {
+    // float32 h: the per-wave maxima start at zero (waves without rows leave
+    // their entries so); no split-K in this mode
+    if (a.splits > 1 || !a.h_amax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zero_i32, dim3((unsigned)std::min<int64_t>((a.h_amax_n + 255) / 256, 1024)), dim3(256), 0, s,
+                       (int32_t*)a.h_amax, a.h_amax_n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.splits > 1 && a.ws && (a.G == 1 && a.a_dq || !gemm_uses_big_tiles(a.G, a.M, a.K, true))) {
     // few workgroups for the chip (gemm_splitk_splits): K split, then the
     // partial sums reduced in split order, to the output or (fused) through
@@ -1979,6 +2008,16 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 }
 
 int64_t moe_persistent_counters(int64_t G, int64_t M) { return 2 + (M + 31) / 32 + G; }
+
+int64_t gemm_silu_f32_amax_slots(int64_t G, int64_t M, int64_t I) {
+  // the fused launches of launch_tiled: 128-row tiles (slots4 x n_tiles
+  // workgroups) or the streaming kernel (one per 32-row slot and column tile)
+  const int64_t n_tiles = (2 * I + 255) / 256;
+  const int64_t slots4 = (M / BIG4 + G + 7) / 8 * 8;
+  const int64_t slots32 = (M + 31) / 32 + G;
+  // (a multiple of 8, so that nvfp4_global_scale can reduce the array)
+  return (4 * n_tiles * std::max(slots4, slots32) + 7) / 8 * 8;
+}
 
 hipError_t launch_moe_persistent(const GemmArgs& l1, const GemmArgs& l2, int32_t* ctr, int32_t spin_limit,
                                  hipStream_t s) {

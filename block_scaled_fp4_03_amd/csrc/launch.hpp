@@ -88,6 +88,13 @@ struct GemmArgs {
   uint8_t* h_codes;    // [M, I/2]
   uint8_t* h_scales;   // [M, I/16]
   uint16_t* h_dq;      // nullable: [M, I] f16, e2m1 * e4m3 of h
+  // fuse = 1 with h_f32: h is written in float32 instead ([M, I], row pitch
+  // I; h_gs, h_codes, h_scales and h_dq unused), and each wave of the launch
+  // stores the largest |h| of its rows at h_amax[4 * workgroup + wave] (the
+  // launcher zeroes the h_amax_n entries first)
+  float* h_f32;
+  float* h_amax;
+  int64_t h_amax_n;
   // split-K (splits > 1): raw partial sums [splits, M, N] float32 in ws,
   // added in split order and scaled by alpha by a second kernel
   int32_t splits;
@@ -103,6 +110,9 @@ bool gemm_uses_big_tiles(int64_t G, int64_t M, int64_t K, bool tiled);
 // one group of at most 128 rows on the 128-row tiles split over K
 bool gemm_small_split(int64_t G, int64_t M, bool tiled);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+// entries of h_amax that a fused launch with h_f32 of these sizes may write
+// (four per workgroup of the largest grid it can use)
+int64_t gemm_silu_f32_amax_slots(int64_t G, int64_t M, int64_t I);
 // the expert MLP in one persistent launch: l1 the first GEMM with the fused
 // SiLU-requant epilogue, l2 the second GEMM over the same groups (A = h);
 // ctr holds moe_persistent_counters(G, M) int32 counters

@@ -31,6 +31,9 @@ SIGNATURES = {
     "nvfp4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "nvfp4_grouped_gemm_silu_requant": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
                                                _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_grouped_gemm_silu_f32_partials": (_SZ, [_I32, _I64, _I64]),
+    "nvfp4_grouped_gemm_silu_f32": (_I32, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
+                                           _P, _P, _I64, _P]),
     "nvfp4_grouped_gemm_reads_dq": (_I32, [_I32, _I64, _I64, _I64, _I32]),
     "nvfp4_moe_expert_mlp_workspace_size": (_SZ, [_I32, _I64]),
     "nvfp4_moe_expert_mlp": (_I32, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P,

@@ -213,6 +213,29 @@ def grouped_gemm_silu_requant(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offs
     return (codes, scales, dq) if want_dq else (codes, scales)
 
 
+def grouped_gemm_silu_f32(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, M, I, K, a_row_index=None,
+                          a_dq=None, h=None, partials=None):
+    """First GEMM of the expert MLP with h = SiLU(gate)*up written in float32
+    (nvfp4_grouped_gemm_silu_f32): returns (h [M, I] float32, partial maxima
+    of |h| [n] float32, whose maximum is max |h|)."""
+    _check_dev(a_codes, a_scales, a_gs, w_tiled, w_gs, group_offsets, a_row_index, a_dq, h, partials)
+    G = w_gs.shape[0]
+    dev = a_codes.device
+    if h is None:
+        h = torch.empty(M, I, dtype=torch.float32, device=dev)
+    elif h.dtype != torch.float32 or tuple(h.shape) != (M, I) or not h.is_contiguous():
+        raise ValueError("h must be a contiguous float32 [%d, %d] tensor" % (M, I))
+    if partials is not None and (partials.dtype != torch.float32 or not partials.is_contiguous()):
+        raise ValueError("partials must be a contiguous float32 tensor")
+    n = _lib.load().nvfp4_grouped_gemm_silu_f32_partials(G, M, I) if M > 0 else 8
+    if partials is None:
+        partials = torch.empty(max(n, 8), dtype=torch.float32, device=dev)
+    _lib.call("nvfp4_grouped_gemm_silu_f32", _p(a_codes), _p(a_scales), _p(a_gs), a_codes.shape[0],
+              _p(a_row_index), _p(a_dq), _p(w_tiled), _p(w_gs), _p(group_offsets), G, M, I, K, _p(h),
+              _p(partials), partials.numel(), _stream())
+    return h, partials
+
+
 def moe_expert_mlp(x_codes, x_scales, x_gs, sorted_ids, offsets, w1_tiled, w1_gs, w2_tiled, w2_gs, R, H, I, gs_h,
                    workspace=None):
     """The experts' MLP in one persistent launch (nvfp4_moe_expert_mlp):

@@ -87,6 +87,18 @@ class NVFP4Weights:
         return ops.grouped_gemm_silu_requant(a_codes, a_scales, a_gs, self.tiled, self.gs, group_offsets, M,
                                              N // 2, 2 * K2, gs_h, **kw)
 
+    def can_fuse_silu_f32(self, M):
+        """Whether a first GEMM of M rows can write SiLU(gate)*up in float32
+        with its maxima (the dynamic-scale route): the fused epilogue without
+        a split K."""
+        G, N, K2 = self.codes.shape
+        return self.can_fuse_silu() and ops.gemm_workspace_size(G, M, N, 2 * K2, True) == 0
+
+    def gemm_silu_f32(self, a_codes, a_scales, a_gs, group_offsets, M, **kw):
+        G, N, K2 = self.codes.shape
+        return ops.grouped_gemm_silu_f32(a_codes, a_scales, a_gs, self.tiled, self.gs, group_offsets, M, N // 2,
+                                         2 * K2, **kw)
+
 
 def quantize_stack(mats, n_seg, device):
     """Quantise float32 matrices (each [N, K], one global scale per column
@@ -145,11 +157,13 @@ def can_persist(w1, w2):
 
 def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xdq=None, fused=None,
                 persistent=False):
-    """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` (static
-    gs_h and a fusable W1) the re-quantisation runs in the L1 epilogue, with
-    identical results and no float32 gate_up in memory; None picks
-    w1.fuse_by_default (fused wherever W1 allows it).  gs_h None computes it from
-    this batch's gate_up.  With `persistent`, both GEMMs and the fused
+    """L1 -> SiLU-requant -> L2 over R (gathered) rows.  With `fused` and a
+    static gs_h the re-quantisation runs in the L1 epilogue; with `fused` and
+    gs_h None (a scale from this batch) the L1 epilogue writes h in float32
+    and the maxima of |h|, from which gs_h comes, and h is then quantised.
+    Both give the unfused route's results bit for bit without its float32
+    gate_up; None picks w1.fuse_by_default (static) or w1.can_fuse_silu_f32
+    (dynamic).  With `persistent`, both GEMMs and the fused
     SiLU-requant run as one persistent launch (nvfp4_moe_expert_mlp; static
     gs_h): h is identical, y identical in the streaming regime.  Returns (y
     bf16, stages)."""
@@ -161,14 +175,23 @@ def _expert_mlp(xc, xs, gs_x, off, R, w1, w2, gs_h, a_rows, a_row_index=None, xd
                                        N // 2, gs_h)
         return y, dict(hc=hc, hs=hs, y=y, gs_h=gs_h)
     if fused is None:
-        fused = gs_h is not None and w1.fuse_by_default(R, a_rows)
-    if fused and (gs_h is None or not w1.can_fuse_silu()):
-        raise ValueError("the fused epilogue needs a static gs_h and tiled W1 with I % 32 == 0")
+        fused = w1.fuse_by_default(R, a_rows) if gs_h is not None else w1.can_fuse_silu_f32(R)
+    if fused and not (w1.can_fuse_silu() if gs_h is not None else w1.can_fuse_silu_f32(R)):
+        raise ValueError("the fused epilogue needs tiled W1 with I % 32 == 0 (and, for a dynamic gs_h, no split K)")
     dq2 = True if w2.reads_dq(R, R) else None
     st = {}
-    if fused:
+    if fused and gs_h is not None:
         hc, hs, *hdq = w1.gemm_silu_requant(xc, xs, gs_x, off, R, gs_h, a_row_index=a_row_index, a_dq=xdq,
                                             dq=dq2)
+    elif fused:
+        # dynamic gs_h: h in float32 and the maxima of |h| from the first
+        # GEMM's epilogue, gs_h from those maxima, then h quantised (the
+        # values, scale and codes of the unfused route, without its float32
+        # gate_up)
+        h32, part = w1.gemm_silu_f32(xc, xs, gs_x, off, R, a_row_index=a_row_index, a_dq=xdq)
+        gs_h = ops.global_scale(part.view(1, -1))
+        hc, hs, *hdq = ops.quantize(h32, gs_h, dq=dq2)
+        st["h_f32"] = h32
     else:
         gu = w1.gemm(xc, xs, gs_x, off, R, a_row_index=a_row_index, out_dtype=torch.float32, a_dq=xdq)
         if gs_h is None:
@@ -187,7 +210,8 @@ def moe_layer(x, logits, k, w1, w2, gs_x, gs_h, keep=False, fused=None, n_shared
     batch), or None for dynamic ones computed on the device from this batch
     (gs_x = amax(x)/2688 before quantising x, gs_h = amax(SiLU(g)*u)/2688
     between the two GEMMs; the host never waits for them).  `fused` runs
-    SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant),
+    SiLU-requant in the first GEMM's epilogue (nvfp4_grouped_gemm_silu_requant;
+    with a dynamic gs_h, nvfp4_grouped_gemm_silu_f32 and then nvfp4_quantize),
     None chooses by the first GEMM's kernel (see _expert_mlp); the results
     are identical either way.  With n_shared, w1/w2 also hold that many
     shared experts as their last groups: every token visits them with weight

@@ -336,6 +336,39 @@ int32_t nvfp4_grouped_gemm_silu_requant(const uint8_t* a_codes, const uint8_t* a
                                         uint16_t* h_dq, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_grouped_gemm_silu_f32 - the first grouped GEMM of the expert MLP with
+ * h = SiLU(gate) * up written in float32, and the maxima of |h| that give its
+ * global scale: the per-batch (dynamic) activation scale of the intermediate
+ * without the float32 [M, 2I] gate_up.  The pages trace their failure to
+ * activation global scales that did not match the data (page "Current Bug:
+ * vLLM produces empty/garbage output", revision a51edd2, section "What the
+ * quant method does"); a scale taken from the batch itself cannot be stale.
+ *   Arguments a_codes ... K as for nvfp4_grouped_gemm_silu_requant.
+ *   h              out [M, I] float32 (row pitch I, 16-byte aligned): every
+ *                  value as silu_mul_requant forms it from the gate_up that
+ *                  nvfp4_grouped_gemm writes (no split-K).  Rows outside
+ *                  every group are left untouched.
+ *   amax_partials  out [n_partials] float32, n_partials >=
+ *                  nvfp4_grouped_gemm_silu_f32_partials(G, M, I): zeroed by
+ *                  the call, then partial maxima of |h| (of rows inside the
+ *                  groups); their maximum is max |h|.
+ * Then nvfp4_global_scale(amax_partials as one slice of n_partials) gives
+ * the same gs_h as silu_mul_global_scale of that gate_up, and
+ * nvfp4_quantize(h, gs_h) the same codes, scales and f16 copy as
+ * silu_mul_requant (both take the maximum, which does not depend on order,
+ * and the same float32 steps).
+ * Errors: as nvfp4_grouped_gemm_silu_requant; ESHAPE if n_partials is too
+ * small; EALIGN unless h is 16-byte and amax_partials 4-byte aligned.
+ */
+size_t nvfp4_grouped_gemm_silu_f32_partials(int32_t G, int64_t M, int64_t I);
+int32_t nvfp4_grouped_gemm_silu_f32(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+                                    int64_t a_rows, const int32_t* a_row_index, const uint16_t* a_dq,
+                                    const uint8_t* w_tiled, const float* w_gs,
+                                    const int32_t* group_offsets, int32_t G, int64_t M, int64_t I,
+                                    int64_t K, float* h, float* amax_partials, int64_t n_partials,
+                                    void* stream);
+
+/*
  * nvfp4_moe_expert_mlp - the routed experts' MLP in ONE persistent launch:
  * the first grouped GEMM over the stacked gate_up weights with SiLU(gate) *
  * up re-quantised in its epilogue, then the second grouped GEMM over the

@@ -136,6 +136,35 @@ def test_fused_gemm_silu_validation(L):
     assert call(M=0, a_codes=NULL, hc=NULL) == lib.OK
 
 
+def test_fused_gemm_silu_f32_validation(L):
+    f = L.nvfp4_grouped_gemm_silu_f32
+    q = L.nvfp4_grouped_gemm_silu_f32_partials
+    n = q(1, 8, 64)
+    assert n > 0 and n % 8 == 0
+    # decode: 384 experts, 1536 rows, I = 3072: four per workgroup of the
+    # streaming grid (one per 32-row slot and 256 columns of the stacked gate_up)
+    assert q(384, 1536, 3072) == 4 * (1536 // 32 + 384) * 24
+    assert q(0, 8, 64) == 0 and q(1, 0, 64) == 0
+
+    def call(**kw):
+        a = dict(a_codes=FAKE, a_scales=FAKE, a_gs=FAKE, a_rows=8, a_row_index=NULL, a_dq=NULL, w=FAKE,
+                 w_gs=FAKE, off=FAKE, G=1, M=8, I=64, K=256, h=FAKE, part=FAKE, n=n)
+        a.update(kw)
+        return f(a["a_codes"], a["a_scales"], a["a_gs"], a["a_rows"], a["a_row_index"], a["a_dq"], a["w"],
+                 a["w_gs"], a["off"], a["G"], a["M"], a["I"], a["K"], a["h"], a["part"], a["n"], NULL)
+    assert call(I=48) == lib.ESHAPE            # I % 32
+    assert call(K=384) == lib.ESHAPE           # K % 256
+    assert call(G=0) == lib.ESHAPE
+    assert call(a_rows=4) == lib.ESHAPE
+    assert call(n=n - 8) == lib.ESHAPE         # too few partial maxima
+    assert call(h=NULL) == lib.EINVAL
+    assert call(part=NULL) == lib.EINVAL
+    assert call(w=NULL) == lib.EINVAL
+    assert call(h=ctypes.c_void_p(0x1008)) == lib.EALIGN
+    assert call(part=ctypes.c_void_p(0x1002)) == lib.EALIGN
+    assert call(M=0, a_codes=NULL, h=NULL, part=NULL) == lib.OK
+
+
 def test_workspace_size_query(L):
     q = L.nvfp4_grouped_gemm_workspace_size
     # one group of 128 rows (the shared expert): K is split

@@ -644,6 +644,70 @@ def test_fused_silu_requant_split_k():
     _fused_case([5, 0, 40, 19], 96, 4096, 35, use_dq=True, split=False)
 
 
+def _silu_f32_case(counts, I, K, seed, gather=True, use_dq=False, extra_rows=0):
+    """nvfp4_grouped_gemm_silu_f32 against the unfused GEMM (float32 gate_up):
+    h must equal silu_mul_requant's float32 SiLU(gate)*up of that gate_up
+    (the oracle's silu_mul, bit for bit), the maximum of the partial maxima
+    must be max |h|, and quantising h with the resulting global scale must
+    give silu_mul_requant's codes, scales and f16 copy.  Rows past the last
+    group offset stay untouched."""
+    log("gemm+silu f32", counts if len(counts) < 12 else (len(counts), sum(counts)), I, K, gather, use_dq,
+        extra_rows)
+    rng = np.random.default_rng(seed)
+    G, Mg = len(counts), int(sum(counts))
+    M = Mg + extra_rows
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a_rows = M + 5 if gather else M
+    ac, as_, ags = oracle_nvfp4(_x(a_rows, K, seed, outliers=True))
+    row_index = rng.integers(0, a_rows, M).astype(np.int32) if gather else None
+    N = 2 * I
+    wc = np.empty((G, N, K // 2), np.uint8)
+    ws = np.empty((G, N, K // 16), np.uint8)
+    wgs = np.empty((G, 2), np.float32)
+    for g in range(G):
+        wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        for sg in range(2):
+            c, sc, gg = oracle_nvfp4(wf[sg * I:(sg + 1) * I])
+            wc[g, sg * I:(sg + 1) * I], ws[g, sg * I:(sg + 1) * I], wgs[g, sg] = c, sc, gg
+    d = dev()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    tiled = ops.prepare_weights(T(wc), T(ws))
+    a_dq = T(quant.dequantize_blocks(ac, as_).astype(np.float16)) if use_dq else None
+    ri = T(row_index) if gather else None
+    args = (T(ac), T(as_), torch.tensor([ags], device=d))
+    assert ops.gemm_workspace_size(G, M, N, K, True) == 0      # no split K in this mode
+    gu = ops.grouped_gemm(*args, T(wc), T(ws), T(wgs), [0, I, N], T(off), M, a_row_index=ri, w_tiled=tiled,
+                          a_dq=a_dq)
+    h0 = torch.full((M, I), -7.0, dtype=torch.float32, device=d)
+    h, part = ops.grouped_gemm_silu_f32(*args, tiled, T(wgs), T(off), M, I, K, a_row_index=ri, a_dq=a_dq, h=h0)
+    g_gu = to_np(gu)[:Mg]
+    h_np = to_np(h)
+    assert np.array_equal(h_np[:Mg].view(np.uint32), moe.silu_mul(g_gu).view(np.uint32)), "h"
+    assert (h_np[Mg:] == -7.0).all(), "rows outside every group"
+    assert to_np(part).max() == np.abs(h_np[:Mg]).max(), "partial maxima"
+    gs_f = ops.global_scale(part.view(1, -1))
+    gs_u = ops.silu_mul_global_scale(gu[:Mg])
+    assert to_np(gs_f)[0] == to_np(gs_u)[0], "gs_h"
+    hc, hs, hdq = ops.quantize(h[:Mg], gs_f, dq=True)
+    rc, rs, rdq = ops.silu_mul_requant(gu[:Mg].contiguous(), gs_u, dq=True)
+    assert np.array_equal(to_np(hc), to_np(rc)) and np.array_equal(to_np(hs), to_np(rs)), "codes"
+    assert np.array_equal(to_np(hdq).view(np.uint16), to_np(rdq).view(np.uint16)), "f16 copy"
+
+
+def test_silu_f32_streaming_and_tiles():
+    # decode-shaped groups on the weight-streaming kernel; many-row groups on
+    # the 128-row tiles with A's f16 form (last tiles of 32, 64 and 128 rows);
+    # and the same groups streamed without it
+    rng = np.random.default_rng(51)
+    counts = rng.integers(0, 12, 40).tolist()
+    counts[3] = 0
+    _silu_f32_case(counts, 160, 512, 51)
+    big = [456, 3, 256, 0, 611, 70, 385]
+    _silu_f32_case(big, 256, 512, 52, use_dq=True, extra_rows=9)
+    _silu_f32_case(big, 256, 512, 53, extra_rows=9)
+    _silu_f32_case([300, 17], 96, 768, 54, gather=False, use_dq=True)
+
+
 # --- SiLU-requant and combine ---------------------------------------------------
 
 @pytest.mark.parametrize("M,I,dtype", [(1, 16, "f32"), (37, 128, "f32"), (200, 3072, "f32"), (64, 512, "bf16")])

@@ -172,17 +172,30 @@ def test_tiny_layer_dynamic_activation_scales():
     # oracle's amax(x)/2688 of the same bf16 x, and gs_h the oracle's
     # amax(SiLU(g)*u)/2688 of the GPU's own L1 output (the stage's input);
     # the layer is then checked stage by stage with those scales
+    # (the unfused route, which keeps the float32 gate_up for these checks);
+    # the default route (h in float32 and the maxima of |h| from the first
+    # GEMM's epilogue, then h quantised) must give its h, gs_h, intermediate
+    # and output bit for bit
     log("pipeline tiny, dynamic activation scales")
     wl, d, w1, w2, ow, W1, W2 = _tiny_setup()
     b = workloads.batch(wl)
-    out, g = pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2, None, None,
-                                keep=True)
+    run = lambda fused: pipeline.moe_layer(b["x"].to(d, torch.bfloat16), b["logits"].to(d), wl.k, w1, w2, None,
+                                           None, keep=True, fused=fused)
+    out, g = run(False)
     gs_x = to_np(g["gs_x"])[0]
     gs_h = to_np(g["gs_h"])[0]
     assert gs_x == quant.global_scale(quant.amax(b["x"].numpy()))
     assert gs_h == quant.global_scale(quant.amax(moe.silu_mul(to_np(g["gate_up"]))))
     c, rel, flips = _tiny_compare(wl, ow, W1, W2, b, gs_x, gs_h, out, g)
-    log("  tiny dynamic: gs_x %.6g, gs_h %.6g, cosine %.7f, audited flips %d" % (gs_x, gs_h, c, flips))
+    out2, g2 = run(None)
+    assert "gate_up" not in g2 and "h_f32" in g2
+    assert np.array_equal(to_np(g2["h_f32"]).view(np.uint32), moe.silu_mul(to_np(g["gate_up"])).view(np.uint32))
+    assert to_np(g2["gs_h"])[0] == gs_h
+    for k_ in ("hc", "hs"):
+        assert np.array_equal(to_np(g[k_]), to_np(g2[k_])), k_
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    log("  tiny dynamic: gs_x %.6g, gs_h %.6g, cosine %.7f, audited flips %d; float32-h route identical" % (
+        gs_x, gs_h, c, flips))
 
 
 def test_tiny_layer_shared_expert_folded():
