@@ -13,7 +13,10 @@ namespace nvfp4 {
 // waits for two memory round trips, not two per slot.  With a residual (bf16
 // [T, H]), its 8 values are loaded with the slices and added to the slot sum
 // as one more float32 addition.
-template <bool kBf16, int KMAX>
+// The grid is (column blocks, tokens) when T fits the grid's y extent: the
+// token is the workgroup's, so its slot indices and weights are uniform
+// loads, and there is no division per thread; else one dimension, strided.
+template <bool kBf16, int KMAX, bool kGrid2D>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t T, int k,
@@ -21,13 +24,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const uint16_t* __restrict__ residual,
                                                       uint16_t* __restrict__ out) {
   const int64_t per_row = H / 8;
-  const int64_t n = T * per_row;
+  const int64_t n = kGrid2D ? per_row : T * per_row;
   constexpr int64_t kElem = kBf16 ? 2 : 4;
   typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / per_row;
-    const int64_t c = (i - t * per_row) * 8;
+    const int64_t t = kGrid2D ? (int64_t)blockIdx.y : i / per_row;
+    const int64_t c = (kGrid2D ? i : i - t * per_row) * 8;
     int64_t row[KMAX];
     float wj[KMAX];
 #pragma unroll
@@ -95,6 +98,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   }
 }
 
+template <bool kBf16, int KMAX>
+static void combine_launch(bool g2, dim3 grid, dim3 block, hipStream_t s, const void* y, const int32_t* inv,
+                           const float* w, int64_t T, int k, int64_t H, int64_t R, const uint16_t* residual,
+                           uint16_t* out) {
+  if (g2)
+    hipLaunchKernelGGL((combine_kernel<kBf16, KMAX, true>), grid, block, 0, s, y, inv, w, T, k, H, R, residual, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<kBf16, KMAX, false>), grid, block, 0, s, y, inv, w, T, k, H, R, residual,
+                       out);
+}
+
 hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const float* w, int64_t T, int k,
                           int64_t H, const uint16_t* residual, uint16_t* out, hipStream_t s) {
   const int64_t n = T * (H / 8);
@@ -102,21 +116,17 @@ hipError_t launch_combine(const void* y, bool bf16, const int32_t* inv, const fl
   int64_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
   const int64_t R = T * k;
+  // (column blocks of 128 threads, tokens) where T fits the grid's y extent
+  const bool g2 = T <= 65535;
+  const dim3 grid = g2 ? dim3((unsigned)((H / 8 + 127) / 128), (unsigned)T) : dim3((unsigned)g);
+  const dim3 block(g2 ? 128 : 256);
   // slots unrolled up to 8 (top-6 with up to two shared experts) or 16
   if (bf16) {
-    if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<true, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
-                         residual, out);
-    else
-      hipLaunchKernelGGL((combine_kernel<true, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
-                         residual, out);
+    if (k <= 8) combine_launch<true, 8>(g2, grid, block, s, y, inv, w, T, k, H, R, residual, out);
+    else combine_launch<true, 16>(g2, grid, block, s, y, inv, w, T, k, H, R, residual, out);
   } else {
-    if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<false, 8>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
-                         residual, out);
-    else
-      hipLaunchKernelGGL((combine_kernel<false, 16>), dim3((unsigned)g), dim3(256), 0, s, y, inv, w, T, k, H, R,
-                         residual, out);
+    if (k <= 8) combine_launch<false, 8>(g2, grid, block, s, y, inv, w, T, k, H, R, residual, out);
+    else combine_launch<false, 16>(g2, grid, block, s, y, inv, w, T, k, H, R, residual, out);
   }
   return hipGetLastError();
 }

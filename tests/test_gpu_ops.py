@@ -734,9 +734,11 @@ def test_silu_mul_requant_bit_exact(M, I, dtype):
     assert g[0] == quant.global_scale(quant.amax(h))
 
 
+# (the last case has more tokens than the grid's y extent: the
+# one-dimensional launch)
 @pytest.mark.parametrize("T,k,H,dtype", [(16, 2, 256, "bf16"), (256, 6, 7168, "bf16"), (9, 1, 24, "f32"),
                                          (33, 16, 64, "f32"), (40, 7, 512, "bf16"), (12, 8, 64, "f32"),
-                                         (21, 11, 128, "bf16")])
+                                         (21, 11, 128, "bf16"), (70001, 2, 16, "bf16")])
 def test_combine_bit_exact(T, k, H, dtype):
     log("combine", T, k, H, dtype)
     rng = np.random.default_rng(T * k)
