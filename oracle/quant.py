@@ -29,7 +29,9 @@ Quantisation of one block x[0..15] (every step one IEEE float32 operation):
   else:       r = 1 / (sf * gs);  v_i = x_i * r;
               code_i = sign(x_i) << 3 | E2M1 magnitude index of |v_i|
 The sign bit of a code is the sign bit of x_i (so -0.1 under a coarse
-scale gives code 0x8, the negative zero).
+scale gives code 0x8, the negative zero).  A zero x_i has magnitude index 0
+also where sf * gs is so small that r overflows to inf (a subnormal gs):
+there the float32 product 0 * inf would be a NaN, and zero stays zero.
 """
 import numpy as np
 
@@ -79,14 +81,19 @@ def _quantize_rows(x, gs):
     xb = x.reshape(rows, cols // BLOCK, BLOCK)
     bamax = np.max(np.abs(xb), axis=2)                    # float32, exact
     d = F32(F32(E2M1_MAX) * gs)
-    s = (bamax / d).astype(F32)
+    with np.errstate(over="ignore"):                       # saturates below
+        s = (bamax / d).astype(F32)
     sq = e4m3_encode_nonneg(s)
     sf = e4m3_decode(sq).astype(F32)                      # exact in float32
-    with np.errstate(divide="ignore"):
+    with np.errstate(divide="ignore", over="ignore"):
         denom = (sf * gs).astype(F32)
         r = (F32(1.0) / denom).astype(F32)
     r = np.where(sf == 0, F32(0.0), r).astype(F32)
-    v = (xb * r[:, :, None]).astype(F32)
+    with np.errstate(invalid="ignore"):
+        v = (xb * r[:, :, None]).astype(F32)
+    # zero encodes as zero, also in a block whose 1/(sf*gs) overflowed to inf
+    # (where the float32 product 0 * inf would be a NaN)
+    v = np.where(xb == 0, F32(0.0), v).astype(F32)
     mag = e2m1_magnitude_index(np.abs(v))
     sign = np.signbit(xb).astype(np.uint8) << 3
     code = (mag | sign).astype(np.uint8)
@@ -133,5 +140,7 @@ def pre_rounding_values(x, gs):
     with np.errstate(divide="ignore"):
         r = (F32(1.0) / (sf * gs).astype(F32)).astype(F32)
     r = np.where(sf == 0, F32(0.0), r).astype(F32)
-    v = (xb * r[:, :, None]).astype(F32).reshape(rows, cols)
+    with np.errstate(invalid="ignore"):
+        v = (xb * r[:, :, None]).astype(F32)
+    v = np.where(xb == 0, F32(0.0), v).astype(F32).reshape(rows, cols)
     return s, v

@@ -131,6 +131,26 @@ def test_zero_block_gives_zero_codes_and_scale():
     assert s[0, 0] == 0 and (c[0, :8] == 0).all()
 
 
+def test_reciprocal_overflow_keeps_zero_codes_and_saturates_the_rest():
+    """A global scale so small that 1/(sf*gs) overflows float32: each step is
+    still one float32 operation, so a non-zero element times inf saturates to
+    6 (index 7) with its sign, and a zero element (either sign) keeps the
+    magnitude code of zero instead of the NaN that 0 * inf would give."""
+    gs = np.float32(1e-40)                                  # a float32 subnormal
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 1], x[0, 2], x[0, 3] = np.float32(5e-39), np.float32(-1e-39), np.float32(-0.0)
+    x[0, 16:] = np.linspace(-1, 1, 16, dtype=np.float32)   # an ordinary block
+    c, s = quant.quantize(x, gs)
+    sf = formats.e4m3_decode(s[0, 0])
+    with np.errstate(over="ignore"):
+        assert sf > 0 and not np.isfinite(np.float32(1.0) / np.float32(np.float32(sf) * gs))
+    codes = np.empty(32, dtype=np.uint8)
+    codes[0::2], codes[1::2] = c[0] & 0xF, c[0] >> 4
+    assert codes[0] == 0 and codes[1] == 0x7 and codes[2] == 0xF and codes[3] == 0x8
+    assert (codes[4:16] == 0).all()
+    assert s[0, 1] == 0x7E and (codes[16:] & 7).max() == 7   # 1/(448*gs) is finite
+
+
 def test_brute_force_tiny_block_reconstruction_is_nearest_grid_point():
     """For unsaturated normal blocks, every element decodes to the grid point
     of {+-e2m1 * sf * gs} nearest to it (ties either way)."""
