@@ -571,13 +571,7 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
     float rcp;
     bool zero;
     const uint32_t sq = block_scale(bmax, gs, rcp, zero);
-    uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t code = e2m1_code(h[e], rcp, zero);
-      if (e < 8) lo |= code << (4 * e);
-      else hi |= code << (4 * (e - 8));
-    }
+    const uint32_t lo = e2m1_pack<4>(h, rcp, zero), hi = e2m1_pack<4>(h + 8, rcp, zero);
     const int64_t m = row0 + 32 * rb + r;
     if (m < row1) {
       uint32_t* hc = (uint32_t*)(p.h_codes + m * (I / 2) + hcol / 2);
@@ -1261,9 +1255,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_silu_requant(GemmArgs p) {
     float r;
     bool zero;
     const uint32_t sq = block_scale(amax, gs, r, zero);
-    uint32_t bits = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bits |= e2m1_code(h[e], r, zero) << (4 * e);
+    const uint32_t bits = e2m1_pack<2>(h, r, zero);
     *(uint16_t*)(p.h_codes + m * (I / 2) + cb * 8 + 2 * qd) = (uint16_t)bits;
     if (qd == 0) p.h_scales[m * bpr + cb] = (uint8_t)sq;
     if (p.h_dq) {

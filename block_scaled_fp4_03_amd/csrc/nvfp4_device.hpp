@@ -54,8 +54,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
-// Quantise one 16-element block.  x: 16 finite floats.  Returns the scale code
-// and writes the 16 packed codes (element 2i in the low nibble) as two words.
 // Scale code of a block whose largest magnitude is bamax, with the
 // reciprocal r that maps its elements onto the E2M1 grid; `zero` when the
 // scale decodes to 0 (then every code of the block is 0x0).  Each step is
@@ -78,6 +76,32 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float r, bool zero) {
   return e2m1_index(__builtin_fabsf(v)) | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// E2M1 codes of the 2P values x[0..2P) of one block with reciprocal r, value
+// i in nibble i: the code e2m1_code gives for each.  gfx950's packed
+// conversion (scale 1) rounds exactly like e2m1_code on every float32 that is
+// not a NaN, sign included (checked over all 2^32 patterns), so for a finite
+// r > 0 a pair costs two multiplies and one conversion; x * r can be a NaN
+// only when r is not such a number (sf * gs underflowed, or a global scale
+// that is not positive), and those blocks take the comparison encoder.
+template <int P>
+__device__ __forceinline__ uint32_t e2m1_pack(const float* x, float r, bool zero) {
+  static_assert(P >= 1 && P <= 4, "one to four pairs per word");
+  if (zero) return 0u;
+  uint32_t w = 0u;
+  if (r > 0.0f && r < __builtin_inff()) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0] * r, x[1] * r, 1.0f, 0);
+    if constexpr (P > 1) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2] * r, x[3] * r, 1.0f, 1);
+    if constexpr (P > 2) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4] * r, x[5] * r, 1.0f, 2);
+    if constexpr (P > 3) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6] * r, x[7] * r, 1.0f, 3);
+    return w;
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * P; ++i) w |= e2m1_code(x[i], r, false) << (4 * i);
+  return w;
+}
+
+// Quantise one 16-element block.  x: 16 finite floats.  Returns the scale code
+// and writes the 16 packed codes (element 2i in the low nibble) as two words.
 __device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float gs,
                                                      uint32_t& lo, uint32_t& hi) {
   float bamax = 0.0f;
@@ -86,14 +110,8 @@ __device__ __forceinline__ uint32_t quantize_block16(const float (&x)[16], float
   float r;
   bool zero;
   const uint32_t sq = block_scale(bamax, gs, r, zero);
-  lo = 0u;
-  hi = 0u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t c = e2m1_code(x[i], r, zero);
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
-  }
+  lo = e2m1_pack<4>(x, r, zero);
+  hi = e2m1_pack<4>(x + 8, r, zero);
   return sq;
 }
 

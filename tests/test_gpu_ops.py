@@ -54,6 +54,20 @@ def test_quantize_saturation_and_tiny_gs():
         assert np.array_equal(to_np(c), c_ref) and np.array_equal(to_np(s), s_ref), gs
 
 
+def test_quantize_reciprocal_overflow():
+    """A subnormal global scale: blocks whose 1/(sf*gs) overflows to inf take
+    the comparison encoder (zeros stay zero), the rest the packed conversion."""
+    log("quantize reciprocal overflow")
+    x = _x(8, 64, 9).astype(np.float32)
+    x[2, :16] = 0.0
+    x[2, 1], x[2, 2], x[2, 3] = F32(5e-39), F32(-1e-39), F32(-0.0)
+    x[3, 16:32] *= F32(1e-38)
+    for gs in [F32(1e-40), F32(3e-39)]:
+        c_ref, s_ref = quant.quantize(x, gs)
+        c, s = ops.quantize(torch.from_numpy(x).to(dev()), torch.tensor([gs], device=dev()))
+        assert np.array_equal(to_np(c), c_ref) and np.array_equal(to_np(s), s_ref), gs
+
+
 def test_quantize_row_pitch_and_empty():
     log("quantize pitch")
     x = _x(9, 96, 4)
