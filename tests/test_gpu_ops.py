@@ -54,6 +54,34 @@ def test_quantize_saturation_and_tiny_gs():
         assert np.array_equal(to_np(c), c_ref) and np.array_equal(to_np(s), s_ref), gs
 
 
+def test_quantize_rounding_ties_and_signs():
+    """Every E2M1 rounding midpoint, both signs, signed zeros and values just
+    either side of a midpoint, in blocks whose reciprocal is exactly 1 (gs = 1,
+    block maximum 6), so each value reaches the encoder unchanged."""
+    log("quantize ties")
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for m in mids:
+        vals += [m, -m, float(np.nextafter(F32(m), F32(0))), float(np.nextafter(F32(m), F32(8)))]
+    vals += [0.0, -0.0, 6.0, -6.0]
+    vals = np.array(vals, dtype=np.float32)
+    blocks = []
+    for b0 in range(0, len(vals), 15):
+        chunk = vals[b0:b0 + 15]
+        blk = np.zeros(16, dtype=np.float32)
+        blk[0] = 6.0                        # the block maximum: scale 1
+        blk[1:1 + len(chunk)] = chunk
+        blocks.append(blk)
+    x = np.stack(blocks).reshape(1, -1).repeat(3, axis=0)
+    x[1] *= -1.0
+    gs = F32(1.0)
+    c_ref, s_ref = quant.quantize(x, gs)
+    assert (s_ref == 0x38).all()           # E4M3 1.0 everywhere
+    c, s = ops.quantize(torch.from_numpy(x).to(dev()), torch.tensor([gs], device=dev()))
+    assert np.array_equal(to_np(s), s_ref)
+    assert np.array_equal(to_np(c), c_ref)
+
+
 def test_quantize_reciprocal_overflow():
     """A subnormal global scale: blocks whose 1/(sf*gs) overflows to inf take
     the comparison encoder (zeros stay zero), the rest the packed conversion."""
