@@ -185,7 +185,8 @@ int32_t nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, cons
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: need M >= 0, N >= 1, K >= 32 and K %% 32 == 0");
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: M and N must be below 2^31");
-  if (tiled && K % 256) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: the tiled layout needs K %% 256 == 0");
+  if (tiled && (K % 256 || K > nvfp4::kMaxTiledK))
+    return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: the tiled layout needs K %% 256 == 0 and K <= 2^24");
   if (ld_out < N) return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: ld_out < N");
   if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
     return fail(NVFP4_ESHAPE, "nvfp4_grouped_gemm: a_rows too small");
@@ -246,8 +247,9 @@ static int32_t fused_gemm_args(const char* who, const uint8_t* a_codes, const ui
                                const uint8_t* w_tiled, const float* w_gs, const int32_t* group_offsets, int32_t G,
                                int64_t M, int64_t I, int64_t K, nvfp4::GemmArgs* a) {
   if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
-  if (M < 0 || I < 32 || I % 32 || K < 256 || K % 256)
-    return fail(NVFP4_ESHAPE, "%s: need M >= 0, I >= 32 with I %% 32 == 0, K >= 256 with K %% 256 == 0", who);
+  if (M < 0 || I < 32 || I % 32 || K < 256 || K % 256 || K > nvfp4::kMaxTiledK)
+    return fail(NVFP4_ESHAPE, "%s: need M >= 0, I >= 32 with I %% 32 == 0, 256 <= K <= 2^24 with K %% 256 == 0",
+                who);
   if (M >= ((int64_t)1 << 31) || 2 * I >= ((int64_t)1 << 31))
     return fail(NVFP4_ESHAPE, "%s: M and 2 I must be below 2^31", who);
   if (a_rows < 0 || (!a_row_index && a_rows < M) || (M > 0 && a_rows < 1))
@@ -363,8 +365,8 @@ int32_t nvfp4_moe_expert_mlp(const uint8_t* x_codes, const uint8_t* x_scales, co
                              uint8_t* h_scales, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   const char* who = "nvfp4_moe_expert_mlp";
   if (G < 1 || G > NVFP4_MAX_EXPERTS) return fail(NVFP4_ESHAPE, "%s: G=%d", who, G);
-  if (R < 0 || H < 256 || H % 256 || I < 256 || I % 256)
-    return fail(NVFP4_ESHAPE, "%s: need R >= 0, H and I >= 256 and multiples of 256", who);
+  if (R < 0 || H < 256 || H % 256 || I < 256 || I % 256 || H > nvfp4::kMaxTiledK || I > nvfp4::kMaxTiledK)
+    return fail(NVFP4_ESHAPE, "%s: need R >= 0, H and I in [256, 2^24] and multiples of 256", who);
   if (R >= ((int64_t)1 << 31) || 2 * I >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 31))
     return fail(NVFP4_ESHAPE, "%s: R, 2 I and H must be below 2^31", who);
   if (x_rows < 0 || (!sorted_token_ids && x_rows < R) || (R > 0 && x_rows < 1))
@@ -452,8 +454,8 @@ size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K) {
 
 int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t G, int64_t N, int64_t K,
                               uint8_t* out, void* stream) {
-  if (G < 1 || N < 1 || K < 256 || K % 256)
-    return fail(NVFP4_ESHAPE, "nvfp4_prepare_weights: need G >= 1, N >= 1, K >= 256 and K %% 256 == 0");
+  if (G < 1 || N < 1 || K < 256 || K % 256 || K > nvfp4::kMaxTiledK)
+    return fail(NVFP4_ESHAPE, "nvfp4_prepare_weights: need G >= 1, N >= 1, 256 <= K <= 2^24 and K %% 256 == 0");
   if (!w_codes || !w_scales || !out) return fail(NVFP4_EINVAL, "nvfp4_prepare_weights: null pointer");
   if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(out, 16))
     return fail(NVFP4_EALIGN, "nvfp4_prepare_weights: buffers must be 16-byte aligned");

@@ -680,13 +680,15 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   // VGPR set once, the half-step's offset in an SGPR (no 64-bit address
   // arithmetic per load); the non-temporal bit in the cache-policy field
   const int64_t nb_per_g = (p.N + kTileRows - 1) / kTileRows;
-  __amdgpu_buffer_rsrc_t w_rsrc[NBW];
+  __amdgpu_buffer_rsrc_t w_rsrc[NBW], w_none[NBW];
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     int64_t nb = FUSE ? j + cb * (p.N / 64) : n0 / 32 + cb;
     nb = nb < nb_per_g ? nb : nb_per_g - 1;
     w_rsrc[cb] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes),
                                                    (short)0, (int)(nks * kTileBytes), 0x00020000);
+    w_none[cb] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w_codes + ((int64_t)g * nb_per_g + nb) * nks * kTileBytes),
+                                                   (short)0, 0, 0x00020000);
   }
   constexpr int kPol = NT ? 2 : 0;
   const int w_lo = 16 * lane, w_hi = 16 * lane + 1024, w_sc = 4 * lane + 4096;
@@ -720,7 +722,13 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
       }
     }
   };
-  auto load_w = [&](int64_t hs, Ops& d) {
+  // dead: the set is never used (the loads of the last two half-steps);
+  // its weight loads then go through a resource of no records, where the
+  // buffer unit returns zeros without a memory access (on the second GEMM of
+  // the decode layer, reloading the last half-step's words instead cost
+  // 20 us: a wave cannot end while its loads are in flight).  The choice of
+  // resource is a scalar select, no vector work.
+  auto load_w = [&](int64_t hs, Ops& d, bool dead) {
     const int ks = (int)(hs >> 1), h = (int)(hs & 1);
     // (uniform by construction; said so, or the compiler keeps them in
     // vector registers and loops over the lanes' distinct values)
@@ -728,14 +736,15 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     const int ss = __builtin_amdgcn_readfirstlane(ks * kTileBytes + 256 * h);
 #pragma unroll
     for (int cb = 0; cb < NBW; ++cb) {
-      d.w0[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_lo, so, kPol);
-      d.w1[cb] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc[cb], w_hi, so, kPol);
-      d.ws[cb] = __builtin_amdgcn_raw_buffer_load_b32(w_rsrc[cb], w_sc, ss, kPol);
+      const __amdgpu_buffer_rsrc_t r = dead ? w_none[cb] : w_rsrc[cb];
+      d.w0[cb] = __builtin_amdgcn_raw_buffer_load_b128(r, w_lo, so, kPol);
+      d.w1[cb] = __builtin_amdgcn_raw_buffer_load_b128(r, w_hi, so, kPol);
+      d.ws[cb] = __builtin_amdgcn_raw_buffer_load_b32(r, w_sc, ss, kPol);
     }
   };
-  auto load = [&](int64_t hs, Ops& d) {
+  auto load = [&](int64_t hs, Ops& d, bool dead = false) {
     load_a(hs, d);
-    load_w(hs, d);
+    load_w(hs, d, dead);
   };
   auto compute = [&](const Ops& o) {
     // the four E4M3 scale bytes of each word, two per conversion (exact:
@@ -777,8 +786,8 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
   // defined values
   Ops s0{}, s1{}, s2{};
   if (sy.wait_ctr) {
-    load_w(h0, s0);
-    load_w(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
+    load_w(h0, s0, false);
+    load_w(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1, false);
     tile_wait(sy);
     load_a(h0, s0);
     load_a(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
@@ -786,9 +795,9 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     load(h0, s0);
     load(h0 + 1 < nhs ? h0 + 1 : nhs - 1, s1);
   }
-  // (the last two half-steps reload the last one: no branch around a load)
+  // (the last two half-steps issue dead loads: no branch around a load)
   auto step = [&](int64_t hs, const Ops& cur, Ops& ld) {
-    load(hs + 2 < nhs ? hs + 2 : nhs - 1, ld);
+    load(hs + 2 < nhs ? hs + 2 : nhs - 1, ld, hs + 2 >= nhs);
     // the loads go out before the half-step's conversions and MFMAs (the
     // scheduler would otherwise sink them towards their use)
     __builtin_amdgcn_sched_barrier(0);

@@ -42,6 +42,9 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
 // (4096 B) then scales (512 B).
 constexpr int kTileRows = 32;
 constexpr int kTileBytes = 4608;
+// Largest K of the tiled layout: one 32-row block's K range (K / 256 tiles)
+// stays far below 2^31 bytes, the reach of the kernels' buffer resources.
+constexpr int64_t kMaxTiledK = (int64_t)1 << 24;
 
 // --- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld_x,

@@ -265,8 +265,8 @@ int32_t moe_route_permute_shared(const float* logits, int64_t T, int32_t E, int3
  *                      calls that share one workspace must not overlap.
  * Errors: EINVAL for null pointers, an unknown dtype or layout; ESHAPE
  * unless 1 <= G <= NVFP4_MAX_EXPERTS, 1 <= n_segs <= NVFP4_MAX_SEGMENTS,
- * M >= 0, N >= 1, K >= 32 with K % 32 == 0 (K % 256 == 0 for the tiled
- * layout), ld_out >= N, a_rows >= 1 when M > 0 (and >= M when a_row_index
+ * M >= 0, N >= 1, K >= 32 with K % 32 == 0 (K % 256 == 0 and K <= 2^24
+ * for the tiled layout), ld_out >= N, a_rows >= 1 when M > 0 (and >= M when a_row_index
  * is NULL), n_seg increasing from 0 to N; EALIGN unless codes (and the tiled
  * buffer), a_dq and out are 16-byte aligned and scales 4-byte aligned.
  */
@@ -323,8 +323,8 @@ size_t nvfp4_grouped_gemm_workspace_size(int32_t G, int64_t M, int64_t N, int64_
  *                      both.  Caller-owned; calls that share one workspace
  *                      must not overlap.
  * Errors: EINVAL for null pointers; ESHAPE unless 1 <= G <=
- * NVFP4_MAX_EXPERTS, M >= 0, I >= 32 with I % 32 == 0, K >= 256 with
- * K % 256 == 0, a_rows as for nvfp4_grouped_gemm; EALIGN unless codes,
+ * NVFP4_MAX_EXPERTS, M >= 0, I >= 32 with I % 32 == 0, 256 <= K <= 2^24
+ * with K % 256 == 0, a_rows as for nvfp4_grouped_gemm; EALIGN unless codes,
  * w_tiled, a_dq, h_codes and h_dq are 16-byte aligned and scales and global
  * scales 4-byte aligned.
  */
@@ -413,7 +413,7 @@ int32_t nvfp4_grouped_gemm_silu_f32(const uint8_t* a_codes, const uint8_t* a_sca
  * int32 workspace word 1 is set non-zero and the results are unspecified
  * (under NVFP4MOE_SYNC_CHECK=1 the call then returns NVFP4_EHIP).
  * Errors: EINVAL for null pointers; ESHAPE unless 1 <= G <=
- * NVFP4_MAX_EXPERTS, R >= 0, H and I are multiples of 256 (>= 256), x_rows
+ * NVFP4_MAX_EXPERTS, R >= 0, H and I are multiples of 256 in [256, 2^24], x_rows
  * as for nvfp4_grouped_gemm, the workspace is large enough; EALIGN as
  * stated.  R == 0 is a no-op.
  */
@@ -454,7 +454,7 @@ int32_t nvfp4_grouped_gemm_reads_dq(int32_t G, int64_t M, int64_t K, int64_t a_r
  * row's 128 code bytes of the step (i = 0, 1), and bytes
  * [4096 + 256h + 4l, +4) its scale bytes [8h + 4kh, +4) of the step's 16.
  * Errors: EINVAL for null pointers; ESHAPE unless G >= 1, N >= 1,
- * K % 256 == 0 and K >= 256; EALIGN for misaligned pointers.
+ * K % 256 == 0 and 256 <= K <= 2^24; EALIGN for misaligned pointers.
  */
 size_t nvfp4_prepared_weight_bytes(int64_t G, int64_t N, int64_t K);
 int32_t nvfp4_prepare_weights(const uint8_t* w_codes, const uint8_t* w_scales, int64_t G, int64_t N,

@@ -112,6 +112,7 @@ def test_gemm_validation(L):
     assert _gemm(L, M=0, a_codes=NULL, out=NULL) == lib.OK
     assert _gemm(L, w_layout=2) == lib.EINVAL
     assert _gemm(L, w_layout=lib.LAYOUT_TILED) == lib.ESHAPE       # K % 256
+    assert _gemm(L, w_layout=lib.LAYOUT_TILED, K=(1 << 24) + 256) == lib.ESHAPE   # K > 2^24
     assert _gemm(L, w_layout=lib.LAYOUT_ROWS, w_scales=NULL) == lib.EINVAL
 
 
@@ -127,6 +128,7 @@ def test_fused_gemm_silu_validation(L):
                  0, NULL)
     assert call(I=48) == lib.ESHAPE            # I % 32
     assert call(K=384) == lib.ESHAPE           # K % 256
+    assert call(K=(1 << 24) + 256) == lib.ESHAPE   # K > 2^24
     assert call(G=0) == lib.ESHAPE
     assert call(a_rows=4) == lib.ESHAPE
     assert call(h_gs=NULL) == lib.EINVAL
@@ -154,6 +156,7 @@ def test_fused_gemm_silu_f32_validation(L):
                  a["w_gs"], a["off"], a["G"], a["M"], a["I"], a["K"], a["h"], a["part"], a["n"], NULL)
     assert call(I=48) == lib.ESHAPE            # I % 32
     assert call(K=384) == lib.ESHAPE           # K % 256
+    assert call(K=(1 << 24) + 256) == lib.ESHAPE   # K > 2^24
     assert call(G=0) == lib.ESHAPE
     assert call(a_rows=4) == lib.ESHAPE
     assert call(n=n - 8) == lib.ESHAPE         # too few partial maxima
@@ -205,6 +208,7 @@ def test_prepare_validation_and_size(L):
     assert L.nvfp4_prepared_weight_bytes(2, 33, 512) == 2 * 2 * 2 * 4608
     assert L.nvfp4_prepared_weight_bytes(1, 16, 128) == 0
     assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, 128, FAKE, NULL) == lib.ESHAPE
+    assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, (1 << 24) + 256, FAKE, NULL) == lib.ESHAPE
     assert L.nvfp4_prepare_weights(NULL, FAKE, 1, 16, 256, FAKE, NULL) == lib.EINVAL
     assert L.nvfp4_prepare_weights(FAKE, FAKE, 1, 16, 256, ctypes.c_void_p(0x1001), NULL) == lib.EALIGN
 
