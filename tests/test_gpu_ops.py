@@ -283,6 +283,19 @@ def test_gemm_rows_over_16_per_group_and_ragged_n():
     _gemm_case([17, 1, 33, 0, 5], 200, 512, [0, 100, 200], 3, gather=True, out_bf16=True)
 
 
+def test_gemm_streaming_runs_of_column_tiles():
+    # few rows per group and 2K/256 divisible by 3: the streaming kernel takes
+    # runs of column tiles per workgroup; a ragged last tile and last run, a
+    # group of two 32-row slots, an empty group, a segment boundary inside a
+    # column block
+    rng = np.random.default_rng(41)
+    counts = rng.integers(0, 12, 24).tolist()
+    counts[2] = 0
+    counts[5] = 40
+    _gemm_case(counts, 1320, 768, [0, 500, 1320], 41, gather=True, out_bf16=True)
+    _gemm_case(counts[:10], 1064, 1536, [0, 1064], 42)
+
+
 def test_gemm_k_tails():
     for K in (32, 96, 160, 288, 320, 544, 576):
         _gemm_case([5, 9], 72, K, [0, 72], 4 + K)
