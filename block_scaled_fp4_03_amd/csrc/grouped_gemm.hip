@@ -536,10 +536,16 @@ __device__ __forceinline__ void silu_requant_epilogue(const GemmArgs& p, const f
   const int r = lane & 31, hb = lane >> 5;      // after the transpose: row r, half hb of the 32 columns
   const int64_t hcol = 32 * j + 16 * hb;
   float wmax = 0.0f;     // float32 h: the largest |h| of this wave's rows
+  const int64_t rows = row1 - row0;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      // elements 4q .. 4q + 3 hold rows 32 rb + 8q .. + 7 (both lane
+      // halves): skipped, uniformly, where all of them lie past the tile's
+      // last row (their staged values are then stale, and only rows past
+      // the last read them back, whose results are never stored)
+      if (32 * rb + 8 * (i >> 2) >= rows) continue;
       const float gv = alpha_g * acc[rb][0][i];
       const float uv = alpha_u * acc[rb][1][i];
       st[acc32_row(i, kh) * kHStride + c] = silu_mul(gv, uv);
