@@ -840,6 +840,7 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     return;
   }
   const float a_gs = *p.a_gs;
+  const int64_t rows = row1 - row0;
 #pragma unroll
   for (int cb = 0; cb < NBW; ++cb) {
     const int64_t n = n0 + 32 * cb + c;
@@ -849,6 +850,8 @@ __device__ __forceinline__ void stream32_tile(const GemmArgs& p, int g, int64_t 
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        // (rows 32 rb + 8 (i / 4) .. + 7: skipped uniformly past the last row)
+        if (32 * rb + 8 * (i >> 2) >= rows) continue;
         const int64_t m = row0 + 32 * rb + acc32_row(i, kh);
         if (m < row1) store_out(p, m, n, alpha * acc[rb][cb][i]);
       }
